@@ -1,0 +1,130 @@
+"""Workload configurations for the MoE expert layer.
+
+Each configuration fixes the sizes, dtypes and input distributions of one
+seeded synthetic workload.  The five full-size workloads mirror the shapes the
+pages discuss:
+
+* [MND] = page "Lower latency and higher throughput with multi-node DeepSeek
+  deployment" (Perplexity blog, 2025-04-18): 256 routed experts + 1 shared
+  expert, 8 routed experts per token (section "Expert Parallelism");
+  decode batches of 128 per GPU (section "Latency breakdown").
+* [R1P] = page "CANN/cann-recipes-infer: DeepSeek-R1 prefill optimization"
+  (Atlas A3): prefill of 4K-token requests with expert-parallel double routing
+  (section "MoE deployment strategy optimization"), two 4K requests per card
+  (section "micro-batch optimization").
+
+The ``p*`` configurations are reduced copies that keep every structural
+feature (ragged expert loads, empty experts, an expert base offset, the fp8
+scale layout, partial N tiles) at sizes a plain CPU reference finishes in
+seconds.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from typing import Optional
+
+
+@dataclass(frozen=True)
+class MoEConfig:
+    name: str
+    cid: int                 # stable integer folded into every seed
+    T: int                   # tokens (for pretagged: received expanded rows)
+    H: int                   # hidden size
+    E: int                   # routed experts held on this GPU
+    k: int                   # routed experts per token (1 for pretagged rows)
+    I: int                   # routed SwiGLU intermediate size
+    I_shared: int            # shared-expert intermediate size
+    act: str                 # activation dtype: "f32" | "bf16"
+    wt: str                  # expert-weight dtype: "f32" | "bf16" | "fp8"
+    x_std: float = 1.0
+    wg_std: Optional[float] = None   # None -> 1/sqrt(H) (logits ~ N(0,1))
+    w_std: float = 0.02
+    zipf_s: Optional[float] = None   # expert-popularity bias exponent
+    bias_alpha: float = 0.0          # bias b_e = alpha * ln p_e
+    pretagged: bool = False          # rows arrive with expert ids (no gate)
+    e_base: int = 0                  # first global expert id held here
+    E_total: Optional[int] = None    # experts in the whole model (pretagged)
+    T_local: int = 0                 # local tokens for the shared expert (pretagged)
+    seed: int = 0
+    description: str = ""
+
+    @property
+    def R(self) -> int:
+        return self.T * self.k
+
+    @property
+    def gate_std(self) -> float:
+        return self.wg_std if self.wg_std is not None else self.H ** -0.5
+
+    @property
+    def has_bias(self) -> bool:
+        return self.zipf_s is not None and self.bias_alpha != 0.0
+
+    @property
+    def shared_rows(self) -> int:
+        return self.T_local if self.pretagged else self.T
+
+
+# Calibrated by oracle/calibrate_bias.py so that the most-loaded expert receives
+# about 8x the mean rows (max/mean in [7.5, 8.5]) at the full T=16384 workload.
+C5_BIAS_ALPHA = 0.234375
+
+CONFIGS = {
+    "c1_tiny_fp32": MoEConfig(
+        name="c1_tiny_fp32", cid=1, T=64, H=256, E=16, k=2, I=128, I_shared=128,
+        act="f32", wt="f32", x_std=0.02, wg_std=0.02, w_std=0.02,
+        description="tiny MoE layer, fp32, N(0,1)*0.02 tokens and weights"),
+    "c2_prefill_bf16": MoEConfig(
+        name="c2_prefill_bf16", cid=2, T=8192, H=7168, E=256, k=8, I=2048, I_shared=2048,
+        act="bf16", wt="bf16",
+        description="DeepSeek-V3-shaped prefill layer (two 4K requests), bf16"),
+    "c3_ep_rank_bf16": MoEConfig(
+        name="c3_ep_rank_bf16", cid=3, T=8192, H=7168, E=32, k=1, I=2048, I_shared=2048,
+        act="bf16", wt="bf16", pretagged=True, e_base=96, E_total=256, T_local=1024,
+        description="one expert-parallel rank's share at ep=8: 8192 received rows "
+                    "tagged with local experts 96..127, 1024 local tokens"),
+    "c4_decode_bf16": MoEConfig(
+        name="c4_decode_bf16", cid=4, T=128, H=7168, E=256, k=8, I=2048, I_shared=2048,
+        act="bf16", wt="bf16", zipf_s=1.1, bias_alpha=0.5,
+        description="decode batch of 128 tokens, Zipf(1.1) expert popularity"),
+    "c5_skewed_fp8": MoEConfig(
+        name="c5_skewed_fp8", cid=5, T=16384, H=7168, E=256, k=8, I=2048, I_shared=2048,
+        act="bf16", wt="fp8", zipf_s=1.2, bias_alpha=C5_BIAS_ALPHA,
+        description="skewed long prefill, fp8 e4m3 experts with 128x128 scales, "
+                    "bf16 activations quantized 1x128 per token"),
+    # ---- reduced parity workloads -------------------------------------------------
+    "p2_prefill_bf16": MoEConfig(
+        name="p2_prefill_bf16", cid=12, T=1000, H=512, E=16, k=6, I=256, I_shared=256,
+        act="bf16", wt="bf16",
+        description="reduced prefill: ~375 rows/expert, so experts split into units"),
+    "p2b_prefill_bf16": MoEConfig(
+        name="p2b_prefill_bf16", cid=22, T=613, H=640, E=32, k=8, I=384, I_shared=384,
+        act="bf16", wt="bf16",
+        description="reduced prefill with H=640 (partial 256-wide N tile) and I=384"),
+    "p3_ep_rank_bf16": MoEConfig(
+        name="p3_ep_rank_bf16", cid=13, T=1500, H=512, E=8, k=1, I=256, I_shared=256,
+        act="bf16", wt="bf16", pretagged=True, e_base=24, E_total=64, T_local=200,
+        description="reduced expert-parallel rank share (experts 24..31 of 64)"),
+    "p4_decode_bf16": MoEConfig(
+        name="p4_decode_bf16", cid=14, T=24, H=512, E=64, k=8, I=256, I_shared=256,
+        act="bf16", wt="bf16", zipf_s=1.1, bias_alpha=0.5,
+        description="reduced decode: many experts with 0-2 rows"),
+    "p5_skewed_fp8": MoEConfig(
+        name="p5_skewed_fp8", cid=15, T=700, H=512, E=16, k=4, I=256, I_shared=256,
+        act="bf16", wt="fp8", zipf_s=1.2, bias_alpha=1.0,
+        description="reduced skewed fp8 layer"),
+    "p1_small_fp32": MoEConfig(
+        name="p1_small_fp32", cid=11, T=150, H=384, E=12, k=3, I=256, I_shared=128,
+        act="f32", wt="f32", x_std=0.02, wg_std=0.02, w_std=0.02,
+        description="fp32 layer with a ragged tail and I != I_shared"),
+}
+
+FULL_CONFIGS = ["c1_tiny_fp32", "c2_prefill_bf16", "c3_ep_rank_bf16",
+                "c4_decode_bf16", "c5_skewed_fp8"]
+SMALL_CONFIGS = ["c1_tiny_fp32", "p1_small_fp32", "p2_prefill_bf16", "p2b_prefill_bf16",
+                 "p3_ep_rank_bf16", "p4_decode_bf16", "p5_skewed_fp8"]
+
+
+def get(name: str, **overrides) -> MoEConfig:
+    cfg = CONFIGS[name]
+    return replace(cfg, **overrides) if overrides else cfg

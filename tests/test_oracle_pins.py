@@ -1,0 +1,364 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each test checks an oracle function against brute force on tiny inputs, a
+closed form, an invariant the pages or the mathematics fix, or an independent
+library routine -- never against a retyped copy of its own formula.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+from oracle import moe
+from synth import configs, inputs
+
+
+# ----------------------------------------------------------------------------- fp8 format
+
+def _all_bf16_values():
+    v = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    return v[np.isfinite(v)]
+
+
+def test_fp8_encode_matches_library_cast_on_every_bf16_value():
+    """Independent routine: torch's float8_e4m3fn cast (round-to-nearest-even) agrees
+    with the oracle encoder on every finite bf16 value inside the format's range."""
+    v = _all_bf16_values()
+    v = v[np.abs(v) <= 464.0]            # beyond 464 the library cast gives NaN, the oracle saturates
+    ref = torch.from_numpy(v.copy()).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(moe.fp8_e4m3fn_encode(v), ref)
+
+
+def test_fp8_encode_random_float32_matches_library_cast():
+    r = np.random.default_rng(7).standard_normal(200_000).astype(np.float32)
+    r = np.concatenate([r * np.float32(0.01), r * np.float32(3.0), r * np.float32(100.0)])
+    r = r[np.abs(r) <= 464.0]
+    ref = torch.from_numpy(r).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(moe.fp8_e4m3fn_encode(r), ref)
+
+
+def test_fp8_decode_matches_library_on_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = moe.fp8_e4m3fn_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    same = (mine == ref) | (np.isnan(mine) & np.isnan(ref))
+    assert same.all()
+
+
+@pytest.mark.parametrize("value,code", [
+    (448.0, 0x7E), (-448.0, 0xFE),          # largest finite magnitude 1.75 * 2^8
+    (1.0, 0x38), (2.0 ** -6, 0x08),         # smallest normal
+    (2.0 ** -9, 0x01),                      # smallest subnormal
+    (1.0625, 0x38),                         # tie between 1 and 1.125 -> even mantissa (1.0)
+    (1.1875, 0x3A),                         # tie between 1.125 and 1.25 -> even mantissa (1.25)
+    (1000.0, 0x7E), (-1e30, 0xFE),          # saturation
+    (2.0 ** -11, 0x00), (-0.0, 0x80),       # underflow to zero keeps the sign
+])
+def test_fp8_encode_closed_form_points(value, code):
+    assert int(moe.fp8_e4m3fn_encode(np.array([value], np.float32))[0]) == code
+
+
+def test_quant_1x128_amax_maps_to_448_and_zero_block():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 384)).astype(np.float32)
+    x[2, 128:256] = 0.0
+    q, s = moe.quant_1x128(x)
+    # [MND §Quantization]: one scale per 128-element activation vector, shape M x ceil(K/128)
+    assert q.shape == (5, 384) and s.shape == (5, 3) and s.dtype == np.float32
+    blocks = x.reshape(5, 3, 128)
+    for m in range(5):
+        for b in range(3):
+            if m == 2 and b == 1:
+                assert s[m, b] == 1.0 and (q[m, 128 * b:128 * b + 128] == 0).all()
+                continue
+            i = int(np.argmax(np.abs(blocks[m, b])))
+            c = int(q[m, 128 * b + i])
+            assert c in (0x7E, 0xFE)                     # amax element is exactly +-448
+            assert (c == 0xFE) == (blocks[m, b, i] < 0)
+
+
+def test_quant_1x128_error_bound():
+    """e4m3 has 3 mantissa bits: relative error of a normal value <= 2^-4."""
+    x = np.random.default_rng(2).standard_normal((64, 256)).astype(np.float32)
+    q, s = moe.quant_1x128(x)
+    d = moe.dequant_1x128(q, s)
+    normal = np.abs(x) >= np.repeat(s, 128, axis=1) * 2.0 ** -6
+    err = np.abs(d - x)
+    assert (err[normal] <= 2.0 ** -4 * np.abs(x[normal]) * (1 + 1e-6)).all()
+    # subnormal range: absolute error <= half the subnormal spacing times the scale
+    assert (err[~normal] <= 0.5 * 2.0 ** -9 * np.repeat(s, 128, axis=1)[~normal] * (1 + 1e-6)).all()
+
+
+def test_dequant_block128_scale_layout():
+    """[MND §Quantization]: a weight [N, K] carries ceil(K/128) x ceil(N/128) scales,
+    one per 128x128 tile.  Put a distinct power of two in each tile and check that
+    exactly that tile is scaled."""
+    N, K = 256, 384
+    q = np.full((N, K), 0x38, dtype=np.uint8)       # every code = 1.0
+    s = np.exp2(np.arange(6, dtype=np.float32)).reshape(2, 3)
+    d = moe.dequant_block128(q, s)
+    for nb in range(2):
+        for kb in range(3):
+            assert (d[nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128] == 2.0 ** (3 * nb + kb)).all()
+
+
+# ----------------------------------------------------------------------------- router
+
+def _brute_topk(z, k):
+    """Enumerate every k-subset; keep the one in which every member beats every
+    non-member (higher score, or equal score and lower id); order it."""
+    E = len(z)
+    beats = lambda a, b: z[a] > z[b] or (z[a] == z[b] and a < b)
+    winners = [S for S in itertools.combinations(range(E), k)
+               if all(beats(a, b) for a in S for b in range(E) if b not in S)]
+    assert len(winners) == 1
+    S = list(winners[0])
+    # order: selection by repeated "best remaining"
+    out = []
+    while S:
+        best = S[0]
+        for c in S[1:]:
+            if beats(c, best):
+                best = c
+        out.append(best)
+        S.remove(best)
+    return out
+
+
+@settings(max_examples=150, deadline=None)
+@given(st.integers(1, 6), st.integers(1, 6), st.data())
+def test_topk_selection_brute_force(T, E, data):
+    k = data.draw(st.integers(1, E))
+    # a small value alphabet forces ties
+    vals = data.draw(st.lists(st.sampled_from([-1.5, -0.25, 0.0, 0.25, 0.5, 2.0]),
+                              min_size=T * E, max_size=T * E))
+    z = np.array(vals, dtype=np.float32).reshape(T, E)
+    idx, w = moe.route_topk(z, None, k)
+    for t in range(T):
+        assert list(idx[t]) == _brute_topk(list(z[t]), k)
+        assert abs(float(w[t].sum()) - 1.0) <= 1e-6     # weights sum to 1
+        assert (w[t] > 0).all()
+        assert len(set(idx[t])) == k                    # k distinct experts
+
+
+def test_topk_weights_closed_form():
+    """sigma(ln 3) = 3/4 and sigma(0) = 1/2, so renormalized weights are 0.6 / 0.4."""
+    z = np.array([[0.0, math.log(3.0), -5.0]], dtype=np.float32)
+    idx, w = moe.route_topk(z, None, 2)
+    assert list(idx[0]) == [1, 0]
+    assert abs(w[0, 0] - 0.6) < 1e-6 and abs(w[0, 1] - 0.4) < 1e-6
+
+
+def test_topk_k_equals_E_and_k_one():
+    z = np.random.default_rng(3).standard_normal((10, 7)).astype(np.float32)
+    idx, w = moe.route_topk(z, None, 7)
+    assert (np.sort(idx, axis=1) == np.arange(7)).all()          # every expert selected
+    assert (np.diff(np.take_along_axis(z, idx, 1), axis=1) <= 0).all()
+    idx1, w1 = moe.route_topk(z, None, 1)
+    assert (idx1[:, 0] == np.argmax(z, axis=1)).all() and (w1 == 1.0).all()
+
+
+def test_topk_bias_shifts_selection():
+    z = np.zeros((1, 4), dtype=np.float32)
+    b = np.array([0.0, 0.0, 1.0, 0.5], dtype=np.float32)
+    idx, w = moe.route_topk(z, b, 2)
+    assert list(idx[0]) == [2, 3]
+    s = [1 / (1 + math.exp(-1.0)), 1 / (1 + math.exp(-0.5))]
+    assert np.allclose(w[0], np.array(s) / sum(s), atol=1e-7)
+
+
+# ----------------------------------------------------------------------------- routing
+
+def _brute_routing(ids, E, e_base):
+    flat = [int(v) - e_base for v in np.asarray(ids).reshape(-1)]
+    R = len(flat)
+    counts = [0] * E
+    sorted_src = []
+    for e in range(E):                    # expert by expert, slots in ascending order
+        for s in range(R):
+            if flat[s] == e:
+                counts[e] += 1
+                sorted_src.append(s)
+    eri = [-1] * R
+    for r, s in enumerate(sorted_src):
+        eri[s] = r
+    return counts, sorted_src, eri
+
+
+@settings(max_examples=150, deadline=None)
+@given(st.integers(0, 7), st.integers(1, 5), st.integers(1, 3), st.integers(0, 3), st.data())
+def test_init_routing_brute_force(T, E, k, e_base, data):
+    ids = np.array(data.draw(st.lists(st.integers(e_base - 1, e_base + E), min_size=T * k,
+                                      max_size=T * k)), dtype=np.int32).reshape(T, k)
+    r = moe.init_routing(ids, E, e_base)
+    counts, sorted_src, eri = _brute_routing(ids, E, e_base)
+    assert list(r["tokens_per_expert"]) == counts
+    assert list(r["sorted_src"]) == sorted_src
+    assert list(r["expanded_row_idx"]) == eri
+    assert list(r["expert_offsets"]) == [sum(counts[:e]) for e in range(E + 1)]
+
+
+def _distinct_topk_ids(rng, T, E, k):
+    return np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(1, 300), st.integers(1, 40), st.data())
+def test_init_routing_invariants(T, E, data):
+    k = data.draw(st.integers(1, min(E, 8)))
+    rng = np.random.default_rng(data.draw(st.integers(0, 2 ** 31)))
+    ids = _distinct_topk_ids(rng, T, E, k)
+    r = moe.init_routing(ids, E)
+    ss, eri, tpe = r["sorted_src"], r["expanded_row_idx"], r["tokens_per_expert"]
+    assert tpe.sum() == T * k                                    # sums to T*k
+    assert np.array_equal(np.bincount(ss // k, minlength=T), np.full(T, k))   # each token k times
+    assert np.array_equal(eri[ss], np.arange(T * k))             # round trip to identity
+    assert np.array_equal(ss[eri], np.arange(T * k))
+    e_of_row = ids.reshape(-1)[ss]
+    assert (np.diff(e_of_row) >= 0).all()                        # grouped by expert
+    same = np.diff(e_of_row) == 0
+    assert (np.diff(ss)[same] > 0).all()                         # stable inside an expert
+
+
+def test_init_routing_base_offset_and_invalid():
+    ids = np.array([[96, 99], [97, 40], [127, 96]], dtype=np.int32)
+    r = moe.init_routing(ids, 32, 96)
+    assert r["n_invalid"] == 1
+    assert r["expanded_row_idx"][3] == -1
+    assert list(r["tokens_per_expert"][:4]) == [2, 1, 0, 1] and r["tokens_per_expert"][31] == 1
+    assert list(r["sorted_src"]) == [0, 5, 2, 1, 4]
+
+
+def test_expand_rows_and_unsort_round_trip():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((50, 8))
+    ids = rng.integers(0, 6, size=(50, 1)).astype(np.int32)
+    r = moe.init_routing(ids, 6)
+    ex = moe.expand_rows(x, r["sorted_src"], 1)
+    for rr, s in enumerate(r["sorted_src"]):
+        assert np.array_equal(ex[rr], x[s])
+    # [R1P] un-sort through argsort(gathered_ids_unsort) restores arrival order exactly,
+    # and equals finalize with k = 1, no weights, no skip
+    assert np.array_equal(moe.unsort(ex, r["sorted_src"]), x)
+    assert np.array_equal(moe.finalize(ex, r["expanded_row_idx"], 1), x)
+
+
+# ----------------------------------------------------------------------------- experts
+
+def _loop_swiglu(a, w13, w2):
+    I = len(w13) // 2
+    H = len(w2)
+    out = []
+    for row in a:
+        h = []
+        for i in range(I):
+            g = sum(row[c] * w13[i][c] for c in range(len(row)))
+            u = sum(row[c] * w13[I + i][c] for c in range(len(row)))
+            h.append(g / (1.0 + math.exp(-g)) * u)
+        out.append([sum(h[i] * w2[o][i] for i in range(I)) for o in range(H)])
+    return np.array(out)
+
+
+def test_swiglu_ffn_matches_explicit_loops():
+    rng = np.random.default_rng(5)
+    a, w13, w2 = rng.standard_normal((3, 5)), rng.standard_normal((6, 5)), rng.standard_normal((5, 3))
+    assert np.allclose(moe.swiglu_ffn(a, w13, w2), _loop_swiglu(a.tolist(), w13.tolist(), w2.tolist()),
+                       rtol=1e-12, atol=1e-12)
+
+
+def test_swiglu_zero_gate_or_up_gives_zero():
+    rng = np.random.default_rng(6)
+    a, w13, w2 = rng.standard_normal((4, 8)), rng.standard_normal((6, 8)), rng.standard_normal((8, 3))
+    wz = w13.copy(); wz[:3] = 0.0                   # silu(0) = 0
+    assert np.all(moe.swiglu_ffn(a, wz, w2) == 0.0)
+    wz = w13.copy(); wz[3:] = 0.0                   # up projection 0
+    assert np.all(moe.swiglu_ffn(a, wz, w2) == 0.0)
+
+
+def test_grouped_ffn_single_group_is_dense_ffn():
+    rng = np.random.default_rng(8)
+    a, w13, w2 = rng.standard_normal((9, 8)), rng.standard_normal((6, 8)), rng.standard_normal((8, 3))
+    y = moe.grouped_ffn(a, np.array([0, 9]), lambda e: (w13, w2))
+    assert np.array_equal(y, moe.swiglu_ffn(a, w13, w2))
+
+
+def test_finalize_matches_explicit_loops():
+    rng = np.random.default_rng(9)
+    T, k, H = 4, 2, 3
+    y = rng.standard_normal((T * k, H))
+    eri = rng.permutation(T * k).astype(np.int32)
+    w = rng.random((T, k))
+    skip = rng.standard_normal((T, H))
+    out = moe.finalize(y, eri, k, w, skip)
+    for t in range(T):
+        for h in range(H):
+            ref = skip[t, h] + sum(w[t, j] * y[eri[t * k + j], h] for j in range(k))
+            assert abs(out[t, h] - ref) < 1e-12
+
+
+def _layer_with(cfg_name, mutate):
+    cfg = configs.get(cfg_name)
+    d = inputs.layer_inputs(cfg)
+    mutate(d)
+    return cfg, d, moe.moe_layer(d)
+
+
+def test_identical_experts_make_output_independent_of_routing():
+    """Sum of weights = 1, so if every expert has the same weights the routed part is
+    FFN(x) whatever the routing: out = shared(x) + FFN(x)."""
+    def same(d):
+        d["w13"][:] = d["w13"][0]
+        d["w2"][:] = d["w2"][0]
+    cfg, d, r = _layer_with("p1_small_fp32", same)
+    x = moe.to_f64(d["x"], cfg.act)
+    ffn = moe.swiglu_ffn(x, moe.to_f64(d["w13"][0], cfg.wt), moe.to_f64(d["w2"][0], cfg.wt))
+    # the float32 weights sum to 1 within a few float32 ulps
+    assert np.abs(r["out"] - (r["shared"] + ffn)).max() <= 1e-6 * np.abs(ffn).max()
+
+
+def test_zero_down_projection_leaves_shared_expert():
+    def zero(d):
+        d["w2"][:] = 0
+    cfg, d, r = _layer_with("p2_prefill_bf16", zero)
+    assert np.array_equal(r["out"], r["shared"])
+
+
+def test_identity_ffn_combine_returns_tokens():
+    """With y = expanded_x (an identity 'FFN'), the combine returns sum_j w_j x_t = x_t."""
+    cfg = configs.get("p2_prefill_bf16")
+    d = inputs.layer_inputs(cfg, with_experts=False)
+    x = moe.to_f64(d["x"], cfg.act)
+    idx, w = moe.route_topk(moe.gate_logits(x, moe.to_f64(d["w_gate"], cfg.act)).astype(np.float32),
+                            None, cfg.k)
+    rt = moe.init_routing(idx, cfg.E)
+    y = moe.expand_rows(x, rt["sorted_src"], cfg.k)
+    out = moe.finalize(y, rt["expanded_row_idx"], cfg.k, w)
+    assert np.allclose(out, x, rtol=1e-6, atol=1e-6)
+
+
+def test_fp8_layer_dequantized_operands_close_to_exact():
+    """The fp8 layer's expanded rows dequantize to the bf16 tokens within the e4m3 bound."""
+    cfg = configs.get("p5_skewed_fp8")
+    d = inputs.layer_inputs(cfg)
+    r = moe.moe_layer(d)
+    a = moe.dequant_1x128(r["expanded_x"], r["expanded_scale"])
+    x = moe.to_f64(d["x"], cfg.act)[r["sorted_src"] // cfg.k]
+    assert np.all(np.abs(a - x) <= 2.0 ** -4 * np.abs(x) + 2.0 ** -9 * np.repeat(r["expanded_scale"], 128, 1))
+
+
+def test_gate_logits_is_plain_product():
+    rng = np.random.default_rng(10)
+    x, wg = rng.standard_normal((3, 4)), rng.standard_normal((5, 4))
+    l = moe.gate_logits(x, wg)
+    for t in range(3):
+        for e in range(5):
+            assert abs(l[t, e] - sum(x[t, h] * wg[e, h] for h in range(4))) < 1e-12
+
+
+def test_bf16_decode_exact():
+    # 0x7F7F is the largest finite bf16: (2 - 2^-7) * 2^127
+    assert moe.bf16_bits_to_f64(np.array([0x3F80, 0xC000, 0x0000, 0x7F7F], np.uint16)).tolist() == \
+        [1.0, -2.0, 0.0, (2.0 - 2.0 ** -7) * 2.0 ** 127]
