@@ -1,0 +1,191 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) DeepSeek-V3/R1-style MoE expert layer.
+ *
+ * One GPU's share of a mixture-of-experts layer: every token is gated to its
+ * top-k routed experts plus one shared expert; the token copies are expanded
+ * and sorted by expert, the per-expert SwiGLU FFNs run as one ragged grouped
+ * GEMM, and the rows are un-permuted and combined with the top-k weights plus
+ * the shared-expert output.
+ *
+ * Sources, cited by short name:
+ *   [MND] page "Lower latency and higher throughput with multi-node DeepSeek
+ *         deployment" (Perplexity, 2025-04-18).
+ *   [R1P] page "CANN/cann-recipes-infer: DeepSeek-R1 prefill optimization"
+ *         (DeepSeek-R1 prefill on Atlas A3).
+ *
+ * Conventions shared by every call
+ *   - Tensor pointers are DEVICE pointers, row-major, 16-byte aligned.  The
+ *     caller allocates and owns every buffer and the workspace; the library
+ *     allocates nothing, frees nothing and keeps no state between calls.
+ *   - Every call only enqueues work on `stream`; none synchronizes or reads
+ *     device memory on the host (routing counts stay on the device, so a call
+ *     sequence can be captured in a HIP graph).  moe_get_error() is the one
+ *     call that synchronizes.
+ *   - bf16 is passed as raw 16-bit patterns, fp8 as OCP E4M3FN bytes
+ *     (max 448), indices as int32.  Weights are [out, in] (the reduction
+ *     dimension is contiguous), as both matrix-core operands want them.
+ *   - Host-side validation failures return a negative moe_status at once and
+ *     enqueue nothing.  A failed kernel launch returns MOE_EHIP.  Bad data found
+ *     on the device (an expert id outside [e_base, e_base + E)) is recorded in
+ *     the workspace and reported by moe_get_error().
+ *   - Calls are reentrant: concurrent calls are fine on different streams with
+ *     different workspaces.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,        /* null pointer, bad size, k > E, ... */
+  MOE_EUNSUPPORTED = -2,  /* dtype combination or size the kernels do not cover */
+  MOE_EWORKSPACE = -3,    /* workspace smaller than the size query returned */
+  MOE_EHIP = -4,          /* a HIP launch or runtime call failed */
+  MOE_EDEVICE = -5        /* device-detected bad input (see moe_get_error) */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/* Problem shape of one call.
+ *   T        tokens (for re-routing: received rows)
+ *   H        hidden size; a multiple of 128 for bf16/fp8, of 4 for fp32
+ *   E        routed experts held by this call (the local experts)
+ *   k        routed experts per token, 1 <= k <= E (1 for re-routing)
+ *   I        routed SwiGLU intermediate size (multiple of 128 for bf16/fp8)
+ *   I_shared shared-expert intermediate size (multiple of 128 for bf16/fp8)
+ *   act      activation dtype: MOE_F32 or MOE_BF16
+ *   wt       expert-weight dtype: MOE_F32 (with act F32), MOE_BF16 (with act
+ *            BF16) or MOE_FP8_E4M3 (with act BF16; the expert inputs are then
+ *            quantized to fp8 with one fp32 scale per 1x128 vector)           */
+typedef struct {
+  int32_t T, H, E, k, I, I_shared;
+  int32_t act, wt;
+} moe_shape;
+
+/* Workspace bytes needed by moe_layer and moe_init_routing for shape `s`
+ * (0 if the shape is invalid). */
+size_t moe_workspace_bytes(const moe_shape* s);
+
+/* Workspace bytes needed by moe_grouped_ffn for G groups and at most R_max rows. */
+size_t moe_grouped_ffn_workspace_bytes(const moe_shape* s, int32_t G, int32_t R_max);
+
+/* Gate and top-k router.  [MND §Expert Parallelism]: each token is sent to k
+ * different routed experts whose outputs are weighted-summed; [MND §MoE Router]:
+ * a sort that tracks indices yields the top-k expert ids and scores per token.
+ *   x       [T, H]  act           tokens
+ *   w_gate  [E, H]  act           gate matrix
+ *   bias    [E]     fp32 or NULL  added to the logits: z = logit + bias
+ *   logits  [T, E]  fp32          OUT: x . w_gate^T (fp32 accumulate), required
+ *   topk_idx[T, k]  int32         OUT: the k largest z, descending; equal z -> lower id
+ *   topk_w  [T, k]  fp32          OUT: sigmoid(z) of the selected, renormalized to sum 1
+ *   ws      workspace of moe_workspace_bytes(s) bytes                          */
+moe_status moe_gate_topk(const moe_shape* s, const void* x, const void* w_gate,
+                         const float* bias, float* logits, int32_t* topk_idx,
+                         float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Expand-and-sort routing.  [R1P §MoE deployment strategy optimization]:
+ * init-routing expands every token once per chosen expert and sorts the copies
+ * by expert, giving expanded_x, tokens_per_expert and expanded_row_idx (the
+ * map that later restores token order); re-routing is the same sort with k = 1
+ * over received, unordered rows.
+ *   x                 [T, H] act     tokens (or received rows); may be NULL when
+ *                                    expanded_x is NULL (routing only)
+ *   ids               [T, k] int32   global expert ids; local id = id - e_base
+ *   expanded_x        [T*k, H]       OUT or NULL: row r = x[sorted_src[r] / k];
+ *                                    act dtype, or fp8 codes when s->wt is fp8
+ *   expanded_scale    [T*k, H/128]   OUT fp32 1x128 scales (fp8 only, else NULL)
+ *   expanded_row_idx  [T*k] int32    OUT: slot s = t*k + j -> destination row, -1
+ *                                    for an invalid id
+ *   sorted_src        [T*k] int32    OUT or NULL: destination row -> slot s
+ *                                    (entries past expert_offsets[E] are unspecified)
+ *   tokens_per_expert [E] int32      OUT: valid slots per local expert
+ *   expert_offsets    [E+1] int32    OUT: exclusive prefix sum of tokens_per_expert
+ * Rows of one expert keep ascending slot order, so every output is unique
+ * and bit-reproducible.  Slots with an id outside [e_base, e_base + E) are left
+ * out and flagged for moe_get_error().                                          */
+moe_status moe_init_routing(const moe_shape* s, const void* x, const int32_t* ids,
+                            int32_t e_base, void* expanded_x, float* expanded_scale,
+                            int32_t* expanded_row_idx, int32_t* sorted_src,
+                            int32_t* tokens_per_expert, int32_t* expert_offsets,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Grouped SwiGLU experts.  [MND §Roofline / GroupGEMM]: g groups, group i has
+ * m_i rows and multiplies [m_i, k] x [k, n]; here each group runs
+ * y = (silu(a W1^T) * (a W3^T)) W2^T with its own weights.  The group sizes
+ * are read on the device ([MND §Quantization]: kernels read the routed token
+ * counts instead of sizing work by the buffer bound).
+ *   G              number of groups (experts)
+ *   R_max          rows in a and y (>= group_offsets[G], which the kernels read)
+ *   a              [R_max, H]  act, or fp8 codes when s->wt is fp8
+ *   a_scale        [R_max, H/128] fp32 (fp8 only, else NULL)
+ *   group_offsets  [G+1] int32 device array, non-decreasing, offsets[0] = 0
+ *   w13            [G, 2I, H]  wt: rows 0..I-1 = W1 (gate), I..2I-1 = W3 (up)
+ *   w13_scale      [G, 2I/128, H/128] fp32 (fp8 only, else NULL)
+ *   w2             [G, H, I]   wt
+ *   w2_scale       [G, H/128, I/128] fp32 (fp8 only, else NULL)
+ *   y              [R_max, H]  act  OUT (rows past offsets[G] are not written)
+ *   ws             workspace of moe_grouped_ffn_workspace_bytes(s, G, R_max)  */
+moe_status moe_grouped_ffn(const moe_shape* s, int32_t G, int32_t R_max, const void* a,
+                           const float* a_scale, const int32_t* group_offsets,
+                           const void* w13, const float* w13_scale, const void* w2,
+                           const float* w2_scale, void* y, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* Un-permute and combine.  [R1P §MoE deployment strategy optimization]:
+ * finalize-routing restores token order through expanded_row_idx and forms
+ * the weighted sum of the routed outputs plus the shared-expert output:
+ *   out[t] = skip[t] + sum_j topk_w[t, j] * y[expanded_row_idx[t*k + j]]
+ * accumulated in fp32 and rounded once.  With k = 1, topk_w = NULL and
+ * skip = NULL this is the plain un-sort of re-routed rows.
+ *   y                [R, H]  act  (R >= the largest index used)
+ *   skip             [T, H]  act or NULL
+ *   topk_w           [T, k]  fp32 or NULL (weights 1)
+ *   expanded_row_idx [T*k]   int32; entries < 0 contribute nothing
+ *   out              [T, H]  act  OUT                                         */
+moe_status moe_finalize_routing(const moe_shape* s, const void* y, const void* skip,
+                                const float* topk_w, const int32_t* expanded_row_idx,
+                                void* out, hipStream_t stream);
+
+/* Weights of one MoE layer. */
+typedef struct {
+  const void* w_gate;      /* [E, H] act                                       */
+  const void* w13;         /* [E, 2I, H] wt                                    */
+  const void* w2;          /* [E, H, I] wt                                     */
+  const void* sh_w13;      /* [2*I_shared, H] act (shared expert, never fp8)   */
+  const void* sh_w2;       /* [H, I_shared] act                                */
+  const float* w13_scale;  /* [E, 2I/128, H/128] (fp8 only, else NULL)         */
+  const float* w2_scale;   /* [E, H/128, I/128]  (fp8 only, else NULL)         */
+  const float* bias;       /* [E] gate-logit bias or NULL                      */
+} moe_weights;
+
+/* The whole layer: gate + top-k, init-routing, grouped experts, shared expert
+ * and finalize-routing, enqueued on one stream with no host synchronization.
+ *   x        [T, H] act
+ *   out      [T, H] act  OUT
+ *   topk_idx [T, k] int32 OUT or NULL;  topk_w [T, k] fp32 OUT or NULL;
+ *   logits   [T, E] fp32  OUT or NULL
+ *   ws       workspace of moe_workspace_bytes(s) bytes                         */
+moe_status moe_layer(const moe_shape* s, const moe_weights* w, const void* x, void* out,
+                     int32_t* topk_idx, float* topk_w, float* logits, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+/* Waits for `stream`, then reads and clears the device error word of `ws`:
+ * MOE_EDEVICE if a routing call since the last check saw an expert id outside
+ * its [e_base, e_base + E) range, else MOE_OK (MOE_EHIP on a runtime error). */
+moe_status moe_get_error(void* ws, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* moe_status_str(moe_status st);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

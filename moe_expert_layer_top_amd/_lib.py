@@ -1,0 +1,171 @@
+"""ctypes binding of ``libmoe.so`` -- argument marshalling only.
+
+Every step of the layer runs in the HIP kernels behind the C ABI declared in
+``include/moe.h``; this module converts torch tensors to device pointers and the
+current torch stream to a ``hipStream_t``, and raises on a non-OK status.  It
+never computes anything itself, and it fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads torch's HIP runtime first, so libmoe.so binds to the same one
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP, MOE_EDEVICE = 0, -1, -2, -3, -4, -5
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
+
+EXPORTS = [
+    "moe_workspace_bytes", "moe_grouped_ffn_workspace_bytes", "moe_gate_topk", "moe_init_routing",
+    "moe_grouped_ffn", "moe_finalize_routing", "moe_layer", "moe_get_error", "moe_status_str",
+]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} ({status})")
+
+
+class moe_shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("I", ctypes.c_int32), ("I_shared", ctypes.c_int32),
+                ("act", ctypes.c_int32), ("wt", ctypes.c_int32)]
+
+
+class moe_weights(ctypes.Structure):
+    _fields_ = [("w_gate", ctypes.c_void_p), ("w13", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("sh_w13", ctypes.c_void_p), ("sh_w2", ctypes.c_void_p),
+                ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
+                ("bias", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run `python -m moe_expert_layer_top_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, S, I32, SZ = ctypes.c_void_p, ctypes.POINTER(moe_shape), ctypes.c_int32, ctypes.c_size_t
+        sig = {
+            "moe_workspace_bytes": (SZ, [S]),
+            "moe_grouped_ffn_workspace_bytes": (SZ, [S, I32, I32]),
+            "moe_gate_topk": (I32, [S, P, P, P, P, P, P, P, SZ, P]),
+            "moe_init_routing": (I32, [S, P, P, I32, P, P, P, P, P, P, P, SZ, P]),
+            "moe_grouped_ffn": (I32, [S, I32, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
+            "moe_finalize_routing": (I32, [S, P, P, P, P, P, P]),
+            "moe_layer": (I32, [S, ctypes.POINTER(moe_weights), P, P, P, P, P, P, SZ, P]),
+            "moe_get_error": (I32, [P, P]),
+            "moe_status_str": (ctypes.c_char_p, [I32]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().moe_status_str(int(status)).decode()
+
+
+def shape(T, H, E, k, I, I_shared, act="bf16", wt="bf16") -> moe_shape:
+    return moe_shape(int(T), int(H), int(E), int(k), int(I), int(I_shared),
+                     DTYPE_CODES[act] if isinstance(act, str) else int(act),
+                     DTYPE_CODES[wt] if isinstance(wt, str) else int(wt))
+
+
+def shape_of(cfg) -> moe_shape:
+    """moe_shape of a workload configuration (synth.configs.MoEConfig)."""
+    return shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared, cfg.act, cfg.wt)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError("tensor must live in device memory")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(st: int, where: str):
+    if st != MOE_OK:
+        raise MoEError(st, where)
+
+
+def moe_workspace_bytes(s: moe_shape) -> int:
+    return lib().moe_workspace_bytes(ctypes.byref(s))
+
+
+def moe_grouped_ffn_workspace_bytes(s: moe_shape, G: int, R_max: int) -> int:
+    return lib().moe_grouped_ffn_workspace_bytes(ctypes.byref(s), int(G), int(R_max))
+
+
+def moe_gate_topk(s, x, w_gate, bias, logits, topk_idx, topk_w, ws, stream=None):
+    _check(lib().moe_gate_topk(ctypes.byref(s), _ptr(x), _ptr(w_gate), _ptr(bias), _ptr(logits),
+                               _ptr(topk_idx), _ptr(topk_w), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(stream)), "moe_gate_topk")
+
+
+def moe_init_routing(s, x, ids, e_base, expanded_x, expanded_scale, expanded_row_idx, sorted_src,
+                     tokens_per_expert, expert_offsets, ws, stream=None):
+    _check(lib().moe_init_routing(ctypes.byref(s), _ptr(x), _ptr(ids), int(e_base), _ptr(expanded_x),
+                                  _ptr(expanded_scale), _ptr(expanded_row_idx), _ptr(sorted_src),
+                                  _ptr(tokens_per_expert), _ptr(expert_offsets), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_init_routing")
+
+
+def moe_grouped_ffn(s, G, R_max, a, a_scale, group_offsets, w13, w13_scale, w2, w2_scale, y, ws,
+                    stream=None):
+    _check(lib().moe_grouped_ffn(ctypes.byref(s), int(G), int(R_max), _ptr(a), _ptr(a_scale),
+                                 _ptr(group_offsets), _ptr(w13), _ptr(w13_scale), _ptr(w2),
+                                 _ptr(w2_scale), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(stream)), "moe_grouped_ffn")
+
+
+def moe_finalize_routing(s, y, skip, topk_w, expanded_row_idx, out, stream=None):
+    _check(lib().moe_finalize_routing(ctypes.byref(s), _ptr(y), _ptr(skip), _ptr(topk_w),
+                                      _ptr(expanded_row_idx), _ptr(out), _stream(stream)),
+           "moe_finalize_routing")
+
+
+def weights(w_gate, w13, w2, sh_w13, sh_w2, w13_scale=None, w2_scale=None, bias=None) -> moe_weights:
+    return moe_weights(_ptr(w_gate), _ptr(w13), _ptr(w2), _ptr(sh_w13), _ptr(sh_w2),
+                       _ptr(w13_scale), _ptr(w2_scale), _ptr(bias))
+
+
+def moe_layer(s, w: moe_weights, x, out, topk_idx, topk_w, logits, ws, stream=None):
+    _check(lib().moe_layer(ctypes.byref(s), ctypes.byref(w), _ptr(x), _ptr(out), _ptr(topk_idx),
+                           _ptr(topk_w), _ptr(logits), _ptr(ws), ws.numel() * ws.element_size(),
+                           _stream(stream)), "moe_layer")
+
+
+def moe_get_error(ws, stream=None) -> int:
+    """MOE_OK or MOE_EDEVICE for the last routing call on this workspace (synchronizes)."""
+    st = lib().moe_get_error(_ptr(ws), _stream(stream))
+    if st not in (MOE_OK, MOE_EDEVICE):
+        raise MoEError(st, "moe_get_error")
+    return st
+
+
+def moe_status_str(st: int) -> str:
+    return status_str(st)

@@ -1,0 +1,434 @@
+// C ABI of the MoE layer: argument validation, workspace layout and the launch
+// sequence of each call.  Declarations and contracts are in include/moe.h.
+//
+// [MND] = page "Lower latency and higher throughput with multi-node DeepSeek
+//         deployment"; [R1P] = page "CANN/cann-recipes-infer: DeepSeek-R1
+//         prefill optimization".
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cstdint>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+using moe::GemmArgs;
+using moe::Unit;
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 64;
+constexpr int kGateMaxSplits = 64;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int elem_bytes(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 2 : 1; }
+
+bool dtypes_ok(const moe_shape* s) {
+  if (s->act == MOE_F32) return s->wt == MOE_F32;
+  if (s->act == MOE_BF16) return s->wt == MOE_BF16 || s->wt == MOE_FP8_E4M3;
+  return false;
+}
+
+// Shape checks shared by every call (I sizes are checked by the calls that use them).
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return MOE_EINVAL;
+  if (s->T < 0 || s->H <= 0 || s->E < 1 || s->k < 1 || s->k > s->E) return MOE_EINVAL;
+  if (s->act != MOE_F32 && s->act != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (s->wt != MOE_F32 && s->wt != MOE_BF16 && s->wt != MOE_FP8_E4M3) return MOE_EUNSUPPORTED;
+  if (!dtypes_ok(s)) return MOE_EUNSUPPORTED;
+  if (s->E > kMaxE || s->k > kMaxK) return MOE_EUNSUPPORTED;
+  if (s->act == MOE_F32 ? (s->H % 4) : (s->H % 128)) return MOE_EUNSUPPORTED;
+  if (static_cast<long long>(s->T) * s->k > INT32_MAX / 2) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_inter(const moe_shape* s, int I) {
+  if (I <= 0) return MOE_EINVAL;
+  if (s->act != MOE_F32 && I % 128) return MOE_EUNSUPPORTED;
+  // weight panels are addressed with 32-bit offsets inside one expert
+  if (2LL * I * s->H * elem_bytes(s->wt) >= (1LL << 31)) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+int nseg_of(long long R) { return static_cast<int>((R + moe::kSegSlots - 1) / moe::kSegSlots); }
+
+// ------------------------------------------------------------------ gate split-k
+struct GatePlan {
+  int splits, k_chunk;
+};
+
+GatePlan gate_plan(const moe_shape* s) {
+  if (s->act == MOE_F32) return {1, s->H};
+  const int bm = moe::gemm_block_m(moe::CFG_GATE, false);
+  const int mtiles = std::max(1, (s->T + bm - 1) / bm);
+  const int ksteps = s->H / 64;
+  int splits = std::min(ksteps, std::max(1, 512 / mtiles));
+  splits = std::min(splits, kGateMaxSplits);
+  const int steps_per = (ksteps + splits - 1) / splits;
+  splits = (ksteps + steps_per - 1) / steps_per;
+  return {splits, steps_per * 64};
+}
+
+// ------------------------------------------------------------------ grouped FFN plan
+moe::GemmCfg ffn_cfg(int G, int R_max) {
+  // decode-sized groups (a few rows each) take the short tile, prefill the tall one
+  return (G > 0 && R_max <= 64LL * G) ? moe::CFG_SMALL : moe::CFG_BIG;
+}
+
+int max_units(moe::GemmCfg cfg, bool fp8, int G, int R_max) {
+  const int bm = moe::gemm_block_m(cfg, fp8);
+  return R_max / bm + std::min(G, R_max);
+}
+
+struct FfnLayout {
+  size_t units, n_units, h, h_scale, total;
+};
+
+FfnLayout ffn_layout(const moe_shape* s, int G, int R_max, int I) {
+  FfnLayout L{};
+  size_t o = 0;
+  if (s->act == MOE_F32) {
+    L.h = o;
+    o += align_up(static_cast<size_t>(R_max) * I * 4);
+    L.total = o;
+    return L;
+  }
+  const moe::GemmCfg cfg = ffn_cfg(G, R_max);
+  L.units = o;
+  o += align_up(static_cast<size_t>(std::max(1, max_units(cfg, s->wt == MOE_FP8_E4M3, G, R_max))) *
+                 sizeof(Unit));
+  L.n_units = o;
+  o += kAlign;
+  L.h = o;
+  const bool fp8 = s->wt == MOE_FP8_E4M3;
+  o += align_up(static_cast<size_t>(R_max) * I * (fp8 ? 1 : 2));
+  L.h_scale = o;
+  if (fp8) o += align_up(static_cast<size_t>(R_max) * (I / 128) * 4);
+  L.total = o;
+  return L;
+}
+
+// ------------------------------------------------------------------ layer layout
+struct Layout {
+  size_t err, seg_err, part, logits, idx, w, counts, tpe, offsets, eri, sorted_src, ex, ex_scale,
+      y, ffn, sh_out, sh_ffn, total;
+};
+
+Layout layer_layout(const moe_shape* s) {
+  Layout L{};
+  const size_t T = static_cast<size_t>(s->T), E = static_cast<size_t>(s->E);
+  const size_t R = T * s->k, H = static_cast<size_t>(s->H);
+  const GatePlan gp = gate_plan(s);
+  const bool fp8 = s->wt == MOE_FP8_E4M3;
+  const int ab = elem_bytes(s->act);
+  size_t o = 0;
+  L.err = o;           o += kAlign;
+  L.seg_err = o;       o += align_up(static_cast<size_t>(std::max(1, nseg_of(R))) * 4);
+  L.part = o;          o += align_up(static_cast<size_t>(gp.splits) * T * E * 4);
+  L.logits = o;        o += align_up(T * E * 4);
+  L.idx = o;           o += align_up(R * 4);
+  L.w = o;             o += align_up(R * 4);
+  L.counts = o;        o += align_up(static_cast<size_t>(std::max(1, nseg_of(R))) * E * 4);
+  L.tpe = o;           o += align_up(E * 4);
+  L.offsets = o;       o += align_up((E + 1) * 4);
+  L.eri = o;           o += align_up(R * 4);
+  L.sorted_src = o;    o += align_up(R * 4);
+  L.ex = o;            o += align_up(R * H * (fp8 ? 1 : ab));
+  L.ex_scale = o;      if (fp8) o += align_up(R * (H / 128) * 4);
+  L.y = o;             o += align_up(R * H * ab);
+  L.ffn = o;           o += ffn_layout(s, s->E, static_cast<int>(R), s->I).total;
+  L.sh_out = o;        o += align_up(T * H * ab);
+  moe_shape sh = *s;
+  sh.wt = s->act;  // the shared expert is never fp8
+  L.sh_ffn = o;        o += ffn_layout(&sh, 1, s->T, s->I_shared).total;
+  L.total = o;
+  return L;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<uint8_t*>(ws) + off);
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+// ------------------------------------------------------------------ launch sequences
+moe_status run_gate_topk(const moe_shape* s, const void* x, const void* w_gate, const float* bias,
+                         float* logits, int32_t* idx, float* w, float* part, hipStream_t st) {
+  const GatePlan gp = gate_plan(s);
+  hipError_t e;
+  if (s->act == MOE_F32) {
+    e = moe::launch_gemm_nt_f32(static_cast<const float*>(x), static_cast<const float*>(w_gate),
+                                part, s->T, s->E, s->H, st);
+  } else {
+    GemmArgs a{};
+    a.A = static_cast<const uint8_t*>(x);
+    a.lda = static_cast<long long>(s->H) * 2;
+    a.B = static_cast<const uint8_t*>(w_gate);
+    a.ldb = static_cast<long long>(s->H) * 2;
+    a.b_group = 0;
+    a.C = part;
+    a.ldc = s->E;
+    a.c_split = static_cast<long long>(s->T) * s->E;
+    a.uniform_rows = s->T;
+    a.N = s->E;
+    a.K = s->H;
+    a.n_tiles = (s->E + moe::gemm_block_n(moe::CFG_GATE) - 1) / moe::gemm_block_n(moe::CFG_GATE);
+    a.splits = gp.splits;
+    a.k_chunk = gp.k_chunk;
+    const int bm = moe::gemm_block_m(moe::CFG_GATE, false);
+    e = s->T > 0 ? moe::launch_gemm(moe::CFG_GATE, moe::EPI_STORE_F32, false, a,
+                                    (s->T + bm - 1) / bm, st)
+                 : hipSuccess;
+  }
+  if (e != hipSuccess) return MOE_EHIP;
+  return hip_status(moe::launch_topk(part, gp.splits, static_cast<long long>(s->T) * s->E, s->T,
+                                     s->E, s->k, bias, logits, idx, w, st));
+}
+
+struct FfnIo {
+  const void* a;
+  const float* a_scale;
+  const int32_t* offsets;  // NULL: one group of R_max rows
+  const void* w13;
+  const float* w13_scale;
+  const void* w2;
+  const float* w2_scale;
+  void* y;
+};
+
+moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io, void* ws,
+                   hipStream_t st) {
+  if (R_max == 0) return MOE_OK;
+  const FfnLayout L = ffn_layout(s, G, R_max, I);
+  const int H = s->H;
+  if (s->act == MOE_F32) {
+    return hip_status(moe::launch_grouped_ffn_f32(
+        static_cast<const float*>(io.a), io.offsets, G, R_max, static_cast<const float*>(io.w13),
+        static_cast<const float*>(io.w2), at<float>(ws, L.h), static_cast<float*>(io.y), H, I, st));
+  }
+  const bool fp8 = s->wt == MOE_FP8_E4M3;
+  const int eb = fp8 ? 1 : 2;
+  const moe::GemmCfg cfg = ffn_cfg(G, R_max);
+  const int bm = moe::gemm_block_m(cfg, fp8);
+  Unit* units = at<Unit>(ws, L.units);
+  int32_t* n_units = at<int32_t>(ws, L.n_units);
+  int mu;
+  if (io.offsets) {
+    mu = max_units(cfg, fp8, G, R_max);
+    hipError_t e = moe::launch_plan(io.offsets, G, 0, bm, std::max(1, mu), units, n_units, st);
+    if (e != hipSuccess) return MOE_EHIP;
+  } else {
+    mu = (R_max + bm - 1) / bm;
+  }
+  GemmArgs g1{};
+  g1.A = static_cast<const uint8_t*>(io.a);
+  g1.lda = static_cast<long long>(H) * eb;
+  g1.a_scale = io.a_scale;
+  g1.a_scale_ld = H / 128;
+  g1.B = static_cast<const uint8_t*>(io.w13);
+  g1.ldb = static_cast<long long>(H) * eb;
+  g1.b_group = 2LL * I * H * eb;
+  g1.b_scale = io.w13_scale;
+  g1.b_scale_group = static_cast<long long>(2 * I / 128) * (H / 128);
+  g1.b_scale_ld = H / 128;
+  g1.C = at<uint8_t>(ws, L.h);
+  g1.ldc = I;
+  g1.c_scale = fp8 ? at<float>(ws, L.h_scale) : nullptr;
+  g1.c_scale_ld = I / 128;
+  g1.units = units;
+  g1.n_units = n_units;
+  g1.uniform_rows = io.offsets ? 0 : R_max;
+  g1.N = I;
+  g1.K = H;
+  g1.up_off = I;
+  g1.n_tiles = I / 128;
+  g1.splits = 1;
+  g1.k_chunk = H;
+  hipError_t e = moe::launch_gemm(cfg, fp8 ? moe::EPI_SWIGLU_FP8 : moe::EPI_SWIGLU_BF16, fp8, g1,
+                                  mu, st);
+  if (e != hipSuccess) return MOE_EHIP;
+  GemmArgs g2 = g1;
+  g2.A = at<uint8_t>(ws, L.h);
+  g2.lda = static_cast<long long>(I) * eb;
+  g2.a_scale = fp8 ? at<float>(ws, L.h_scale) : nullptr;
+  g2.a_scale_ld = I / 128;
+  g2.B = static_cast<const uint8_t*>(io.w2);
+  g2.ldb = static_cast<long long>(I) * eb;
+  g2.b_group = static_cast<long long>(H) * I * eb;
+  g2.b_scale = io.w2_scale;
+  g2.b_scale_group = static_cast<long long>(H / 128) * (I / 128);
+  g2.b_scale_ld = I / 128;
+  g2.C = io.y;
+  g2.ldc = H;
+  g2.c_scale = nullptr;
+  g2.N = H;
+  g2.K = I;
+  g2.up_off = 0;
+  g2.n_tiles = (H + moe::gemm_block_n(cfg) - 1) / moe::gemm_block_n(cfg);
+  g2.k_chunk = I;
+  return hip_status(moe::launch_gemm(cfg, moe::EPI_STORE_BF16, fp8, g2, mu, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK || check_inter(s, s->I) != MOE_OK) return 0;
+  moe_shape sh = *s;
+  sh.wt = s->act;
+  if (check_inter(&sh, s->I_shared) != MOE_OK) return 0;
+  return layer_layout(s).total;
+}
+
+size_t moe_grouped_ffn_workspace_bytes(const moe_shape* s, int32_t G, int32_t R_max) {
+  if (check_shape(s) != MOE_OK || check_inter(s, s->I) != MOE_OK || G < 1 || R_max < 0) return 0;
+  return std::max<size_t>(ffn_layout(s, G, R_max, s->I).total, kAlign);
+}
+
+moe_status moe_gate_topk(const moe_shape* s, const void* x, const void* w_gate, const float* bias,
+                         float* logits, int32_t* topk_idx, float* topk_w, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->T > 0 && (!x || !w_gate || !logits || !topk_idx || !topk_w)) return MOE_EINVAL;
+  if (!ws) return MOE_EINVAL;
+  const size_t need = moe_workspace_bytes(s);
+  if (need == 0) return MOE_EINVAL;
+  if (ws_bytes < need) return MOE_EWORKSPACE;
+  if (s->T == 0) return MOE_OK;
+  const Layout L = layer_layout(s);
+  return run_gate_topk(s, x, w_gate, bias, logits, topk_idx, topk_w, at<float>(ws, L.part), stream);
+}
+
+moe_status moe_init_routing(const moe_shape* s, const void* x, const int32_t* ids, int32_t e_base,
+                            void* expanded_x, float* expanded_scale, int32_t* expanded_row_idx,
+                            int32_t* sorted_src, int32_t* tokens_per_expert,
+                            int32_t* expert_offsets, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  const bool fp8 = s->wt == MOE_FP8_E4M3;
+  if (!tokens_per_expert || !expert_offsets || !ws) return MOE_EINVAL;
+  if (s->T > 0 && (!ids || !expanded_row_idx)) return MOE_EINVAL;
+  if (expanded_x && s->T > 0 && !x) return MOE_EINVAL;
+  if (expanded_x && fp8 && !expanded_scale) return MOE_EINVAL;
+  const size_t need = moe_workspace_bytes(s);
+  if (need == 0) return MOE_EINVAL;
+  if (ws_bytes < need) return MOE_EWORKSPACE;
+  const Layout L = layer_layout(s);
+  const long long R = static_cast<long long>(s->T) * s->k;
+  hipError_t e = moe::launch_routing(ids, R, e_base, s->E, at<int32_t>(ws, L.counts),
+                                     at<int32_t>(ws, L.seg_err), at<int32_t>(ws, L.err),
+                                     expanded_row_idx, sorted_src, tokens_per_expert,
+                                     expert_offsets, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  if (expanded_x && s->T > 0) {
+    e = moe::launch_expand(x, s->T, s->H, s->k, elem_bytes(s->act), fp8, expanded_row_idx,
+                           expanded_x, expanded_scale, stream);
+    if (e != hipSuccess) return MOE_EHIP;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_grouped_ffn(const moe_shape* s, int32_t G, int32_t R_max, const void* a,
+                           const float* a_scale, const int32_t* group_offsets, const void* w13,
+                           const float* w13_scale, const void* w2, const float* w2_scale, void* y,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if ((st = check_inter(s, s->I)) != MOE_OK) return st;
+  if (G < 1 || R_max < 0) return MOE_EINVAL;
+  const bool fp8 = s->wt == MOE_FP8_E4M3;
+  if (!group_offsets || !ws) return MOE_EINVAL;
+  if (R_max > 0 && (!a || !w13 || !w2 || !y)) return MOE_EINVAL;
+  if (fp8 && R_max > 0 && (!a_scale || !w13_scale || !w2_scale)) return MOE_EINVAL;
+  if (ws_bytes < moe_grouped_ffn_workspace_bytes(s, G, R_max)) return MOE_EWORKSPACE;
+  FfnIo io{a, a_scale, group_offsets, w13, w13_scale, w2, w2_scale, y};
+  return run_ffn(s, G, R_max, s->I, io, ws, stream);
+}
+
+moe_status moe_finalize_routing(const moe_shape* s, const void* y, const void* skip,
+                                const float* topk_w, const int32_t* expanded_row_idx, void* out,
+                                hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;
+  if (!y || !expanded_row_idx || !out) return MOE_EINVAL;
+  return hip_status(moe::launch_finalize(y, skip, topk_w, expanded_row_idx, out, s->T, s->H, s->k,
+                                         elem_bytes(s->act), stream));
+}
+
+moe_status moe_layer(const moe_shape* s, const moe_weights* w, const void* x, void* out,
+                     int32_t* topk_idx, float* topk_w, float* logits, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if ((st = check_inter(s, s->I)) != MOE_OK) return st;
+  if (!w || !ws) return MOE_EINVAL;
+  const bool fp8 = s->wt == MOE_FP8_E4M3;
+  if (s->T > 0 && (!x || !out || !w->w_gate || !w->w13 || !w->w2 || !w->sh_w13 || !w->sh_w2))
+    return MOE_EINVAL;
+  if (fp8 && (!w->w13_scale || !w->w2_scale)) return MOE_EINVAL;
+  const size_t need = moe_workspace_bytes(s);
+  if (need == 0) return MOE_EINVAL;
+  if (ws_bytes < need) return MOE_EWORKSPACE;
+  if (s->T == 0) return MOE_OK;
+  const Layout L = layer_layout(s);
+  float* lg = logits ? logits : at<float>(ws, L.logits);
+  int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
+  float* tw = topk_w ? topk_w : at<float>(ws, L.w);
+  // gate + router  ([MND §Expert Parallelism], [MND §MoE Router])
+  st = run_gate_topk(s, x, w->w_gate, w->bias, lg, idx, tw, at<float>(ws, L.part), stream);
+  if (st != MOE_OK) return st;
+  // first routing: expand and sort by expert  ([R1P §MoE deployment strategy optimization])
+  int32_t* eri = at<int32_t>(ws, L.eri);
+  int32_t* offs = at<int32_t>(ws, L.offsets);
+  st = moe_init_routing(s, x, idx, 0, at<void>(ws, L.ex), fp8 ? at<float>(ws, L.ex_scale) : nullptr,
+                        eri, at<int32_t>(ws, L.sorted_src), at<int32_t>(ws, L.tpe), offs, ws,
+                        ws_bytes, stream);
+  if (st != MOE_OK) return st;
+  // routed experts as one grouped GEMM over the expert-sorted rows
+  const int R = s->T * s->k;
+  FfnIo io{at<void>(ws, L.ex), fp8 ? at<float>(ws, L.ex_scale) : nullptr, offs, w->w13,
+           w->w13_scale, w->w2, w->w2_scale, at<void>(ws, L.y)};
+  st = run_ffn(s, s->E, R, s->I, io, at<void>(ws, L.ffn), stream);
+  if (st != MOE_OK) return st;
+  // shared expert on every token ([MND §Expert Parallelism]: its output is added)
+  moe_shape sh = *s;
+  sh.wt = s->act;
+  FfnIo sio{x, nullptr, nullptr, w->sh_w13, nullptr, w->sh_w2, nullptr, at<void>(ws, L.sh_out)};
+  st = run_ffn(&sh, 1, s->T, s->I_shared, sio, at<void>(ws, L.sh_ffn), stream);
+  if (st != MOE_OK) return st;
+  // finalize: un-permute, weighted sum, plus the shared expert
+  return moe_finalize_routing(s, at<void>(ws, L.y), at<void>(ws, L.sh_out), tw, eri, out, stream);
+}
+
+moe_status moe_get_error(void* ws, hipStream_t stream) {
+  if (!ws) return MOE_EINVAL;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MOE_EHIP;
+  int32_t v = 0;
+  if (hipMemcpy(&v, ws, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MOE_EHIP;
+  if (hipMemset(ws, 0, sizeof(v)) != hipSuccess) return MOE_EHIP;
+  return v ? MOE_EDEVICE : MOE_OK;
+}
+
+const char* moe_status_str(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP runtime error";
+    case MOE_EDEVICE: return "device-detected bad input (expert id out of range)";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,490 @@
+// Grouped GEMM on gfx950 matrix cores for the MoE experts and the gate.
+//
+// [MND] = page "Lower latency and higher throughput with multi-node DeepSeek
+//         deployment".  [MND §Roofline / GroupGEMM]: g groups, group i has m_i
+// rows and multiplies [m_i, k] x [k, n] -> [m_i, n].  Here group g is one expert
+// and its rows are a contiguous slice of the expert-sorted activations.
+//
+// Design (one kernel template, several tile shapes):
+//   * Work unit = (expert, row slice of at most BM rows) x (N tile) x (K split).
+//     The unit table is built on the device from the routed counts
+//     ([MND §Quantization]: kernels read the number of tokens per expert rather
+//     than sizing work by the buffer bound), so no count ever crosses to the host.
+//     An expert's rows are cut into ceil(n/BM) near-equal slices, so a prefill
+//     expert (n <= BM) streams its weight panel from HBM exactly once.
+//   * Workgroups are dealt round-robin to the 8 XCDs; the block -> unit mapping
+//     keeps all N tiles of one unit on one XCD, so the unit's activation rows are
+//     fetched from HBM once and re-read from that XCD's L2.
+//   * Operands are both K-contiguous ([out, in] weights).  Each stage moves a
+//     128-byte K slice of BM activation rows and BN weight rows into LDS through
+//     registers (double-buffered, one barrier per stage), XOR-swizzled by row so
+//     the 16-byte fragment reads of 8 consecutive lanes hit distinct banks.
+//   * Wavefronts own 16-row tiles round-robin, so a partially filled unit spreads
+//     its valid rows over all wavefronts; tiles past the unit's rows are skipped.
+//   * bf16: v_mfma_f32_16x16x32_bf16.  fp8 (e4m3): one v_mfma 16x16x128 per
+//     128-wide K block, promoted into the fp32 accumulator with the 1x128
+//     activation scale times the 128x128 weight scale ([MND §Quantization]:
+//     activation scales vary only along K, so the promotion happens once per
+//     K block).
+//   * Epilogues: SwiGLU (h = silu(gate) * up, gate and up columns of the same
+//     h column sit in the same lane), optional 1x128 fp8 quantization of h,
+//     bf16 store, or fp32 split-k partials.
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+template <int WM, int WN, int TM, int TN, int EPI, bool FP8>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int BM = WM * TM * 16;
+  constexpr int BN = WN * TN * 16;
+  constexpr int ROWB = 128;              // bytes per operand row per stage
+  constexpr int KSTEP = FP8 ? 128 : 64;  // elements per stage
+  constexpr int EB = FP8 ? 1 : 2;        // operand element bytes
+  constexpr int A_CH = BM * 8 / NT;
+  constexpr int B_CH = BN * 8 / NT;
+  constexpr bool SWIGLU = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_FP8);
+  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile loads must divide evenly");
+  static_assert((NT / 8) % 8 == 0, "swizzle assumes row stride of loads multiple of 8");
+  static_assert(!SWIGLU || TN % 2 == 0, "swiglu needs gate/up tile pairs");
+
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * ROWB];
+  __shared__ float lds_sa[FP8 ? 2 : 1][FP8 ? BM : 1];
+  __shared__ float lds_rmax[EPI == EPI_SWIGLU_FP8 ? WN : 1][EPI == EPI_SWIGLU_FP8 ? BM : 1];
+
+  // ---- block -> (unit, n tile, k split); all tiles of a unit stay on one XCD
+  const int bid = blockIdx.x;
+  const int xcd = bid % kXcds;
+  const int slot = bid / kXcds;
+  const int per_unit = p.n_tiles * p.splits;
+  const int u = (slot / per_unit) * kXcds + xcd;
+  const int rem = slot % per_unit;
+  const int nt = rem % p.n_tiles;
+  const int split = rem / p.n_tiles;
+  Unit un;
+  if (p.uniform_rows > 0) {
+    if (u * BM >= p.uniform_rows) return;
+    un.group = 0;
+    un.row0 = u * BM;
+    un.rows = min(BM, p.uniform_rows - u * BM);
+  } else {
+    if (u >= *p.n_units) return;
+    un = p.units[u];
+  }
+  const int rows = un.rows;
+  if (rows <= 0) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  const int mtiles = (rows + 15) >> 4;
+  int jcount = mtiles > wm ? (mtiles - wm + WM - 1) / WM : 0;
+  if (jcount > TM) jcount = TM;
+
+  const int k0 = split * p.k_chunk;
+  const int k1 = min(p.K, k0 + p.k_chunk);
+  const int nsteps = (k1 - k0) / KSTEP;
+
+  // ---- per-thread load plan (constant over K): global offsets and LDS offsets
+  const uint8_t* a_base = p.A + static_cast<long long>(un.row0) * p.lda + static_cast<long long>(k0) * EB;
+  const uint8_t* b_base = p.B + static_cast<long long>(un.group) * p.b_group + static_cast<long long>(k0) * EB;
+  const int ch = tid & 7;
+  const int sw = (ch ^ ((tid >> 3) & 7)) << 4;
+  // Rows past the unit and columns past N re-load a valid row (an L1/L2 hit) so every
+  // load and LDS store is unconditional; their results are never stored.
+  uint32_t a_off[A_CH], b_off[B_CH];
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int r = (tid >> 3) + i * (NT / 8);
+    const int rc = r < rows ? r : rows - 1;
+    a_off[i] = static_cast<uint32_t>(rc * p.lda + ch * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const int j = (tid >> 3) + i * (NT / 8);
+    int col, grow;
+    if constexpr (SWIGLU) {
+      constexpr int WCOLS = TN * 16, HALF = TN * 8;
+      const int wn2 = j / WCOLS, jj = j % WCOLS;
+      col = nt * (BN / 2) + wn2 * HALF + (jj % HALF);
+      grow = (jj < HALF ? 0 : p.up_off) + col;
+    } else {
+      col = nt * BN + j;
+      grow = col;
+    }
+    if (col >= p.N) grow -= col - (p.N - 1);
+    b_off[i] = static_cast<uint32_t>(static_cast<long long>(grow) * p.ldb + ch * 16);
+  }
+
+  u32x4 ra[A_CH], rb[B_CH];
+  float rsa = 0.f;
+  // global -> registers for stage `step`
+#define MOE_GLOAD(step)                                                                        \
+  do {                                                                                         \
+    const long long kb_ = static_cast<long long>(step) * KSTEP * EB;                           \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                           \
+        ra[i] = *reinterpret_cast<const u32x4*>(a_base + a_off[i] + kb_);                      \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                           \
+        rb[i] = *reinterpret_cast<const u32x4*>(b_base + b_off[i] + kb_);                      \
+    if constexpr (FP8) {                                                                       \
+      if (tid < BM) {                                                                          \
+        const int r_ = tid < rows ? tid : rows - 1;                                            \
+        rsa = p.a_scale[static_cast<long long>(un.row0 + r_) * p.a_scale_ld + (k0 / KSTEP) +   \
+                        (step)];                                                               \
+      }                                                                                        \
+    }                                                                                          \
+  } while (0)
+  // registers -> LDS stage `stg` (row-swizzled 16-byte chunks)
+#define MOE_LSTORE(stg)                                                                        \
+  do {                                                                                         \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) {                                         \
+      const int r_ = (tid >> 3) + i * (NT / 8);                                                \
+      *reinterpret_cast<u32x4*>(&lds_a[stg][r_ * ROWB + sw]) = ra[i];                          \
+    }                                                                                          \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                         \
+      const int j_ = (tid >> 3) + i * (NT / 8);                                                \
+      *reinterpret_cast<u32x4*>(&lds_b[stg][j_ * ROWB + sw]) = rb[i];                          \
+    }                                                                                          \
+    if constexpr (FP8) {                                                                       \
+      if (tid < BM) lds_sa[stg][tid] = rsa;                                                    \
+    }                                                                                          \
+  } while (0)
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int j = 0; j < TM; ++j)
+#pragma unroll
+    for (int i = 0; i < TN; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // weight-scale row bases for fp8 (one 128x128 block row per 16-row B tile)
+  long long sb_row[FP8 ? TN : 1];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+      const int j = wn * TN * 16 + 16 * i;
+      int grow;
+      if constexpr (SWIGLU) {
+        constexpr int WCOLS = TN * 16, HALF = TN * 8;
+        const int wn2 = j / WCOLS, jj = j % WCOLS;
+        const int col = nt * (BN / 2) + wn2 * HALF + (jj % HALF);
+        grow = (jj < HALF ? 0 : p.up_off) + col;
+      } else {
+        grow = min(nt * BN + j, p.N - 1);  // tiles past N read a valid scale, never stored
+      }
+      sb_row[i] = static_cast<long long>(un.group) * p.b_scale_group +
+                  static_cast<long long>(grow / kQBlock) * p.b_scale_ld + k0 / KSTEP;
+    }
+  }
+
+  const int frag_row = lane & 15;
+  const int kgrp = lane >> 4;
+
+  if (nsteps > 0) {
+    MOE_GLOAD(0);
+    MOE_LSTORE(0);
+  }
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < nsteps) MOE_GLOAD(s + 1);
+    const uint8_t* la = lds_a[cur];
+    const uint8_t* lb = lds_b[cur];
+    if constexpr (!FP8) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int c = kk * 4 + kgrp;
+        const int coff = (c ^ (lane & 7)) << 4;
+        bf16x8 bfr[TN];
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+          const int rb_ = wn * TN * 16 + 16 * i + frag_row;
+          bfr[i] = *reinterpret_cast<const bf16x8*>(lb + rb_ * ROWB + coff);
+        }
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+          if (j < jcount) {
+            const int ra_ = 16 * (j * WM + wm) + frag_row;
+            const bf16x8 afr = *reinterpret_cast<const bf16x8*>(la + ra_ * ROWB + coff);
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+              acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[i], acc[j][i], 0, 0, 0);
+          }
+        }
+      }
+    } else {
+      // one 16x16x128 fp8 product per (row tile, column tile) and K block, promoted
+      // into the fp32 accumulator with scale_a(row, kb) * scale_w(col block, kb)
+      const int c0 = 2 * kgrp;
+      const int off0 = (c0 ^ (lane & 7)) << 4;
+      const int off1 = ((c0 + 1) ^ (lane & 7)) << 4;
+      i32x8 afr[TM];
+      float sa[TM][4];
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        if (j < jcount) {
+          const int t = j * WM + wm;
+          const int ra_ = 16 * t + frag_row;
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(la + ra_ * ROWB + off0);
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(la + ra_ * ROWB + off1);
+          afr[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sa[j][r] = lds_sa[cur][16 * t + 4 * kgrp + r];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TN; ++i) {
+        const int rb_ = wn * TN * 16 + 16 * i + frag_row;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(lb + rb_ * ROWB + off0);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(lb + rb_ * ROWB + off1);
+        const i32x8 bfr = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const float sb = p.b_scale[sb_row[i] + s];
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+          if (j < jcount) {
+            const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                afr[j], bfr, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[j][i][r] += part[r] * (sa[j][r] * sb);
+          }
+        }
+      }
+    }
+    if (s + 1 < nsteps) MOE_LSTORE(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue.  C fragment of a 16x16 tile: lane holds column (lane & 15),
+  // rows 4 * (lane >> 4) + r, r = 0..3.
+  const int ccol = lane & 15;
+  if constexpr (EPI == EPI_STORE_BF16 || EPI == EPI_STORE_F32) {
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      if (j >= jcount) continue;
+      const int rbase = 16 * (j * WM + wm) + 4 * kgrp;
+#pragma unroll
+      for (int i = 0; i < TN; ++i) {
+        const int col = nt * BN + wn * TN * 16 + 16 * i + ccol;
+        if (col >= p.N) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = rbase + r;
+          if (row >= rows) continue;
+          const long long o = static_cast<long long>(un.row0 + row) * p.ldc + col;
+          if constexpr (EPI == EPI_STORE_BF16) {
+            static_cast<uint16_t*>(p.C)[o] = f32_to_bf16(acc[j][i][r]);
+          } else {
+            static_cast<float*>(p.C)[o + split * p.c_split] = acc[j][i][r];
+          }
+        }
+      }
+    }
+  } else {
+    constexpr int HT = TN / 2;
+    float hv[TM][HT][4];
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+#pragma unroll
+      for (int i = 0; i < HT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float g = acc[j][i][r];
+          const float up = acc[j][i + HT][r];
+          hv[j][i][r] = g / (1.0f + __expf(-g)) * up;
+        }
+    if constexpr (EPI == EPI_SWIGLU_BF16) {
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        if (j >= jcount) continue;
+        const int rbase = 16 * (j * WM + wm) + 4 * kgrp;
+#pragma unroll
+        for (int i = 0; i < HT; ++i) {
+          const int col = nt * (BN / 2) + wn * (TN * 8) + 16 * i + ccol;
+          if (col >= p.N) continue;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = rbase + r;
+            if (row >= rows) continue;
+            static_cast<uint16_t*>(p.C)[static_cast<long long>(un.row0 + row) * p.ldc + col] =
+                f32_to_bf16(hv[j][i][r]);
+          }
+        }
+      }
+    } else {
+      // 1x128 fp8 quantization of h: the block's BN/2 = 128 h columns are one scale
+      // block.  Row amax: lane-local over HT tiles, 16-lane butterfly, then across
+      // the WN wavefronts through LDS.
+      static_assert(EPI != EPI_SWIGLU_FP8 || BN / 2 == kQBlock, "h tile must be one scale block");
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float m = 0.f;
+#pragma unroll
+          for (int i = 0; i < HT; ++i) m = fmaxf(m, fabsf(hv[j][i][r]));
+#pragma unroll
+          for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+          if (j < jcount && ccol == 0) lds_rmax[wn][16 * (j * WM + wm) + 4 * kgrp + r] = m;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        if (j >= jcount) continue;
+        const int rbase = 16 * (j * WM + wm) + 4 * kgrp;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = rbase + r;
+          float amax = 0.f;
+#pragma unroll
+          for (int w = 0; w < WN; ++w) amax = fmaxf(amax, lds_rmax[w][row]);
+          const bool zero = amax == 0.f;
+          const float scale = zero ? 1.0f : amax / 448.0f;
+          const float inv = zero ? 0.0f : 448.0f / amax;
+          if (row >= rows) continue;
+          uint8_t* hrow = static_cast<uint8_t*>(p.C) + static_cast<long long>(un.row0 + row) * p.ldc;
+#pragma unroll
+          for (int i = 0; i < HT; ++i) {
+            const int col = nt * (BN / 2) + wn * (TN * 8) + 16 * i + ccol;
+            const uint32_t q = zero ? 0u : f32_to_e4m3(hv[j][i][r] * inv);
+            if (col < p.N) hrow[col] = static_cast<uint8_t>(q);
+          }
+          if (wn == 0 && ccol == 0)
+            p.c_scale[static_cast<long long>(un.row0 + row) * p.c_scale_ld + nt] = scale;
+        }
+      }
+    }
+  }
+}
+
+#undef MOE_GLOAD
+#undef MOE_LSTORE
+
+// ------------------------------------------------------------------ unit planner
+// One block: units per group = ceil(n / BM) near-equal slices (rows rounded up to
+// 16), prefix-summed over groups, then each group writes its slices.
+// Units past `cap` (only reachable if offsets[G] exceeds the rows the caller sized the
+// workspace for) are dropped rather than written out of bounds.
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int G,
+                                                    int rows_if_null, int BM, int cap,
+                                                    Unit* __restrict__ units,
+                                                    int32_t* __restrict__ n_units) {
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int g0 = 0; g0 < G; g0 += 1024) {
+    const int g = g0 + threadIdx.x;
+    int n = 0, start = 0;
+    if (g < G) {
+      start = offsets ? offsets[g] : 0;
+      n = offsets ? offsets[g + 1] - start : rows_if_null;
+    }
+    const int nu = n > 0 ? (n + BM - 1) / BM : 0;
+    int incl = nu;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    if (w == 0) {
+      const int v = lane < 16 ? wsum[lane] : 0;
+      int inc = v;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const int uu = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += uu;
+      }
+      if (lane < 16) wsum[lane] = inc - v;
+    }
+    __syncthreads();
+    const int base = carry + wsum[w] + incl - nu;
+    if (nu > 0) {
+      const int per = ((n + nu - 1) / nu + 15) & ~15;
+      for (int i = 0; i < nu; ++i) {
+        Unit un;
+        un.group = g;
+        un.row0 = start + i * per;
+        un.rows = min(per, n - i * per);
+        un.pad = 0;
+        if (base + i < cap) units[base + i] = un;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == 1023) carry = base + nu;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *n_units = min(carry, cap);
+}
+
+hipError_t launch_plan(const int32_t* offsets, int G, int rows_if_null, int block_m, int cap,
+                       Unit* units, int32_t* n_units, hipStream_t st) {
+  plan_kernel<<<1, 1024, 0, st>>>(offsets, G, rows_if_null, block_m, cap, units, n_units);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ dispatch
+namespace {
+template <int WM, int WN, int TM, int TN, int EPI, bool FP8>
+hipError_t go(const GemmArgs& a, int max_units, hipStream_t st) {
+  const long long per_unit = static_cast<long long>(a.n_tiles) * a.splits;
+  const long long slots = (static_cast<long long>(max_units) + kXcds - 1) / kXcds;
+  const long long blocks = slots * kXcds * per_unit;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  gemm_kernel<WM, WN, TM, TN, EPI, FP8><<<static_cast<unsigned>(blocks), WM * WN * 64, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int WM, int WN, int TM, int TN>
+hipError_t go_epi(Epilogue epi, bool fp8, const GemmArgs& a, int max_units, hipStream_t st) {
+  if (fp8) {
+    switch (epi) {
+      case EPI_SWIGLU_FP8: return go<WM, WN, TM, TN, EPI_SWIGLU_FP8, true>(a, max_units, st);
+      case EPI_STORE_BF16: return go<WM, WN, TM, TN, EPI_STORE_BF16, true>(a, max_units, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (epi) {
+    case EPI_SWIGLU_BF16: return go<WM, WN, TM, TN, EPI_SWIGLU_BF16, false>(a, max_units, st);
+    case EPI_STORE_BF16: return go<WM, WN, TM, TN, EPI_STORE_BF16, false>(a, max_units, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+}  // namespace
+
+int gemm_block_m(GemmCfg cfg, bool fp8) {
+  switch (cfg) {
+    case CFG_BIG: return fp8 ? 128 : 256;
+    case CFG_SMALL: return 32;
+    default: return 64;
+  }
+}
+
+int gemm_block_n(GemmCfg) { return 256; }
+
+hipError_t launch_gemm(GemmCfg cfg, Epilogue epi, bool fp8, const GemmArgs& a, int max_units,
+                       hipStream_t st) {
+  switch (cfg) {
+    case CFG_BIG:
+      // fp8 keeps a per-K-block product next to the accumulators: shorter row tile
+      return fp8 ? go_epi<4, 2, 2, 8>(epi, fp8, a, max_units, st)
+                 : go_epi<4, 2, 4, 8>(epi, fp8, a, max_units, st);
+    case CFG_SMALL: return go_epi<1, 4, 2, 4>(epi, fp8, a, max_units, st);
+    case CFG_GATE:
+      if (epi != EPI_STORE_F32 || fp8) return hipErrorInvalidValue;
+      return go<1, 4, 4, 4, EPI_STORE_F32, false>(a, max_units, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

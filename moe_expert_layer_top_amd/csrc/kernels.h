@@ -1,0 +1,90 @@
+// Internal launchers of the MoE kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kSegSlots = 1024;  // routing slots per counting-sort segment (one wavefront)
+
+// Unit of grouped-GEMM work: rows [row0, row0 + rows) of group `group`.
+struct Unit {
+  int32_t group, row0, rows, pad;
+};
+
+enum Epilogue : int {
+  EPI_SWIGLU_BF16 = 0,  // h = silu(gate) * up, stored bf16
+  EPI_SWIGLU_FP8 = 1,   // h quantized to e4m3 with one fp32 scale per 1x128 block
+  EPI_STORE_BF16 = 2,   // C stored bf16
+  EPI_STORE_F32 = 3,    // C stored fp32 (split-k partials)
+};
+
+struct GemmArgs {
+  const uint8_t* A;         // activation rows
+  long long lda;            // row pitch in bytes
+  const float* a_scale;     // fp8 only: [rows, K/128]
+  long long a_scale_ld;     // floats per row
+  const uint8_t* B;         // weights of group 0
+  long long ldb;            // row pitch in bytes
+  long long b_group;        // bytes between groups
+  const float* b_scale;     // fp8 only: [Brows/128, K/128] per group
+  long long b_scale_group;  // floats between groups
+  long long b_scale_ld;     // floats per scale row
+  void* C;                  // output
+  long long ldc;            // elements per output row
+  long long c_split;        // elements between split-k partial outputs
+  float* c_scale;           // EPI_SWIGLU_FP8: [rows, N/128]
+  long long c_scale_ld;
+  const Unit* units;        // device unit table (unused when uniform_rows > 0)
+  const int32_t* n_units;   // device unit count (unused when uniform_rows > 0)
+  int uniform_rows;         // > 0: one group of this many rows cut into BM slices
+  int N;                    // logical output columns
+  int K;                    // reduction length in elements
+  int up_off;               // swiglu: first row of the up projection (= I)
+  int n_tiles;              // output tiles along N
+  int splits;               // split-k factor
+  int k_chunk;              // elements of K per split (multiple of the stage depth)
+};
+
+enum GemmCfg : int {
+  CFG_BIG = 0,    // 256 (fp8: 128) x 256 tiles, 8 wavefronts: prefill-sized groups
+  CFG_SMALL = 1,  // 32 x 256 tiles, 4 wavefronts: decode-sized groups
+  CFG_GATE = 2,   // 64 x 256 tiles, 4 wavefronts: gate projection
+};
+
+int gemm_block_m(GemmCfg cfg, bool fp8);
+int gemm_block_n(GemmCfg cfg);
+hipError_t launch_gemm(GemmCfg cfg, Epilogue epi, bool fp8, const GemmArgs& a, int max_units,
+                       hipStream_t st);
+
+// Builds the unit table of a grouped GEMM on the device.  `offsets` [G+1] or, when
+// NULL, one group of `rows_if_null` rows.
+hipError_t launch_plan(const int32_t* offsets, int G, int rows_if_null, int block_m, int cap,
+                       Unit* units, int32_t* n_units, hipStream_t st);
+
+hipError_t launch_topk(const float* part, int splits, long long split_stride, int T, int E, int k,
+                       const float* bias, float* logits_out, int32_t* idx, float* w,
+                       hipStream_t st);
+
+// counts_ws: [nseg * E] int32, seg_err: [nseg] int32 with nseg = ceil(R / kSegSlots).
+// err_word is overwritten with 1 if any id fell outside [e_base, e_base + E), else 0.
+hipError_t launch_routing(const int32_t* ids, long long R, int e_base, int E, int32_t* counts_ws,
+                          int32_t* seg_err, int32_t* err_word, int32_t* eri, int32_t* sorted_src,
+                          int32_t* tpe, int32_t* offsets, hipStream_t st);
+
+hipError_t launch_expand(const void* x, int T, int H, int k, int act_bytes, bool quant_fp8,
+                         const int32_t* eri, void* out, float* out_scale, hipStream_t st);
+
+hipError_t launch_finalize(const void* y, const void* skip, const float* w, const int32_t* eri,
+                           void* out, int T, int H, int k, int act_bytes, hipStream_t st);
+
+// fp32 path (plain FMA kernels; fp32 matrix and vector peaks are equal on gfx950)
+hipError_t launch_gemm_nt_f32(const float* A, const float* B, float* C, int M, int N, int K,
+                              hipStream_t st);
+// offsets == NULL: one group holding all R_max rows.
+hipError_t launch_grouped_ffn_f32(const float* a, const int32_t* offsets, int G, int R_max,
+                                  const float* w13, const float* w2, float* h, float* y, int H,
+                                  int I, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,373 @@
+// Top-k router and expand-and-sort routing for the MoE layer (gfx950).
+//
+// [MND] = page "Lower latency and higher throughput with multi-node DeepSeek
+//         deployment"; [R1P] = page "CANN/cann-recipes-infer: DeepSeek-R1
+//         prefill optimization".
+//
+// Routing is a stable counting sort in three launches, deterministic without
+// order-dependent atomics:
+//   route_count   one wavefront per segment of kSegSlots consecutive slots counts
+//                 the slots of each expert with ballot-built peer masks
+//   route_scan    per-expert exclusive prefix over segments, then over experts
+//   route_place   each wavefront replays its segment in slot order and places every
+//                 slot at offsets[e] + (earlier slots of e), writing the src->dst
+//                 map (expanded_row_idx) and its inverse (sorted_src)
+// and the copy kernel `expand_rows` reads each token row once and writes its k
+// copies (optionally quantized to fp8 with one scale per 1x128 vector).
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ top-k router
+// [MND §Expert Parallelism]: every token goes to k different routed experts whose
+// outputs are weighted-summed.  [MND §MoE Router]: a sort that tracks element
+// indices selects the top-k.  One wavefront per token; each lane holds
+// ceil(E/64) scores; k rounds of a wave-wide (score desc, id asc) arg-max.
+// The gate GEMM may have split the reduction into `splits` partial sums, added
+// here in split order so the float32 logits are reproducible run to run.
+template <int VPL>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ part, int splits,
+                                                   long long split_stride, int T, int E, int k,
+                                                   const float* __restrict__ bias,
+                                                   float* __restrict__ logits_out,
+                                                   int32_t* __restrict__ idx_out,
+                                                   float* __restrict__ w_out) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float z[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int e = v * 64 + lane;
+    float l = -INFINITY;
+    if (e < E) {
+      const float* p = part + static_cast<long long>(t) * E + e;
+      l = p[0];
+      for (int s = 1; s < splits; ++s) l += p[s * split_stride];
+      if (logits_out) logits_out[static_cast<long long>(t) * E + e] = l;
+      if (bias) l += bias[e];
+    }
+    z[v] = l;
+  }
+  float sel_z = 0.f;  // score of the expert this lane records (lanes 0..k-1)
+  int sel_e = 0;
+  for (int j = 0; j < k; ++j) {
+    // local best (lower id wins ties because v ascends)
+    float bz = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int e = v * 64 + lane;
+      if (e < E && (z[v] > bz || (z[v] == bz && e < be))) {
+        bz = z[v];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float oz = __shfl_xor(bz, o, 64);
+      const int oe = __shfl_xor(be, o, 64);
+      if (oz > bz || (oz == bz && oe < be)) {
+        bz = oz;
+        be = oe;
+      }
+    }
+    if (lane == j) {
+      sel_z = bz;
+      sel_e = be;
+    }
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      if (v * 64 + lane == be) z[v] = -INFINITY;  // remove the winner
+  }
+  // sigmoid of the selected scores, renormalized over the k selected experts
+  const float sg = lane < k ? 1.0f / (1.0f + expf(-sel_z)) : 0.0f;
+  const float tot = wave_sum(sg);
+  if (lane < k) {
+    idx_out[static_cast<long long>(t) * k + lane] = sel_e;
+    w_out[static_cast<long long>(t) * k + lane] = sg / tot;
+  }
+}
+
+hipError_t launch_topk(const float* part, int splits, long long split_stride, int T, int E, int k,
+                       const float* bias, float* logits_out, int32_t* idx, float* w,
+                       hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  const dim3 block(256), grid((T + 3) / 4);
+  const int vpl = (E + 63) / 64;
+#define MOE_TOPK_CASE(N)                                                                   \
+  case N:                                                                                  \
+    topk_kernel<N><<<grid, block, 0, st>>>(part, splits, split_stride, T, E, k, bias,      \
+                                           logits_out, idx, w);                            \
+    break;
+  switch (vpl) {
+    MOE_TOPK_CASE(1)
+    MOE_TOPK_CASE(2)
+    MOE_TOPK_CASE(3)
+    MOE_TOPK_CASE(4)
+    MOE_TOPK_CASE(8)
+    MOE_TOPK_CASE(16)
+    default:
+      if (vpl <= 8) {
+        topk_kernel<8><<<grid, block, 0, st>>>(part, splits, split_stride, T, E, k, bias,
+                                               logits_out, idx, w);
+      } else {
+        topk_kernel<16><<<grid, block, 0, st>>>(part, splits, split_stride, T, E, k, bias,
+                                                logits_out, idx, w);
+      }
+  }
+#undef MOE_TOPK_CASE
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ counting sort
+// Peer mask of a lane: the lanes of the wave (among `active`) holding the same key.
+// Built from one ballot per key bit, so equal keys are found without atomics.
+__device__ __forceinline__ uint64_t peer_mask(uint32_t key, int bits, uint64_t active) {
+  uint64_t m = active;
+  for (int b = 0; b < bits; ++b) {
+    const bool bit = (key >> b) & 1u;
+    const uint64_t bal = __ballot(bit);
+    m &= bit ? bal : ~bal;
+  }
+  return m;
+}
+
+__device__ __forceinline__ uint32_t local_key(const int32_t* ids, long long s, long long R,
+                                              int e_base, int E, int* err) {
+  if (s >= R) return static_cast<uint32_t>(E);
+  const int v = ids[s] - e_base;
+  if (v < 0 || v >= E) {
+    *err = 1;
+    return static_cast<uint32_t>(E);  // sentinel: invalid slot
+  }
+  return static_cast<uint32_t>(v);
+}
+
+// counts[seg * E + e] = slots of expert e in segment seg.
+__global__ __launch_bounds__(256) void route_count_kernel(const int32_t* __restrict__ ids,
+                                                          long long R, int e_base, int E, int bits,
+                                                          int32_t* __restrict__ counts,
+                                                          int nseg, int32_t* __restrict__ seg_err) {
+  extern __shared__ int32_t cnt_lds[];  // [4][E]
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int seg = blockIdx.x * 4 + wave;
+  int32_t* cnt = cnt_lds + wave * E;
+  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  if (seg >= nseg) return;
+  int err = 0;
+  const long long s0 = static_cast<long long>(seg) * kSegSlots;
+  for (int it = 0; it < kSegSlots / 64; ++it) {
+    const long long s = s0 + it * 64 + lane;
+    const uint32_t key = local_key(ids, s, R, e_base, E, &err);
+    const uint64_t active = __ballot(s < R);
+    if (active == 0) break;
+    const uint64_t peers = peer_mask(key, bits, active);
+    const bool leader = (s < R) && key < static_cast<uint32_t>(E) &&
+                        (__builtin_ctzll(peers) == lane);
+    if (leader) cnt[key] += __builtin_popcountll(peers);
+  }
+  for (int e = lane; e < E; e += 64) counts[static_cast<long long>(seg) * E + e] = cnt[e];
+  const bool any_err = __ballot(err) != 0;
+  if (lane == 0) seg_err[seg] = any_err ? 1 : 0;
+}
+
+// One block: base[seg*E+e] = offsets[e] + sum_{seg'<seg} counts[seg'*E+e] (in place),
+// tokens_per_expert[e] and expert_offsets[0..E].
+__global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ counts, int nseg,
+                                                          int E, int32_t* __restrict__ tpe,
+                                                          int32_t* __restrict__ offsets,
+                                                          const int32_t* __restrict__ seg_err,
+                                                          int32_t* __restrict__ err_word) {
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t any_err;
+  const int e = threadIdx.x;
+  if (e == 0) any_err = 0;
+  __syncthreads();
+  for (int s = e; s < nseg; s += blockDim.x)
+    if (seg_err[s]) any_err = 1;  // benign race: every writer stores 1
+  int32_t run = 0;
+  if (e < E) {
+    for (int s = 0; s < nseg; ++s) {
+      const int32_t c = counts[static_cast<long long>(s) * E + e];
+      counts[static_cast<long long>(s) * E + e] = run;
+      run += c;
+    }
+  }
+  // exclusive scan of `run` over experts (block of 1024 threads, 16 waves)
+  const int lane = e & 63, w = e >> 6;
+  int32_t incl = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  if (w == 0) {
+    int32_t v = lane < 16 ? wsum[lane] : 0;
+    int32_t inc = v;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int32_t u = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += u;
+    }
+    if (lane < 16) wsum[lane] = inc - v;  // exclusive wave base
+  }
+  __syncthreads();
+  const int32_t excl = wsum[w] + incl - run;
+  if (e == 0) *err_word = any_err;
+  if (e < E) {
+    tpe[e] = run;
+    offsets[e] = excl;
+    if (e == E - 1) offsets[E] = excl + run;
+  }
+  __syncthreads();
+  if (e < E) {
+    for (int s = 0; s < nseg; ++s) counts[static_cast<long long>(s) * E + e] += excl;
+  }
+}
+
+__global__ __launch_bounds__(256) void route_place_kernel(const int32_t* __restrict__ ids,
+                                                          long long R, int e_base, int E, int bits,
+                                                          const int32_t* __restrict__ base,
+                                                          int nseg, int32_t* __restrict__ eri,
+                                                          int32_t* __restrict__ sorted_src) {
+  extern __shared__ int32_t cnt_lds[];  // [4][E]
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int seg = blockIdx.x * 4 + wave;
+  if (seg >= nseg) return;
+  int32_t* cnt = cnt_lds + wave * E;
+  for (int e = lane; e < E; e += 64) cnt[e] = base[static_cast<long long>(seg) * E + e];
+  int err = 0;
+  const long long s0 = static_cast<long long>(seg) * kSegSlots;
+  for (int it = 0; it < kSegSlots / 64; ++it) {
+    const long long s = s0 + it * 64 + lane;
+    const uint64_t active = __ballot(s < R);
+    if (active == 0) break;
+    const uint32_t key = local_key(ids, s, R, e_base, E, &err);
+    const uint64_t peers = peer_mask(key, bits, active);
+    const bool valid = (s < R) && key < static_cast<uint32_t>(E);
+    int32_t pos = -1;
+    if (valid) {
+      const uint64_t lower = peers & ((1ull << lane) - 1ull);
+      pos = cnt[key] + __builtin_popcountll(lower);
+    }
+    // every lane has read cnt[] before the leaders advance it (in-order LDS within a wave)
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    if (valid && __builtin_ctzll(peers) == lane) cnt[key] += __builtin_popcountll(peers);
+    if (s < R) {
+      eri[s] = pos;
+      if (valid && sorted_src) sorted_src[pos] = static_cast<int32_t>(s);
+    }
+  }
+}
+
+hipError_t launch_routing(const int32_t* ids, long long R, int e_base, int E, int32_t* counts_ws,
+                          int32_t* seg_err, int32_t* err_word, int32_t* eri, int32_t* sorted_src,
+                          int32_t* tpe, int32_t* offsets, hipStream_t st) {
+  const int nseg = static_cast<int>((R + kSegSlots - 1) / kSegSlots);
+  int bits = 0;
+  while ((1 << bits) <= E) ++bits;  // keys 0..E (E = invalid sentinel)
+  const size_t lds = 4 * static_cast<size_t>(E) * sizeof(int32_t);
+  if (nseg > 0) {
+    route_count_kernel<<<(nseg + 3) / 4, 256, lds, st>>>(ids, R, e_base, E, bits, counts_ws, nseg,
+                                                          seg_err);
+  }
+  route_scan_kernel<<<1, 1024, 0, st>>>(counts_ws, nseg, E, tpe, offsets, seg_err, err_word);
+  if (nseg > 0) {
+    route_place_kernel<<<(nseg + 3) / 4, 256, lds, st>>>(ids, R, e_base, E, bits, counts_ws, nseg,
+                                                          eri, sorted_src);
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ row expansion
+// [R1P §MoE deployment strategy optimization]: expanded_x holds every token once
+// per chosen expert, in expert order.  Scatter form: block (t) reads token row t
+// once (16-byte vectors) and writes it to its k destination rows.
+template <int EB>  // element bytes of x and of the expanded rows (4 = fp32, 2 = bf16)
+__global__ __launch_bounds__(256) void expand_copy_kernel(const uint8_t* __restrict__ x, int H,
+                                                          int k, const int32_t* __restrict__ eri,
+                                                          uint8_t* __restrict__ out) {
+  const int t = blockIdx.x;
+  const long long row_bytes = static_cast<long long>(H) * EB;
+  const int nvec = static_cast<int>(row_bytes / 16);
+  const uint4* src = reinterpret_cast<const uint4*>(x + t * row_bytes);
+  const int32_t* dst = eri + static_cast<long long>(t) * k;  // uniform over the block
+  for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
+    const uint4 val = src[v];
+    for (int j = 0; j < k; ++j) {
+      const int32_t d = dst[j];
+      if (d >= 0) reinterpret_cast<uint4*>(out + d * row_bytes)[v] = val;
+    }
+  }
+}
+
+// fp8 variant: [MND §Quantization] activations are quantized on the fly with one
+// fp32 scale per 128-element vector.  16 lanes own one 128-element block (8 bf16
+// each): amax by a 16-lane butterfly, scale = amax / 448, q = e4m3(x * (448/amax)),
+// all in float32 with IEEE division.  A zero block gets scale 1 and zero codes.
+__global__ __launch_bounds__(256) void expand_quant_kernel(const uint16_t* __restrict__ x, int H,
+                                                           int k, const int32_t* __restrict__ eri,
+                                                           uint8_t* __restrict__ out,
+                                                           float* __restrict__ out_scale) {
+  const int t = blockIdx.x;
+  const int nblk = H / kQBlock;
+  const int lane16 = threadIdx.x & 15;
+  const int grp = threadIdx.x >> 4;  // 16 groups of 16 lanes per block
+  const int32_t* dst = eri + static_cast<long long>(t) * k;  // uniform over the block
+  for (int b = grp; b < nblk; b += 16) {
+    const uint4 raw = reinterpret_cast<const uint4*>(x + static_cast<long long>(t) * H +
+                                                     b * kQBlock)[lane16];
+    float v[8];
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+    const bool zero = amax == 0.f;
+    const float scale = zero ? 1.0f : amax / 448.0f;
+    const float inv = zero ? 0.0f : 448.0f / amax;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(v[i] * inv) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(v[4 + i] * inv) << (8 * i);
+    if (zero) lo = hi = 0;
+    const uint2 q = make_uint2(lo, hi);
+    for (int j = 0; j < k; ++j) {
+      const int32_t d = dst[j];
+      if (d < 0) continue;
+      reinterpret_cast<uint2*>(out + static_cast<long long>(d) * H + b * kQBlock)[lane16] = q;
+      if (lane16 == 0) out_scale[static_cast<long long>(d) * nblk + b] = scale;
+    }
+  }
+}
+
+hipError_t launch_expand(const void* x, int T, int H, int k, int act_bytes, bool quant_fp8,
+                         const int32_t* eri, void* out, float* out_scale, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  if (quant_fp8) {
+    expand_quant_kernel<<<T, 256, 0, st>>>(static_cast<const uint16_t*>(x), H, k, eri,
+                                           static_cast<uint8_t*>(out), out_scale);
+  } else if (act_bytes == 2) {
+    expand_copy_kernel<2><<<T, 256, 0, st>>>(static_cast<const uint8_t*>(x), H, k, eri,
+                                             static_cast<uint8_t*>(out));
+  } else {
+    expand_copy_kernel<4><<<T, 256, 0, st>>>(static_cast<const uint8_t*>(x), H, k, eri,
+                                             static_cast<uint8_t*>(out));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

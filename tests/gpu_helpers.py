@@ -1,0 +1,68 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI and
+compare with the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+
+
+def say(*a):
+    print("[gpu]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def tol_of(cfg) -> float:
+    return TOL["fp8"] if cfg.wt == "fp8" else TOL[cfg.act]
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def act_to_f64(t: torch.Tensor, act: str) -> np.ndarray:
+    a = host(t)
+    if act == "bf16":
+        return (a.astype(np.int16).view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def round_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """float -> bf16 bits (round to nearest even), for feeding oracle values to a GPU call."""
+    u = np.ascontiguousarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def max_row_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max over rows of max_h |got - ref| / max_h |ref| (rows of zeros compare absolutely)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    den = np.abs(ref).max(axis=1)
+    den = np.where(den > 0, den, 1.0)
+    return float((np.abs(got - ref).max(axis=1) / den).max())
+
+
+def act_dtype(act: str):
+    return torch.float32 if act == "f32" else torch.int16
+
+
+def empty_act(shape, act, device="cuda"):
+    return torch.empty(shape, dtype=act_dtype(act), device=device)
+
+
+def poison_(t: torch.Tensor):
+    """Fill with a recognisable pattern so unwritten outputs show up."""
+    if t.dtype == torch.float32:
+        t.fill_(float("nan"))
+    elif t.dtype == torch.int32:
+        t.fill_(-7777)
+    elif t.dtype == torch.int16:
+        t.fill_(0x7FC1)  # a bf16 NaN
+    else:
+        t.fill_(0x7F)  # fp8 NaN code
+    return t

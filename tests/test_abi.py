@@ -1,0 +1,90 @@
+"""The C-ABI library loads and exports every entry point of include/moe.h, and its
+host-side validation answers without touching a GPU (nothing here launches work)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import moe_expert_layer_top_amd as M
+from moe_expert_layer_top_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libmoe.so not built")
+    return M.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\sT\s(moe_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(L, name)
+
+
+def test_status_strings(L):
+    for st in (M.MOE_OK, M.MOE_EINVAL, M.MOE_EUNSUPPORTED, M.MOE_EWORKSPACE, M.MOE_EHIP, M.MOE_EDEVICE):
+        assert M.moe_status_str(st) and M.moe_status_str(st) != "unknown status"
+    assert M.moe_status_str(99) == "unknown status"
+
+
+def test_workspace_query(L):
+    c2 = M.shape(8192, 7168, 256, 8, 2048, 2048, "bf16", "bf16")
+    n = M.moe_workspace_bytes(c2)
+    # at least the expanded rows and the routed outputs (2 x R x H bf16)
+    assert n >= 2 * 65536 * 7168 * 2
+    small = M.shape(100, 7168, 256, 8, 2048, 2048, "bf16", "bf16")
+    assert 0 < M.moe_workspace_bytes(small) < n
+    assert M.moe_workspace_bytes(M.shape(8, 128, 4, 5, 128, 128)) == 0          # k > E
+    assert M.moe_workspace_bytes(M.shape(8, 100, 4, 2, 128, 128)) == 0          # H % 128
+    assert M.moe_workspace_bytes(M.shape(8, 128, 4, 2, 100, 128)) == 0          # I % 128
+    assert M.moe_workspace_bytes(M.shape(8, 128, 4, 2, 128, 128, "f32", "bf16")) == 0
+    assert M.moe_workspace_bytes(M.shape(8, 128, 4, 2, 128, 128, "bf16", "fp8")) > 0
+    assert M.moe_grouped_ffn_workspace_bytes(c2, 256, 65536) > 65536 * 2048 * 2
+
+
+DUMMY = ctypes.c_void_p(4096)   # never dereferenced: validation fails first
+
+
+def test_validation_errors_enqueue_nothing(L):
+    s = M.shape(16, 256, 8, 2, 128, 128)
+    bad_k = M.shape(16, 256, 8, 9, 128, 128)
+    bad_dt = M.shape(16, 256, 8, 2, 128, 128, "f32", "fp8")
+    P = [DUMMY] * 6
+    assert L.moe_init_routing(None, *[None] * 2, 0, *[None] * 7, 0, None) == M.MOE_EINVAL
+    assert L.moe_init_routing(ctypes.byref(bad_k), DUMMY, DUMMY, 0, DUMMY, None, DUMMY, DUMMY, DUMMY,
+                              DUMMY, DUMMY, 1 << 30, None) == M.MOE_EINVAL
+    assert L.moe_init_routing(ctypes.byref(bad_dt), DUMMY, DUMMY, 0, DUMMY, None, DUMMY, DUMMY, DUMMY,
+                              DUMMY, DUMMY, 1 << 30, None) == M.MOE_EUNSUPPORTED
+    assert L.moe_init_routing(ctypes.byref(s), DUMMY, DUMMY, 0, DUMMY, None, DUMMY, DUMMY, DUMMY,
+                              DUMMY, DUMMY, 16, None) == M.MOE_EWORKSPACE
+    assert L.moe_gate_topk(ctypes.byref(s), DUMMY, None, None, DUMMY, DUMMY, DUMMY, DUMMY, 1 << 30,
+                           None) == M.MOE_EINVAL
+    assert L.moe_grouped_ffn(ctypes.byref(s), 0, 10, *P[:3], DUMMY, None, DUMMY, None, DUMMY, DUMMY,
+                             1 << 30, None) == M.MOE_EINVAL
+    fp8 = M.shape(16, 256, 8, 2, 128, 128, "bf16", "fp8")
+    assert L.moe_grouped_ffn(ctypes.byref(fp8), 8, 32, DUMMY, None, DUMMY, DUMMY, None, DUMMY, None,
+                             DUMMY, DUMMY, 1 << 30, None) == M.MOE_EINVAL   # fp8 needs scales
+    assert L.moe_finalize_routing(ctypes.byref(s), None, None, None, DUMMY, DUMMY, None) == M.MOE_EINVAL
+    w = M.moe_weights()
+    assert L.moe_layer(ctypes.byref(s), ctypes.byref(w), DUMMY, DUMMY, None, None, None, DUMMY, 1 << 30,
+                       None) == M.MOE_EINVAL
+    assert L.moe_get_error(None, None) == M.MOE_EINVAL
