@@ -1,0 +1,306 @@
+"""Bench of the MI355X MoE expert layer: tokens/s of one full layer call.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu]
+
+A step is one ``moe_layer`` call (gate + top-k, init-routing, grouped SwiGLU
+experts, shared expert, finalize-routing) over T tokens whose inputs are already
+resident in HBM.  The default workload is the DeepSeek-V3-shaped prefill layer
+(T=8192, H=7168, 256 routed experts of I=2048, top-8, one shared expert, bf16).
+Every launch boundary of every timed step is marked with a HIP event on the
+launch stream, which gives the per-kernel-class times and the roofline of the
+dominant kernel.  The CPU oracle is timed on a bounded token sample of the same
+workload.  One JSON line goes to stdout (last line).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+
+METRIC = "MoE-layer tokens/sec on 1 MI355X; % MFMA peak (FFN), % HBM BW (permute)"
+
+
+# ----------------------------------------------------------------------------- accounting
+# [MND §Roofline / GroupGEMM]: a grouped GEMM of g groups of [m, k] x [k, n] does
+# 2*g*m*k*n FLOPs and moves g*(m*k + n*k + m*n) elements; [MND §Roofline / GEMM]:
+# a dense GEMM does 2*m*k*n FLOPs over m*k + n*k + m*n elements.
+
+def group_gemm_flops(g, m, k, n):
+    return 2 * g * m * k * n
+
+
+def group_gemm_elems(g, m, k, n):
+    return g * (m * k + n * k + m * n)
+
+
+def gemm_flops(m, k, n):
+    return 2 * m * k * n
+
+
+def gemm_elems(m, k, n):
+    return m * k + n * k + m * n
+
+
+def rows_per_expert(batch, qlen, topk, ep, experts):
+    """[MND §Roofline / GroupGEMM]: mean rows per expert m = batch*qlen*topk*EP/experts."""
+    return batch * qlen * topk * ep / experts
+
+
+def _bytes(dt):
+    return {"f32": 4, "bf16": 2, "fp8": 1}[dt]
+
+
+def account(cfg, tpe) -> dict:
+    """Algorithmic FLOPs and HBM bytes of every kernel class of one layer call.
+
+    Bytes count what the method must move, each once: the weights of the experts
+    that received rows (never of empty ones), the activations read and written.
+    ``tpe`` is the realized tokens-per-expert histogram."""
+    T, H, E, k, I, Is = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared
+    R = int(np.sum(tpe))
+    active = int(np.count_nonzero(tpe))
+    ab = _bytes(cfg.act)
+    fp8 = cfg.wt == "fp8"
+    wb = _bytes(cfg.wt)
+    eb = 1 if fp8 else ab                         # expanded-row bytes
+    hb = 1 if fp8 else ab
+    sc_a = R * (H // 128) * 4 if fp8 else 0       # 1x128 activation scales
+    sc_h = R * (I // 128) * 4 if fp8 else 0
+    sc_w13 = active * (2 * I // 128) * (H // 128) * 4 if fp8 else 0
+    sc_w2 = active * (H // 128) * (I // 128) * 4 if fp8 else 0
+    mfma_dt = "fp8" if fp8 else ("f32" if cfg.act == "f32" else "bf16")
+    acc = {
+        "gate": dict(flops=gemm_flops(T, H, E), bytes=T * H * ab + E * H * ab + T * E * 4, dt=cfg.act),
+        "topk": dict(flops=0, bytes=T * E * 4 + T * E * 4 + T * k * 8, dt=None),
+        "route": dict(flops=0, bytes=R * 4 + 2 * R * 4 + E * 8, dt=None),
+        "expand": dict(flops=0, bytes=T * H * ab + R * H * eb + sc_a, dt=None),
+        "plan": dict(flops=0, bytes=E * 4, dt=None),
+        "ffn1": dict(flops=2 * R * H * 2 * I,
+                     bytes=active * 2 * I * H * wb + sc_w13 + R * H * eb + sc_a + R * I * hb + sc_h,
+                     dt=mfma_dt),
+        "ffn2": dict(flops=2 * R * I * H,
+                     bytes=active * H * I * wb + sc_w2 + R * I * hb + sc_h + R * H * ab, dt=mfma_dt),
+        "shared": dict(flops=2 * T * H * 2 * Is + 2 * T * Is * H,
+                       bytes=3 * Is * H * ab + T * H * ab + 2 * T * Is * ab + T * H * ab,
+                       dt=cfg.act),
+        "finalize": dict(flops=0, bytes=R * H * ab + 2 * T * H * ab + T * k * 8, dt=None),
+    }
+    return acc
+
+
+def roofline_entry(acc_k: dict, ms: float) -> dict:
+    t = ms / 1e3
+    gbs = acc_k["bytes"] / t / 1e9 if t > 0 else 0.0
+    e = {"ms": ms, "GB/s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
+    if acc_k["flops"]:
+        peak = PEAK_TFLOPS[acc_k["dt"]]
+        tf = acc_k["flops"] / t / 1e12 if t > 0 else 0.0
+        e.update({"TFLOP/s": tf, "mfma_frac": tf / peak,
+                  "bound": "mfma" if acc_k["flops"] / (peak * 1e12) > acc_k["bytes"] / (PEAK_HBM_GBS * 1e9)
+                  else "hbm"})
+    else:
+        e["bound"] = "hbm"
+    return e
+
+
+# ----------------------------------------------------------------------------- GPU run
+
+def run_gpu(cfg, steps, warmup):
+    import torch
+
+    import moe_expert_layer_top_amd as M
+    from synth.device import upload_layer
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    g = upload_layer(cfg, dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    s = M.shape_of(cfg)
+    act_dt = torch.float32 if cfg.act == "f32" else torch.int16
+    out = torch.empty((cfg.T, cfg.H), dtype=act_dt, device=dev)
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+    w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+    logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
+    ws = torch.empty(M.moe_workspace_bytes(s), dtype=torch.uint8, device=dev)
+    W = M.weights(g["w_gate"], g["w13"], g["w2"], g["sh_w13"], g["sh_w2"], g.get("w13_scale"),
+                  g.get("w2_scale"), g.get("bias"))
+    nev = len(M.EV_NAMES)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+    stream = torch.cuda.current_stream()
+    for row in events:              # create the underlying HIP events
+        for e in row:
+            e.record(stream)
+    for _ in range(warmup):
+        M.moe_layer(s, W, g["x"], out, idx, w, logits, ws)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        M.moe_layer_profiled(s, W, g["x"], out, idx, w, logits, ws, events[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    stage_ms = {}
+    for j in range(1, nev):
+        stage_ms[M.EV_NAMES[j]] = float(np.mean([events[i][j - 1].elapsed_time(events[i][j])
+                                                 for i in range(steps)]))
+    tpe = np.bincount(idx.cpu().numpy().reshape(-1), minlength=cfg.E)
+    return dict(total_ms=total_ms, wall_s=wall, stage_ms=stage_ms, tpe=tpe, setup_s=setup_s,
+                logits=logits.cpu().numpy(), idx=idx.cpu().numpy())
+
+
+# ----------------------------------------------------------------------------- CPU oracle baseline
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(cfg, target_s=15.0, max_tokens=None):
+    """Time the oracle (as it stands) on the first T_s tokens of the workload.
+
+    Inputs of the sample -- the tokens, the gate, and the weights of the experts
+    the sample routes to -- are drawn first and not timed, like the GPU side."""
+    import dataclasses
+
+    from oracle import moe as O
+    from synth import inputs
+
+    x_all = inputs.tokens(cfg)
+    wg = inputs.gate_weight(cfg)
+    bias = inputs.expert_bias(cfg)
+
+    def prepare(ts):
+        sub = dataclasses.replace(cfg, T=ts)
+        d = {"cfg": sub, "x": x_all[:ts], "w_gate": wg, "bias": bias,
+             "sh_w13": inputs.shared_w13(cfg), "sh_w2": inputs.shared_w2(cfg)}
+        xl = O.to_f64(d["x"], cfg.act)
+        idx, _ = O.route_topk(O.gate_logits(xl, O.to_f64(wg, cfg.act)).astype(np.float32), bias, cfg.k)
+        experts = sorted(set(idx.reshape(-1).tolist()))
+        w13, w2, w13s, w2s = {}, {}, {}, {}
+        for e, v in inputs.for_each_expert(cfg, inputs.expert_w13, experts):
+            if cfg.wt == "fp8":
+                w13[e], w13s[e] = v
+            else:
+                w13[e] = v
+        for e, v in inputs.for_each_expert(cfg, inputs.expert_w2, experts):
+            if cfg.wt == "fp8":
+                w2[e], w2s[e] = v
+            else:
+                w2[e] = v
+        d.update(w13=w13, w2=w2)
+        if cfg.wt == "fp8":
+            d.update(w13_scale=w13s, w2_scale=w2s)
+        return d
+
+    ts = 2
+    while True:
+        d = prepare(ts)
+        t0 = time.perf_counter()
+        O.moe_layer(d)
+        dt = time.perf_counter() - t0
+        if dt >= target_s * 0.5 or ts >= (max_tokens or cfg.T):
+            break
+        ts = min(max_tokens or cfg.T, max(ts + 1, int(ts * min(8.0, target_s / max(dt, 1e-3)))))
+    return {"value": ts / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"first {ts} of the {cfg.T} tokens of {cfg.name} through the float64 oracle "
+                      f"(gate, top-k, routing, grouped SwiGLU experts, shared expert, combine); "
+                      f"{dt:.1f} s"}
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c2_prefill_bf16")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU: this layer is one GPU's share of tokens and "
+              f"experts, with no cross-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    from synth import configs
+    cfg = configs.get(args.config)
+    r = run_gpu(cfg, args.steps, args.warmup)
+    ms = r["total_ms"] / args.steps
+    tokens = cfg.shared_rows
+    acc = account(cfg, r["tpe"])
+    kern = {name: roofline_entry(acc[name], r["stage_ms"][name]) for name in acc}
+    dom = max(("ffn1", "ffn2"), key=lambda n: r["stage_ms"][n])
+    dk = kern[dom]
+    if dk["bound"] == "mfma":
+        achieved = acc[dom]["flops"] / (r["stage_ms"][dom] / 1e3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": achieved,
+                "peak": PEAK_TFLOPS[acc[dom]["dt"]], "unit": "TFLOP/s"}
+    else:
+        achieved = acc[dom]["bytes"] / (r["stage_ms"][dom] / 1e3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["mfma_frac"] = dk.get("mfma_frac")
+    permute_ms = r["stage_ms"]["expand"] + r["stage_ms"]["finalize"]
+    permute_bytes = acc["expand"]["bytes"] + acc["finalize"]["bytes"]
+    ffn_ms = r["stage_ms"]["ffn1"] + r["stage_ms"]["ffn2"]
+    ffn_flops = acc["ffn1"]["flops"] + acc["ffn2"]["flops"]
+    line = {
+        "metric": METRIC,
+        "value": tokens * 1e3 / ms,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if cfg.wt == "fp8" else cfg.act,
+        "data": "synthetic (seeded; see DESIGN.md input recipe)",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
+                   "I_shared": cfg.I_shared, "act": cfg.act, "wt": cfg.wt},
+        "roofline": roof,
+        "ffn_mfma_frac": ffn_flops / (ffn_ms / 1e3) / 1e12 / PEAK_TFLOPS[acc["ffn1"]["dt"]],
+        "permute_combine_hbm_frac": permute_bytes / (permute_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+        "kernels": kern,
+        "active_experts": int(np.count_nonzero(r["tpe"])),
+        "max_rows_per_expert": int(r["tpe"].max()),
+        "wall_ms_per_step": r["wall_s"] * 1e3 / args.steps,
+        "setup_s": r["setup_s"],
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

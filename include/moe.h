@@ -176,6 +176,30 @@ moe_status moe_layer(const moe_shape* s, const moe_weights* w, const void* x, vo
                      int32_t* topk_idx, float* topk_w, float* logits, void* ws,
                      size_t ws_bytes, hipStream_t stream);
 
+/* Launch boundaries at which moe_layer_profiled records events. */
+enum {
+  MOE_EV_START = 0,      /* before the gate projection                          */
+  MOE_EV_GATE = 1,       /* after the gate projection                           */
+  MOE_EV_TOPK = 2,       /* after the top-k router                              */
+  MOE_EV_ROUTE = 3,      /* after the counting sort (count, scan, place)        */
+  MOE_EV_EXPAND = 4,     /* after the row expansion (+ fp8 quantization)        */
+  MOE_EV_PLAN = 5,       /* after the grouped-GEMM unit table                   */
+  MOE_EV_FFN1 = 6,       /* after the routed gate/up GEMM with SwiGLU           */
+  MOE_EV_FFN2 = 7,       /* after the routed down GEMM                          */
+  MOE_EV_SHARED = 8,     /* after both shared-expert GEMMs                      */
+  MOE_EV_FINALIZE = 9,   /* after the un-permute + combine                      */
+  MOE_EV_COUNT = 10
+};
+
+/* moe_layer, additionally recording events[i] on `stream` at launch boundary i
+ * (i < n_events; NULL entries are skipped), so a profiler can time every kernel
+ * class of one layer from the host ([MND §Latency breakdown]: the time of one
+ * MoE layer split by kernel class).  Same arguments and behaviour as moe_layer. */
+moe_status moe_layer_profiled(const moe_shape* s, const moe_weights* w, const void* x,
+                              void* out, int32_t* topk_idx, float* topk_w, float* logits,
+                              void* ws, size_t ws_bytes, hipStream_t stream,
+                              hipEvent_t* events, int32_t n_events);
+
 /* Waits for `stream`, then reads and clears the device error word of `ws`:
  * MOE_EDEVICE if a routing call since the last check saw an expert id outside
  * its [e_base, e_base + E) range, else MOE_OK (MOE_EHIP on a runtime error). */

@@ -21,8 +21,10 @@ DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 
 EXPORTS = [
     "moe_workspace_bytes", "moe_grouped_ffn_workspace_bytes", "moe_gate_topk", "moe_init_routing",
-    "moe_grouped_ffn", "moe_finalize_routing", "moe_layer", "moe_get_error", "moe_status_str",
+    "moe_grouped_ffn", "moe_finalize_routing", "moe_layer", "moe_layer_profiled", "moe_get_error",
+    "moe_status_str",
 ]
+EV_NAMES = ["start", "gate", "topk", "route", "expand", "plan", "ffn1", "ffn2", "shared", "finalize"]
 
 
 class MoEError(RuntimeError):
@@ -63,6 +65,8 @@ def lib() -> ctypes.CDLL:
             "moe_grouped_ffn": (I32, [S, I32, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
             "moe_finalize_routing": (I32, [S, P, P, P, P, P, P]),
             "moe_layer": (I32, [S, ctypes.POINTER(moe_weights), P, P, P, P, P, P, SZ, P]),
+            "moe_layer_profiled": (I32, [S, ctypes.POINTER(moe_weights), P, P, P, P, P, P, SZ, P,
+                                         ctypes.POINTER(ctypes.c_void_p), I32]),
             "moe_get_error": (I32, [P, P]),
             "moe_status_str": (ctypes.c_char_p, [I32]),
         }
@@ -157,6 +161,17 @@ def moe_layer(s, w: moe_weights, x, out, topk_idx, topk_w, logits, ws, stream=No
     _check(lib().moe_layer(ctypes.byref(s), ctypes.byref(w), _ptr(x), _ptr(out), _ptr(topk_idx),
                            _ptr(topk_w), _ptr(logits), _ptr(ws), ws.numel() * ws.element_size(),
                            _stream(stream)), "moe_layer")
+
+
+def moe_layer_profiled(s, w: moe_weights, x, out, topk_idx, topk_w, logits, ws, events,
+                       stream=None):
+    """moe_layer recording `events` (torch.cuda.Event, already created) at its launch
+    boundaries, in the order of EV_NAMES."""
+    arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    _check(lib().moe_layer_profiled(ctypes.byref(s), ctypes.byref(w), _ptr(x), _ptr(out),
+                                    _ptr(topk_idx), _ptr(topk_w), _ptr(logits), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream), arr,
+                                    len(events)), "moe_layer_profiled")
 
 
 def moe_get_error(ws, stream=None) -> int:

@@ -157,9 +157,19 @@ P* at(void* ws, size_t off) {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
+// Optional event marks at launch boundaries (moe_layer_profiled).
+struct Prof {
+  hipEvent_t* ev = nullptr;
+  int n = 0;
+  hipError_t mark(int i, hipStream_t st) const {
+    return (ev && i < n && ev[i]) ? hipEventRecord(ev[i], st) : hipSuccess;
+  }
+};
+
 // ------------------------------------------------------------------ launch sequences
 moe_status run_gate_topk(const moe_shape* s, const void* x, const void* w_gate, const float* bias,
-                         float* logits, int32_t* idx, float* w, float* part, hipStream_t st) {
+                         float* logits, int32_t* idx, float* w, float* part, hipStream_t st,
+                         const Prof& prof = Prof()) {
   const GatePlan gp = gate_plan(s);
   hipError_t e;
   if (s->act == MOE_F32) {
@@ -186,9 +196,11 @@ moe_status run_gate_topk(const moe_shape* s, const void* x, const void* w_gate, 
                                     (s->T + bm - 1) / bm, st)
                  : hipSuccess;
   }
-  if (e != hipSuccess) return MOE_EHIP;
-  return hip_status(moe::launch_topk(part, gp.splits, static_cast<long long>(s->T) * s->E, s->T,
-                                     s->E, s->k, bias, logits, idx, w, st));
+  if (e != hipSuccess || prof.mark(MOE_EV_GATE, st) != hipSuccess) return MOE_EHIP;
+  e = moe::launch_topk(part, gp.splits, static_cast<long long>(s->T) * s->E, s->T, s->E, s->k, bias,
+                       logits, idx, w, st);
+  if (e != hipSuccess || prof.mark(MOE_EV_TOPK, st) != hipSuccess) return MOE_EHIP;
+  return MOE_OK;
 }
 
 struct FfnIo {
@@ -203,7 +215,8 @@ struct FfnIo {
 };
 
 moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io, void* ws,
-                   hipStream_t st) {
+                   hipStream_t st, const Prof& prof = Prof(), int ev_plan = -1, int ev_ffn1 = -1,
+                   int ev_ffn2 = -1) {
   if (R_max == 0) return MOE_OK;
   const FfnLayout L = ffn_layout(s, G, R_max, I);
   const int H = s->H;
@@ -226,6 +239,7 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
   } else {
     mu = (R_max + bm - 1) / bm;
   }
+  if (prof.mark(ev_plan, st) != hipSuccess) return MOE_EHIP;
   GemmArgs g1{};
   g1.A = static_cast<const uint8_t*>(io.a);
   g1.lda = static_cast<long long>(H) * eb;
@@ -252,7 +266,7 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
   g1.k_chunk = H;
   hipError_t e = moe::launch_gemm(cfg, fp8 ? moe::EPI_SWIGLU_FP8 : moe::EPI_SWIGLU_BF16, fp8, g1,
                                   mu, st);
-  if (e != hipSuccess) return MOE_EHIP;
+  if (e != hipSuccess || prof.mark(ev_ffn1, st) != hipSuccess) return MOE_EHIP;
   GemmArgs g2 = g1;
   g2.A = at<uint8_t>(ws, L.h);
   g2.lda = static_cast<long long>(I) * eb;
@@ -272,7 +286,9 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
   g2.up_off = 0;
   g2.n_tiles = (H + moe::gemm_block_n(cfg) - 1) / moe::gemm_block_n(cfg);
   g2.k_chunk = I;
-  return hip_status(moe::launch_gemm(cfg, moe::EPI_STORE_BF16, fp8, g2, mu, st));
+  e = moe::launch_gemm(cfg, moe::EPI_STORE_BF16, fp8, g2, mu, st);
+  if (e != hipSuccess || prof.mark(ev_ffn2, st) != hipSuccess) return MOE_EHIP;
+  return MOE_OK;
 }
 
 }  // namespace
@@ -307,11 +323,27 @@ moe_status moe_gate_topk(const moe_shape* s, const void* x, const void* w_gate, 
   return run_gate_topk(s, x, w_gate, bias, logits, topk_idx, topk_w, at<float>(ws, L.part), stream);
 }
 
+static moe_status init_routing_impl(const moe_shape* s, const void* x, const int32_t* ids,
+                                    int32_t e_base, void* expanded_x, float* expanded_scale,
+                                    int32_t* expanded_row_idx, int32_t* sorted_src,
+                                    int32_t* tokens_per_expert, int32_t* expert_offsets, void* ws,
+                                    size_t ws_bytes, hipStream_t stream, const Prof& prof);
+
 moe_status moe_init_routing(const moe_shape* s, const void* x, const int32_t* ids, int32_t e_base,
                             void* expanded_x, float* expanded_scale, int32_t* expanded_row_idx,
                             int32_t* sorted_src, int32_t* tokens_per_expert,
                             int32_t* expert_offsets, void* ws, size_t ws_bytes,
                             hipStream_t stream) {
+  return init_routing_impl(s, x, ids, e_base, expanded_x, expanded_scale, expanded_row_idx,
+                           sorted_src, tokens_per_expert, expert_offsets, ws, ws_bytes, stream,
+                           Prof());
+}
+
+static moe_status init_routing_impl(const moe_shape* s, const void* x, const int32_t* ids,
+                                    int32_t e_base, void* expanded_x, float* expanded_scale,
+                                    int32_t* expanded_row_idx, int32_t* sorted_src,
+                                    int32_t* tokens_per_expert, int32_t* expert_offsets, void* ws,
+                                    size_t ws_bytes, hipStream_t stream, const Prof& prof) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   const bool fp8 = s->wt == MOE_FP8_E4M3;
@@ -328,12 +360,13 @@ moe_status moe_init_routing(const moe_shape* s, const void* x, const int32_t* id
                                      at<int32_t>(ws, L.seg_err), at<int32_t>(ws, L.err),
                                      expanded_row_idx, sorted_src, tokens_per_expert,
                                      expert_offsets, stream);
-  if (e != hipSuccess) return MOE_EHIP;
+  if (e != hipSuccess || prof.mark(MOE_EV_ROUTE, stream) != hipSuccess) return MOE_EHIP;
   if (expanded_x && s->T > 0) {
     e = moe::launch_expand(x, s->T, s->H, s->k, elem_bytes(s->act), fp8, expanded_row_idx,
                            expanded_x, expanded_scale, stream);
     if (e != hipSuccess) return MOE_EHIP;
   }
+  if (prof.mark(MOE_EV_EXPAND, stream) != hipSuccess) return MOE_EHIP;
   return MOE_OK;
 }
 
@@ -365,9 +398,29 @@ moe_status moe_finalize_routing(const moe_shape* s, const void* y, const void* s
                                          elem_bytes(s->act), stream));
 }
 
+static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const void* x, void* out,
+                             int32_t* topk_idx, float* topk_w, float* logits, void* ws,
+                             size_t ws_bytes, hipStream_t stream, const Prof& prof);
+
 moe_status moe_layer(const moe_shape* s, const moe_weights* w, const void* x, void* out,
                      int32_t* topk_idx, float* topk_w, float* logits, void* ws, size_t ws_bytes,
                      hipStream_t stream) {
+  return layer_impl(s, w, x, out, topk_idx, topk_w, logits, ws, ws_bytes, stream, Prof());
+}
+
+moe_status moe_layer_profiled(const moe_shape* s, const moe_weights* w, const void* x, void* out,
+                              int32_t* topk_idx, float* topk_w, float* logits, void* ws,
+                              size_t ws_bytes, hipStream_t stream, hipEvent_t* events,
+                              int32_t n_events) {
+  Prof p;
+  p.ev = events;
+  p.n = events ? n_events : 0;
+  return layer_impl(s, w, x, out, topk_idx, topk_w, logits, ws, ws_bytes, stream, p);
+}
+
+static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const void* x, void* out,
+                             int32_t* topk_idx, float* topk_w, float* logits, void* ws,
+                             size_t ws_bytes, hipStream_t stream, const Prof& prof) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if ((st = check_inter(s, s->I)) != MOE_OK) return st;
@@ -385,20 +438,23 @@ moe_status moe_layer(const moe_shape* s, const moe_weights* w, const void* x, vo
   int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
   float* tw = topk_w ? topk_w : at<float>(ws, L.w);
   // gate + router  ([MND §Expert Parallelism], [MND §MoE Router])
-  st = run_gate_topk(s, x, w->w_gate, w->bias, lg, idx, tw, at<float>(ws, L.part), stream);
+  if (prof.mark(MOE_EV_START, stream) != hipSuccess) return MOE_EHIP;
+  st = run_gate_topk(s, x, w->w_gate, w->bias, lg, idx, tw, at<float>(ws, L.part), stream, prof);
   if (st != MOE_OK) return st;
   // first routing: expand and sort by expert  ([R1P §MoE deployment strategy optimization])
   int32_t* eri = at<int32_t>(ws, L.eri);
   int32_t* offs = at<int32_t>(ws, L.offsets);
-  st = moe_init_routing(s, x, idx, 0, at<void>(ws, L.ex), fp8 ? at<float>(ws, L.ex_scale) : nullptr,
-                        eri, at<int32_t>(ws, L.sorted_src), at<int32_t>(ws, L.tpe), offs, ws,
-                        ws_bytes, stream);
+  st = init_routing_impl(s, x, idx, 0, at<void>(ws, L.ex),
+                         fp8 ? at<float>(ws, L.ex_scale) : nullptr, eri,
+                         at<int32_t>(ws, L.sorted_src), at<int32_t>(ws, L.tpe), offs, ws, ws_bytes,
+                         stream, prof);
   if (st != MOE_OK) return st;
   // routed experts as one grouped GEMM over the expert-sorted rows
   const int R = s->T * s->k;
   FfnIo io{at<void>(ws, L.ex), fp8 ? at<float>(ws, L.ex_scale) : nullptr, offs, w->w13,
            w->w13_scale, w->w2, w->w2_scale, at<void>(ws, L.y)};
-  st = run_ffn(s, s->E, R, s->I, io, at<void>(ws, L.ffn), stream);
+  st = run_ffn(s, s->E, R, s->I, io, at<void>(ws, L.ffn), stream, prof, MOE_EV_PLAN, MOE_EV_FFN1,
+               MOE_EV_FFN2);
   if (st != MOE_OK) return st;
   // shared expert on every token ([MND §Expert Parallelism]: its output is added)
   moe_shape sh = *s;
@@ -406,8 +462,11 @@ moe_status moe_layer(const moe_shape* s, const moe_weights* w, const void* x, vo
   FfnIo sio{x, nullptr, nullptr, w->sh_w13, nullptr, w->sh_w2, nullptr, at<void>(ws, L.sh_out)};
   st = run_ffn(&sh, 1, s->T, s->I_shared, sio, at<void>(ws, L.sh_ffn), stream);
   if (st != MOE_OK) return st;
+  if (prof.mark(MOE_EV_SHARED, stream) != hipSuccess) return MOE_EHIP;
   // finalize: un-permute, weighted sum, plus the shared expert
-  return moe_finalize_routing(s, at<void>(ws, L.y), at<void>(ws, L.sh_out), tw, eri, out, stream);
+  st = moe_finalize_routing(s, at<void>(ws, L.y), at<void>(ws, L.sh_out), tw, eri, out, stream);
+  if (st != MOE_OK) return st;
+  return prof.mark(MOE_EV_FINALIZE, stream) == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
 moe_status moe_get_error(void* ws, hipStream_t stream) {

@@ -1,0 +1,181 @@
+"""GPU parity at the full workload sizes, in the launch configuration the bench times.
+
+The whole layer runs on the GPU at full size; the oracle then recomputes a sample
+of tokens one by one (every step of the layer is separable per token, so the
+sample's outputs equal the full layer's outputs for those tokens).  Routing
+integers (top-k ids, counts, offsets, both permutations) are compared bit for
+bit at full size, and the expanded rows of the sampled tokens byte for byte.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe as O
+from synth import configs, inputs
+from synth.device import to_dev, upload_layer
+from tests.gpu_helpers import act_to_f64, empty_act, host, max_row_rel_err, say, tol_of
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
+
+N_SAMPLE = 6
+
+
+@pytest.fixture(scope="module")
+def M():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import moe_expert_layer_top_amd as m
+    m.lib()
+    return m
+
+
+def sample_tokens(T, seed):
+    rng = np.random.default_rng(seed)
+    picks = {0, T - 1} | set(rng.choice(T, size=min(T, N_SAMPLE) - 2, replace=False).tolist())
+    return np.array(sorted(picks))
+
+
+def expert_dict(cfg, experts):
+    w13, w2, s13, s2 = {}, {}, {}, {}
+    for e, v in inputs.for_each_expert(cfg, inputs.expert_w13, experts):
+        if cfg.wt == "fp8":
+            w13[e], s13[e] = v
+        else:
+            w13[e] = v
+    for e, v in inputs.for_each_expert(cfg, inputs.expert_w2, experts):
+        if cfg.wt == "fp8":
+            w2[e], s2[e] = v
+        else:
+            w2[e] = v
+    d = {"w13": w13, "w2": w2}
+    if cfg.wt == "fp8":
+        d.update(w13_scale=s13, w2_scale=s2)
+    return d
+
+
+@pytest.mark.parametrize("name", ["c1_tiny_fp32", "c2_prefill_bf16", "c4_decode_bf16", "c5_skewed_fp8"])
+def test_full_layer_sampled(M, name):
+    cfg = configs.get(name)
+    say("full layer", name, "upload")
+    g = upload_layer(cfg)
+    s = M.shape_of(cfg)
+    T, E, k, H = cfg.T, cfg.E, cfg.k, cfg.H
+    out = empty_act((T, H), cfg.act)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    ws = torch.empty(M.moe_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    W = M.weights(g["w_gate"], g["w13"], g["w2"], g["sh_w13"], g["sh_w2"], g.get("w13_scale"),
+                  g.get("w2_scale"), g.get("bias"))
+    say("full layer", name, "run")
+    M.moe_layer(s, W, g["x"], out, idx, w, logits, ws)
+    torch.cuda.synchronize()
+    l_gpu, i_gpu, w_gpu = host(logits), host(idx), host(w)
+    bias = inputs.expert_bias(cfg)
+    # routing at full size, given the GPU's float32 logits
+    ridx, rw = O.route_topk(l_gpu, bias, k)
+    assert np.array_equal(i_gpu, ridx)
+    assert np.abs(w_gpu - rw).max() <= 1e-6
+    # counting sort at full size through the same kernels
+    say("full layer", name, "routing")
+    R = T * k
+    fp8 = cfg.wt == "fp8"
+    ex = torch.empty((R, H), dtype=torch.uint8 if fp8 else g["x"].dtype, device="cuda")
+    exs = torch.empty((R, H // 128), dtype=torch.float32, device="cuda") if fp8 else None
+    eri = torch.empty(R, dtype=torch.int32, device="cuda")
+    ssrc = torch.empty(R, dtype=torch.int32, device="cuda")
+    tpe = torch.empty(E, dtype=torch.int32, device="cuda")
+    offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    M.moe_init_routing(s, g["x"], idx, 0, ex, exs, eri, ssrc, tpe, offs, ws)
+    torch.cuda.synchronize()
+    rt = O.init_routing(i_gpu, E)
+    assert np.array_equal(host(tpe), rt["tokens_per_expert"])
+    assert np.array_equal(host(offs), rt["expert_offsets"])
+    assert np.array_equal(host(eri), rt["expanded_row_idx"])
+    assert np.array_equal(host(ssrc), rt["sorted_src"])
+    # sampled tokens through the oracle
+    S = sample_tokens(T, cfg.cid)
+    x_all = inputs.tokens(cfg)
+    xs = x_all[S]
+    rows = rt["expanded_row_idx"].reshape(T, k)[S].reshape(-1)
+    if fp8:
+        q, sc = O.quant_1x128(O.to_f64(xs, cfg.act).astype(np.float32))
+        assert np.array_equal(host(ex)[rows], np.repeat(q, k, axis=0))
+        assert np.array_equal(host(exs)[rows], np.repeat(sc, k, axis=0))
+    else:
+        got = host(ex)[rows]
+        if cfg.act == "bf16":
+            got = got.view(np.uint16)
+        assert np.array_equal(got, np.repeat(xs, k, axis=0))
+    experts = sorted(set(i_gpu[S].reshape(-1).tolist()))
+    say("full layer", name, f"oracle on tokens {S.tolist()} ({len(experts)} experts)")
+    d = {"cfg": dataclasses.replace(cfg, T=len(S)), "x": xs, "w_gate": inputs.gate_weight(cfg),
+         "bias": bias, "sh_w13": inputs.shared_w13(cfg), "sh_w2": inputs.shared_w2(cfg)}
+    d.update(expert_dict(cfg, experts))
+    ref = O.moe_layer(d, logits32_override=l_gpu[S])
+    err = max_row_rel_err(act_to_f64(out, cfg.act)[S], ref["out"])
+    say("full layer", name, f"max row rel err {err:.3e}")
+    assert err <= tol_of(cfg), err
+    lerr = np.abs(l_gpu[S] - ref["logits"]).max(axis=1) / np.abs(ref["logits"]).max(axis=1)
+    assert lerr.max() <= 1e-5
+    del g, ws, ex
+    torch.cuda.empty_cache()
+
+
+def test_ep_rank_share_full(M):
+    """One expert-parallel rank at ep=8: 8192 received rows tagged with experts 96..127,
+    re-routed, run through the 32 local experts, un-sorted back to arrival order; plus
+    the shared expert on the 1024 local tokens."""
+    cfg = configs.get("c3_ep_rank_bf16")
+    say("ep share full upload")
+    g = upload_layer(cfg)
+    s = M.shape_of(cfg)
+    R, H, E = cfg.T, cfg.H, cfg.E
+    ws = torch.empty(M.moe_workspace_bytes(s), dtype=torch.uint8, device="cuda")
+    ex = torch.empty((R, H), dtype=torch.int16, device="cuda")
+    eri = torch.empty(R, dtype=torch.int32, device="cuda")
+    ssrc = torch.empty(R, dtype=torch.int32, device="cuda")
+    tpe = torch.empty(E, dtype=torch.int32, device="cuda")
+    offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    say("ep share full run")
+    M.moe_init_routing(s, g["x"], g["ids"], cfg.e_base, ex, None, eri, ssrc, tpe, offs, ws)
+    y = empty_act((R, H), cfg.act)
+    wsf = torch.empty(M.moe_grouped_ffn_workspace_bytes(s, E, R), dtype=torch.uint8, device="cuda")
+    M.moe_grouped_ffn(s, E, R, ex, None, offs, g["w13"], None, g["w2"], None, y, wsf)
+    y_arr = empty_act((R, H), cfg.act)
+    M.moe_finalize_routing(s, y, None, None, eri, y_arr)
+    s_sh = M.shape(cfg.T_local, H, 1, 1, cfg.I_shared, cfg.I_shared, cfg.act, cfg.act)
+    sh = empty_act((cfg.T_local, H), cfg.act)
+    ws2 = torch.empty(M.moe_grouped_ffn_workspace_bytes(s_sh, 1, cfg.T_local), dtype=torch.uint8,
+                      device="cuda")
+    offs1 = torch.tensor([0, cfg.T_local], dtype=torch.int32, device="cuda")
+    M.moe_grouped_ffn(s_sh, 1, cfg.T_local, g["x_local"], None, offs1, g["sh_w13"], None, g["sh_w2"],
+                      None, sh, ws2)
+    torch.cuda.synchronize()
+    ids = inputs.pretagged_ids(cfg)
+    rt = O.init_routing(ids, E, cfg.e_base)
+    assert np.array_equal(host(tpe), rt["tokens_per_expert"])
+    assert np.array_equal(host(offs), rt["expert_offsets"])
+    assert np.array_equal(host(eri), rt["expanded_row_idx"])
+    assert np.array_equal(host(ssrc), rt["sorted_src"])
+    # un-sort is exact: arrival row a is sorted row expanded_row_idx[a]
+    assert np.array_equal(host(y_arr), host(y)[rt["expanded_row_idx"]])
+    S = sample_tokens(R, cfg.cid)
+    x = inputs.tokens(cfg)
+    experts = sorted(set((ids[S, 0] - cfg.e_base).tolist()))
+    wd = expert_dict(cfg, experts)
+    ref = np.stack([O.swiglu_ffn(O.to_f64(x[a:a + 1], cfg.act),
+                                 O.to_f64(wd["w13"][int(ids[a, 0]) - cfg.e_base], cfg.wt),
+                                 O.to_f64(wd["w2"][int(ids[a, 0]) - cfg.e_base], cfg.wt))[0] for a in S])
+    err = max_row_rel_err(act_to_f64(y_arr, cfg.act)[S], ref)
+    say("ep share full", f"routed max row rel err {err:.3e}")
+    assert err <= tol_of(cfg)
+    L = sample_tokens(cfg.T_local, cfg.cid + 1)
+    xl = inputs.local_tokens(cfg)[L]
+    sref = O.swiglu_ffn(O.to_f64(xl, cfg.act), O.to_f64(inputs.shared_w13(cfg), cfg.act),
+                        O.to_f64(inputs.shared_w2(cfg), cfg.act))
+    assert max_row_rel_err(act_to_f64(sh, cfg.act)[L], sref) <= tol_of(cfg)
+    del g, ws, wsf
+    torch.cuda.empty_cache()
