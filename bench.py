@@ -231,6 +231,19 @@ def cpu_baseline(cfg, target_s=15.0, max_tokens=None):
                       f"{dt:.1f} s"}
 
 
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of `nbytes`: reads and writes exactly nbytes per
+    launch, so the FETCH_SIZE / WRITE_SIZE counters of this launch give the factor
+    between counter units and bytes."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": reps}), flush=True)
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -241,7 +254,12 @@ def main():
     ap.add_argument("--config", default="c2_prefill_bf16")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (scales the HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: this layer is one GPU's share of tokens and "
               f"experts, with no cross-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)

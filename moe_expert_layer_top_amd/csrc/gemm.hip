@@ -35,8 +35,8 @@
 
 namespace moe {
 
-template <int WM, int WN, int TM, int TN, int EPI, bool FP8>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
+template <int WM, int WN, int TM, int TN, int EPI, bool FP8, bool UNIFORM>
+__device__ __forceinline__ void gemm_body(const GemmArgs& p) {
   constexpr int NT = WM * WN * 64;
   constexpr int BM = WM * TM * 16;
   constexpr int BN = WN * TN * 16;
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
   const int nt = rem % p.n_tiles;
   const int split = rem / p.n_tiles;
   Unit un;
-  if (p.uniform_rows > 0) {
+  if constexpr (UNIFORM) {
     if (u * BM >= p.uniform_rows) return;
     un.group = 0;
     un.row0 = u * BM;
@@ -366,6 +366,19 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
 #undef MOE_GLOAD
 #undef MOE_LSTORE
 
+// Experts: units come from the device-built table.
+template <int WM, int WN, int TM, int TN, int EPI, bool FP8>
+__global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs p) {
+  gemm_body<WM, WN, TM, TN, EPI, FP8, false>(p);
+}
+
+// One group of `uniform_rows` rows (shared expert, gate projection): units are
+// consecutive BM-row slices, known without a table.
+template <int WM, int WN, int TM, int TN, int EPI, bool FP8>
+__global__ __launch_bounds__(WM* WN * 64) void dense_gemm_kernel(GemmArgs p) {
+  gemm_body<WM, WN, TM, TN, EPI, FP8, true>(p);
+}
+
 // ------------------------------------------------------------------ unit planner
 // One block: units per group = ceil(n / BM) near-equal slices (rows rounded up to
 // 16), prefix-summed over groups, then each group writes its slices.
@@ -441,7 +454,13 @@ hipError_t go(const GemmArgs& a, int max_units, hipStream_t st) {
   const long long blocks = slots * kXcds * per_unit;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  gemm_kernel<WM, WN, TM, TN, EPI, FP8><<<static_cast<unsigned>(blocks), WM * WN * 64, 0, st>>>(a);
+  if (a.uniform_rows > 0) {
+    dense_gemm_kernel<WM, WN, TM, TN, EPI, FP8>
+        <<<static_cast<unsigned>(blocks), WM * WN * 64, 0, st>>>(a);
+  } else {
+    grouped_gemm_kernel<WM, WN, TM, TN, EPI, FP8>
+        <<<static_cast<unsigned>(blocks), WM * WN * 64, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 
