@@ -1,0 +1,57 @@
+"""The bench's roofline accounting against the formulas and worked numbers the pages print.
+
+Fixture: tests/golden/page_accounting.json (each value cites its passage)."""
+import json
+import os
+
+import numpy as np
+
+import bench
+from synth import configs
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_accounting.json")))
+
+
+def test_rows_per_expert_worked_example():
+    ex = GOLD["rows_per_expert"]
+    assert bench.rows_per_expert(ex["batch"], ex["qlen"], ex["topk"], ex["ep"], ex["experts"]) == ex["m"]
+
+
+def test_group_gemm_formulas():
+    g = GOLD["group_gemm"]
+    assert bench.group_gemm_flops(g["g"], g["m"], g["k"], g["n"]) == g["flops"]
+    assert bench.group_gemm_elems(g["g"], g["m"], g["k"], g["n"]) == g["elems"]
+    d = GOLD["gemm"]
+    assert bench.gemm_flops(d["m"], d["k"], d["n"]) == d["flops"]
+    assert bench.gemm_elems(d["m"], d["k"], d["n"]) == d["elems"]
+
+
+def test_fp8_scale_shapes():
+    s = GOLD["fp8_scale_shapes"]
+    M, K, N = s["M"], s["K"], s["N"]
+    assert (M, -(-K // 128)) == tuple(s["activation"])
+    assert (-(-K // 128), -(-N // 128)) == tuple(s["weight"])
+
+
+def test_layer_accounting_matches_group_gemm_formula():
+    """With every expert holding m rows, GEMM1's FLOPs are the grouped-GEMM formula with
+    n = 2I, and its weight bytes are E panels of 2I x H."""
+    cfg = configs.get("c2_prefill_bf16")
+    tpe = np.full(cfg.E, cfg.T * cfg.k // cfg.E)
+    acc = bench.account(cfg, tpe)
+    m = cfg.T * cfg.k // cfg.E
+    assert acc["ffn1"]["flops"] == bench.group_gemm_flops(cfg.E, m, cfg.H, 2 * cfg.I)
+    assert acc["ffn2"]["flops"] == bench.group_gemm_flops(cfg.E, m, cfg.I, cfg.H)
+    w = cfg.E * 2 * cfg.I * cfg.H * 2
+    assert acc["ffn1"]["bytes"] == w + cfg.R * cfg.H * 2 + cfg.R * cfg.I * 2
+    # empty experts cost no weight bytes
+    tpe2 = tpe.copy()
+    tpe2[:10] = 0
+    assert bench.account(cfg, tpe2)["ffn1"]["bytes"] < acc["ffn1"]["bytes"]
+
+
+def test_activated_experts_per_gpu_example():
+    """[MND §Single node vs multi-node]: batch 1, query length 2, top-8 over 8 GPUs ->
+    on average 2*8/8 = 2 activated experts per GPU."""
+    ex = GOLD["activated_experts"]
+    assert ex["tokens"] * ex["topk"] / ex["gpus"] == ex["per_gpu"]
