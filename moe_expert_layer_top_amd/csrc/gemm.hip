@@ -366,6 +366,291 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
 #undef MOE_GLOAD
 #undef MOE_LSTORE
 
+// ------------------------------------------------------------------ DMA pipeline (bf16)
+// Second pipeline for bf16 operands: global -> LDS with global_load_lds_dwordx4 (each
+// lane lands 16 bytes at lds + 16 * lane, no staging registers) into an NST-deep ring
+// of stage buffers; step s waits only for its own loads (vmcnt), so NST - 1 stages of
+// weight traffic are in flight per workgroup.  Stage = ROWB bytes of K for all BM
+// activation rows and BN weight rows.  The ring buffers are distinct LDS objects and
+// the step loop is unrolled by NST so every buffer index is a compile-time constant:
+// the compiler can then see that the DMA into one buffer never aliases the fragment
+// reads of another and keeps them unordered.
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without a memory fence.  __syncthreads() also drains every
+// outstanding global access (vmcnt(0)), which would empty the DMA ring at each step;
+// here each wave has already waited for its own stage loads (wait_vmcnt), its LDS
+// fragment reads have returned before their MFMAs, and the empty asm statements keep
+// the compiler from moving memory operations across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 16 bytes per lane from `g` into lds_chunk + 16 * lane (global_load_lds_dwordx4; the
+// LDS base goes through M0).  Issued as inline assembly so the compiler does not
+// track it: it would otherwise wait for every in-flight DMA before any LDS read it
+// cannot prove disjoint.  Ordering is explicit instead: each step waits on vmcnt for
+// its own stage, and vmcnt completes in order, so extra in-flight DMAs can only make
+// compiler-generated waits stricter, never looser.
+__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_chunk) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+          (__attribute__((address_space(3))) uint8_t*)lds_chunk)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(m0)
+               : "memory", "m0");
+}
+
+template <int ROWB>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (ROWB == 128) return row & 7;
+  else return (row >> 1) & 3;
+}
+
+template <int WM, int WN, int TM, int TN, int EPI, bool UNIFORM, int ROWB, int NST>
+__device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int NW = NT / 64;
+  constexpr int BM = WM * TM * 16;
+  constexpr int BN = WN * TN * 16;
+  constexpr int EB = 2;
+  constexpr int KSTEP = ROWB / EB;       // elements per stage
+  constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
+  constexpr int RPC = 64 / CPR;          // rows per 1 KB DMA (one wave instruction)
+  constexpr int A_LD = BM / RPC, B_LD = BN / RPC;
+  constexpr int LD_ALL = A_LD + B_LD;
+  constexpr int LMAX = (LD_ALL + NW - 1) / NW;   // DMA instructions per wave per stage
+  constexpr int LREM = LD_ALL % NW;              // waves < LREM issue LMAX, others LMAX-1
+  constexpr int STAGE = (BM + BN) * ROWB;
+  constexpr bool SWIGLU = (EPI == EPI_SWIGLU_BF16);
+  static_assert(BM % RPC == 0 && BN % RPC == 0, "tiles are whole DMA chunks");
+  static_assert(NST >= 2 && NST <= 4, "ring depth");
+  static_assert(!SWIGLU || TN % 2 == 0, "swiglu needs gate/up tile pairs");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[NST > 2 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[NST > 3 ? STAGE : 16];
+
+  const int bid = blockIdx.x;
+  const int xcd = bid % kXcds;
+  const int slot = bid / kXcds;
+  const int per_unit = p.n_tiles * p.splits;
+  const int u = (slot / per_unit) * kXcds + xcd;
+  const int rem = slot % per_unit;
+  const int nt = rem % p.n_tiles;
+  const int split = rem / p.n_tiles;
+  Unit un;
+  if constexpr (UNIFORM) {
+    if (u * BM >= p.uniform_rows) return;
+    un.group = 0;
+    un.row0 = u * BM;
+    un.rows = min(BM, p.uniform_rows - u * BM);
+  } else {
+    if (u >= *p.n_units) return;
+    un = p.units[u];
+  }
+  const int rows = un.rows;
+  if (rows <= 0) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  const int mtiles = (rows + 15) >> 4;
+  int jcount = mtiles > wm ? (mtiles - wm + WM - 1) / WM : 0;
+  if (jcount > TM) jcount = TM;
+
+  const int k0 = split * p.k_chunk;
+  const int k1 = min(p.K, k0 + p.k_chunk);
+  const int nsteps = (k1 - k0) / KSTEP;
+
+  const uint8_t* a_base = p.A + static_cast<long long>(un.row0) * p.lda + static_cast<long long>(k0) * EB;
+  const uint8_t* b_base = p.B + static_cast<long long>(un.group) * p.b_group + static_cast<long long>(k0) * EB;
+
+  // DMA plan: chunk q = wave + i * NW; lane -> (row q*RPC + lane/CPR, physical 16-byte
+  // slot lane%CPR), which holds logical K chunk (lane%CPR) ^ swz(row).  Rows past the
+  // unit and columns past N re-load a valid row; their results are never stored.
+  uint32_t goff[LMAX];
+  const int lrow = lane / CPR;
+  const int lphys = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < LMAX; ++i) {
+    const int q = wave + i * NW;
+    uint32_t off = 0;
+    if (q < A_LD) {
+      const int r = q * RPC + lrow;
+      const int rc = r < rows ? r : rows - 1;
+      off = static_cast<uint32_t>(rc * p.lda + ((lphys ^ swz<ROWB>(r)) << 4));
+    } else if (q < LD_ALL) {
+      const int j = (q - A_LD) * RPC + lrow;
+      int col, grow;
+      if constexpr (SWIGLU) {
+        constexpr int WCOLS = TN * 16, HALF = TN * 8;
+        const int wn2 = j / WCOLS, jj = j % WCOLS;
+        col = nt * (BN / 2) + wn2 * HALF + (jj % HALF);
+        grow = (jj < HALF ? 0 : p.up_off) + col;
+      } else {
+        col = nt * BN + j;
+        grow = col;
+      }
+      if (col >= p.N) grow -= col - (p.N - 1);
+      off = static_cast<uint32_t>(static_cast<long long>(grow) * p.ldb + ((lphys ^ swz<ROWB>(j)) << 4));
+    }
+    goff[i] = off;
+  }
+
+  auto issue = [&](int step, uint8_t* buf) __attribute__((always_inline)) {
+    const long long kb = static_cast<long long>(step) * ROWB;
+#pragma unroll
+    for (int i = 0; i < LMAX; ++i) {
+      const int q = wave + i * NW;
+      if (q < A_LD) {
+        dma16(a_base + goff[i] + kb, buf + q * 1024);
+      } else if (q < LD_ALL) {
+        dma16(b_base + goff[i] + kb, buf + BM * ROWB + (q - A_LD) * 1024);
+      }
+    }
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int j = 0; j < TM; ++j)
+#pragma unroll
+    for (int i = 0; i < TN; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int frag_row = lane & 15;
+  const int kgrp = lane >> 4;
+
+  auto compute = [&](const uint8_t* buf) __attribute__((always_inline)) {
+    const uint8_t* lb = buf + BM * ROWB;
+#pragma unroll
+    for (int kk = 0; kk < ROWB / 64; ++kk) {
+      const int c = kk * 4 + kgrp;
+      bf16x8 bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TN; ++i) {
+        const int rb_ = wn * TN * 16 + 16 * i + frag_row;
+        bfr[i] = *reinterpret_cast<const bf16x8*>(lb + rb_ * ROWB + ((c ^ swz<ROWB>(rb_)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        if (j < jcount) {
+          const int ra_ = 16 * (j * WM + wm) + frag_row;
+          const bf16x8 afr =
+              *reinterpret_cast<const bf16x8*>(buf + ra_ * ROWB + ((c ^ swz<ROWB>(ra_)) << 4));
+#pragma unroll
+          for (int i = 0; i < TN; ++i)
+            acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[i], acc[j][i], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // per-wave count of DMA instructions per stage (wave-uniform)
+  const bool more = wave < (LREM == 0 ? NW : LREM);
+  // wait until the loads of the current step landed; `later` = steps issued after it
+  auto wait_step = [&](int later) __attribute__((always_inline)) {
+    if (later >= NST - 2 && NST > 2) {
+      if (more) wait_vmcnt<(NST > 2 ? (NST - 2) * LMAX : 0)>();
+      else wait_vmcnt<(NST > 2 ? (NST - 2) * (LMAX - 1) : 0)>();
+    } else if (later == 1 && NST > 3) {
+      if (more) wait_vmcnt<LMAX>();
+      else wait_vmcnt<LMAX - 1>();
+    } else {
+      wait_vmcnt<0>();
+    }
+  };
+
+  // prologue: steps 0 .. NST-2
+#pragma unroll
+  for (int b = 0; b < NST - 1; ++b) {
+    if (b < nsteps) issue(b, b == 0 ? st0 : b == 1 ? st1 : b == 2 ? st2 : st3);
+  }
+  for (int s0 = 0; s0 < nsteps; s0 += NST) {
+#pragma unroll
+    for (int b = 0; b < NST; ++b) {
+      const int s = s0 + b;
+      if (s < nsteps) {
+        const int issued_after = min(nsteps - 1, s + NST - 2) - s;
+        wait_step(issued_after);
+        lds_barrier();
+        // refill the buffer consumed at step s - 1 with step s + NST - 1
+        const int nb = (b + NST - 1) % NST;
+        if (s + NST - 1 < nsteps) issue(s + NST - 1, nb == 0 ? st0 : nb == 1 ? st1 : nb == 2 ? st2 : st3);
+        compute(b == 0 ? st0 : b == 1 ? st1 : b == 2 ? st2 : st3);
+      }
+    }
+  }
+
+  // ---- epilogue (C fragment: lane holds column lane & 15, rows 4 * (lane >> 4) + r)
+  const int ccol = lane & 15;
+  if constexpr (EPI == EPI_STORE_BF16 || EPI == EPI_STORE_F32) {
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      if (j >= jcount) continue;
+      const int rbase = 16 * (j * WM + wm) + 4 * kgrp;
+#pragma unroll
+      for (int i = 0; i < TN; ++i) {
+        const int col = nt * BN + wn * TN * 16 + 16 * i + ccol;
+        if (col >= p.N) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = rbase + r;
+          if (row >= rows) continue;
+          const long long o = static_cast<long long>(un.row0 + row) * p.ldc + col;
+          if constexpr (EPI == EPI_STORE_BF16) {
+            static_cast<uint16_t*>(p.C)[o] = f32_to_bf16(acc[j][i][r]);
+          } else {
+            static_cast<float*>(p.C)[o + split * p.c_split] = acc[j][i][r];
+          }
+        }
+      }
+    }
+  } else {
+    constexpr int HT = TN / 2;
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      if (j >= jcount) continue;
+      const int rbase = 16 * (j * WM + wm) + 4 * kgrp;
+#pragma unroll
+      for (int i = 0; i < HT; ++i) {
+        const int col = nt * (BN / 2) + wn * (TN * 8) + 16 * i + ccol;
+        if (col >= p.N) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = rbase + r;
+          if (row >= rows) continue;
+          const float g = acc[j][i][r];
+          const float up = acc[j][i + HT][r];
+          static_cast<uint16_t*>(p.C)[static_cast<long long>(un.row0 + row) * p.ldc + col] =
+              f32_to_bf16(g / (1.0f + __expf(-g)) * up);
+        }
+      }
+    }
+  }
+}
+
+template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST>
+__global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs p) {
+  gemm_dma_body<WM, WN, TM, TN, EPI, false, ROWB, NST>(p);
+}
+
+template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST>
+__global__ __launch_bounds__(WM* WN * 64) void dense_gemm_dma_kernel(GemmArgs p) {
+  gemm_dma_body<WM, WN, TM, TN, EPI, true, ROWB, NST>(p);
+}
+
 // Experts: units come from the device-built table.
 template <int WM, int WN, int TM, int TN, int EPI, bool FP8>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs p) {
@@ -464,6 +749,23 @@ hipError_t go(const GemmArgs& a, int max_units, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST>
+hipError_t go_dma(const GemmArgs& a, int max_units, hipStream_t st) {
+  const long long per_unit = static_cast<long long>(a.n_tiles) * a.splits;
+  const long long slots = (static_cast<long long>(max_units) + kXcds - 1) / kXcds;
+  const long long blocks = slots * kXcds * per_unit;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (a.uniform_rows > 0) {
+    dense_gemm_dma_kernel<WM, WN, TM, TN, EPI, ROWB, NST>
+        <<<static_cast<unsigned>(blocks), WM * WN * 64, 0, st>>>(a);
+  } else {
+    grouped_gemm_dma_kernel<WM, WN, TM, TN, EPI, ROWB, NST>
+        <<<static_cast<unsigned>(blocks), WM * WN * 64, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
+
 template <int WM, int WN, int TM, int TN>
 hipError_t go_epi(Epilogue epi, bool fp8, const GemmArgs& a, int max_units, hipStream_t st) {
   if (fp8) {
@@ -483,7 +785,7 @@ hipError_t go_epi(Epilogue epi, bool fp8, const GemmArgs& a, int max_units, hipS
 
 int gemm_block_m(GemmCfg cfg, bool fp8) {
   switch (cfg) {
-    case CFG_BIG: return fp8 ? 128 : 256;
+    case CFG_BIG: return fp8 ? 128 : 320;
     case CFG_SMALL: return 32;
     default: return 64;
   }
@@ -496,12 +798,18 @@ hipError_t launch_gemm(GemmCfg cfg, Epilogue epi, bool fp8, const GemmArgs& a, i
   switch (cfg) {
     case CFG_BIG:
       // fp8 keeps a per-K-block product next to the accumulators: shorter row tile
-      return fp8 ? go_epi<4, 2, 2, 8>(epi, fp8, a, max_units, st)
-                 : go_epi<4, 2, 4, 8>(epi, fp8, a, max_units, st);
-    case CFG_SMALL: return go_epi<1, 4, 2, 4>(epi, fp8, a, max_units, st);
+      if (fp8) return go_epi<4, 2, 2, 8>(epi, fp8, a, max_units, st);
+      if (epi == EPI_SWIGLU_BF16) return go_dma<4, 2, 5, 8, EPI_SWIGLU_BF16, 64, 4>(a, max_units, st);
+      if (epi == EPI_STORE_BF16) return go_dma<4, 2, 5, 8, EPI_STORE_BF16, 64, 4>(a, max_units, st);
+      return hipErrorInvalidValue;
+    case CFG_SMALL:
+      if (fp8) return go_epi<1, 4, 2, 4>(epi, fp8, a, max_units, st);
+      if (epi == EPI_SWIGLU_BF16) return go_dma<1, 4, 2, 4, EPI_SWIGLU_BF16, 128, 4>(a, max_units, st);
+      if (epi == EPI_STORE_BF16) return go_dma<1, 4, 2, 4, EPI_STORE_BF16, 128, 4>(a, max_units, st);
+      return hipErrorInvalidValue;
     case CFG_GATE:
       if (epi != EPI_STORE_F32 || fp8) return hipErrorInvalidValue;
-      return go<1, 4, 4, 4, EPI_STORE_F32, false>(a, max_units, st);
+      return go_dma<1, 4, 4, 4, EPI_STORE_F32, 128, 3>(a, max_units, st);
   }
   return hipErrorInvalidValue;
 }
