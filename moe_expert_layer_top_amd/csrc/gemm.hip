@@ -30,6 +30,8 @@
 //     h column sit in the same lane), optional 1x128 fp8 quantization of h,
 //     bf16 store, or fp32 split-k partials.
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -374,7 +376,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& p) {
 // activation rows and BN weight rows.  The ring buffers are distinct LDS objects and
 // the step loop is unrolled by NST so every buffer index is a compile-time constant:
 // the compiler can then see that the DMA into one buffer never aliases the fragment
-// reads of another and keeps them unordered.
+// reads of another and keeps them unordered.  Prefill tiles (320 x 256) use 128-byte
+// stages in a 2-deep ring: each stage then reads whole 128-byte lines of every row,
+// which the L2 serves at a markedly higher rate than the 64-byte half lines of a
+// deeper 64-byte ring, and that outweighs the shallower prefetch.
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -532,28 +537,33 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   const int frag_row = lane & 15;
   const int kgrp = lane >> 4;
 
-  auto compute = [&](const uint8_t* buf) __attribute__((always_inline)) {
+  // One stage of MFMAs for a wavefront owning J valid 16-row tiles.  J is a
+  // compile-time constant (the main loop is instantiated per row-tile count), so
+  // every fragment read of a K slice is issued before its first MFMA and no
+  // branch separates them.
+  auto compute = [&](const uint8_t* buf, auto Jc) __attribute__((always_inline)) {
+    constexpr int J = decltype(Jc)::value;
     const uint8_t* lb = buf + BM * ROWB;
 #pragma unroll
     for (int kk = 0; kk < ROWB / 64; ++kk) {
       const int c = kk * 4 + kgrp;
       bf16x8 bfr[TN];
+      bf16x8 afr[J > 0 ? J : 1];
 #pragma unroll
       for (int i = 0; i < TN; ++i) {
         const int rb_ = wn * TN * 16 + 16 * i + frag_row;
         bfr[i] = *reinterpret_cast<const bf16x8*>(lb + rb_ * ROWB + ((c ^ swz<ROWB>(rb_)) << 4));
       }
 #pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        if (j < jcount) {
-          const int ra_ = 16 * (j * WM + wm) + frag_row;
-          const bf16x8 afr =
-              *reinterpret_cast<const bf16x8*>(buf + ra_ * ROWB + ((c ^ swz<ROWB>(ra_)) << 4));
-#pragma unroll
-          for (int i = 0; i < TN; ++i)
-            acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[i], acc[j][i], 0, 0, 0);
-        }
+      for (int j = 0; j < J; ++j) {
+        const int ra_ = 16 * (j * WM + wm) + frag_row;
+        afr[j] = *reinterpret_cast<const bf16x8*>(buf + ra_ * ROWB + ((c ^ swz<ROWB>(ra_)) << 4));
       }
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[j], bfr[i], acc[j][i], 0, 0, 0);
     }
   };
 
@@ -577,20 +587,33 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   for (int b = 0; b < NST - 1; ++b) {
     if (b < nsteps) issue(b, b == 0 ? st0 : b == 1 ? st1 : b == 2 ? st2 : st3);
   }
-  for (int s0 = 0; s0 < nsteps; s0 += NST) {
+  auto mainloop = [&](auto Jc) __attribute__((always_inline)) {
+    for (int s0 = 0; s0 < nsteps; s0 += NST) {
 #pragma unroll
-    for (int b = 0; b < NST; ++b) {
-      const int s = s0 + b;
-      if (s < nsteps) {
-        const int issued_after = min(nsteps - 1, s + NST - 2) - s;
-        wait_step(issued_after);
-        lds_barrier();
-        // refill the buffer consumed at step s - 1 with step s + NST - 1
-        const int nb = (b + NST - 1) % NST;
-        if (s + NST - 1 < nsteps) issue(s + NST - 1, nb == 0 ? st0 : nb == 1 ? st1 : nb == 2 ? st2 : st3);
-        compute(b == 0 ? st0 : b == 1 ? st1 : b == 2 ? st2 : st3);
+      for (int b = 0; b < NST; ++b) {
+        const int s = s0 + b;
+        if (s < nsteps) {
+          const int issued_after = min(nsteps - 1, s + NST - 2) - s;
+          wait_step(issued_after);
+          lds_barrier();
+          // refill the buffer consumed at step s - 1 with step s + NST - 1
+          const int nb = (b + NST - 1) % NST;
+          if (s + NST - 1 < nsteps) issue(s + NST - 1, nb == 0 ? st0 : nb == 1 ? st1 : nb == 2 ? st2 : st3);
+          compute(b == 0 ? st0 : b == 1 ? st1 : b == 2 ? st2 : st3, Jc);
+        }
       }
     }
+  };
+  // jcount is wave-uniform and at most TM; every instantiation runs the same
+  // sequence of barriers, so wavefronts with different counts stay in step.
+  static_assert(TM <= 5, "row-tile dispatch covers TM <= 5");
+  switch (jcount) {
+    case 5: if constexpr (TM >= 5) mainloop(std::integral_constant<int, (TM >= 5 ? 5 : 0)>{}); break;
+    case 4: if constexpr (TM >= 4) mainloop(std::integral_constant<int, (TM >= 4 ? 4 : 0)>{}); break;
+    case 3: if constexpr (TM >= 3) mainloop(std::integral_constant<int, (TM >= 3 ? 3 : 0)>{}); break;
+    case 2: if constexpr (TM >= 2) mainloop(std::integral_constant<int, (TM >= 2 ? 2 : 0)>{}); break;
+    case 1: mainloop(std::integral_constant<int, 1>{}); break;
+    default: mainloop(std::integral_constant<int, 0>{}); break;
   }
 
   // ---- epilogue (C fragment: lane holds column lane & 15, rows 4 * (lane >> 4) + r)
@@ -799,8 +822,8 @@ hipError_t launch_gemm(GemmCfg cfg, Epilogue epi, bool fp8, const GemmArgs& a, i
     case CFG_BIG:
       // fp8 keeps a per-K-block product next to the accumulators: shorter row tile
       if (fp8) return go_epi<4, 2, 2, 8>(epi, fp8, a, max_units, st);
-      if (epi == EPI_SWIGLU_BF16) return go_dma<4, 2, 5, 8, EPI_SWIGLU_BF16, 64, 4>(a, max_units, st);
-      if (epi == EPI_STORE_BF16) return go_dma<4, 2, 5, 8, EPI_STORE_BF16, 64, 4>(a, max_units, st);
+      if (epi == EPI_SWIGLU_BF16) return go_dma<4, 2, 5, 8, EPI_SWIGLU_BF16, 128, 2>(a, max_units, st);
+      if (epi == EPI_STORE_BF16) return go_dma<4, 2, 5, 8, EPI_STORE_BF16, 128, 2>(a, max_units, st);
       return hipErrorInvalidValue;
     case CFG_SMALL:
       if (fp8) return go_epi<1, 4, 2, 4>(epi, fp8, a, max_units, st);
