@@ -95,9 +95,32 @@ def account(cfg, tpe) -> dict:
         "shared": dict(flops=2 * T * H * 2 * Is + 2 * T * Is * H,
                        bytes=3 * Is * H * ab + T * H * ab + 2 * T * Is * ab + T * H * ab,
                        dt=cfg.act),
+        # the shared expert's two GEMMs separately (x -> h_s, h_s -> s)
+        "shared1": dict(flops=2 * T * H * 2 * Is, bytes=2 * Is * H * ab + T * H * ab + T * Is * ab,
+                        dt=cfg.act),
+        "shared2": dict(flops=2 * T * Is * H, bytes=Is * H * ab + T * Is * ab + T * H * ab,
+                        dt=cfg.act),
         "finalize": dict(flops=0, bytes=R * H * ab + 2 * T * H * ab + T * k * 8, dt=None),
     }
     return acc
+
+
+def shared_is_merged(cfg) -> bool:
+    """moe_layer runs the shared expert as one more group of the routed grouped-GEMM
+    launches when it has the routed experts' shape and dtype (bf16, I_shared == I)."""
+    return cfg.act == "bf16" and cfg.wt == "bf16" and cfg.I_shared == cfg.I
+
+
+def launch_accounting(cfg, acc: dict) -> dict:
+    """Work per timed launch class: with the shared expert merged, the ffn1 / ffn2
+    launches also do the shared expert's two GEMMs and there is no shared stage."""
+    out = {k: v for k, v in acc.items() if k not in ("shared1", "shared2")}
+    if shared_is_merged(cfg):
+        for k, sk in (("ffn1", "shared1"), ("ffn2", "shared2")):
+            out[k] = dict(flops=acc[k]["flops"] + acc[sk]["flops"],
+                          bytes=acc[k]["bytes"] + acc[sk]["bytes"], dt=acc[k]["dt"])
+        del out["shared"]
+    return out
 
 
 def roofline_entry(acc_k: dict, ms: float) -> dict:
@@ -270,8 +293,10 @@ def main():
     r = run_gpu(cfg, args.steps, args.warmup)
     ms = r["total_ms"] / args.steps
     tokens = cfg.shared_rows
-    acc = account(cfg, r["tpe"])
+    acc = launch_accounting(cfg, account(cfg, r["tpe"]))
     kern = {name: roofline_entry(acc[name], r["stage_ms"][name]) for name in acc}
+    if shared_is_merged(cfg):
+        kern["shared"] = {"ms": r["stage_ms"]["shared"], "merged_into": ["ffn1", "ffn2"]}
     dom = max(("ffn1", "ffn2"), key=lambda n: r["stage_ms"][n])
     dk = kern[dom]
     if dk["bound"] == "mfma":

@@ -80,16 +80,26 @@ moe::GemmCfg ffn_cfg(int G, int R_max) {
   return (G > 0 && R_max <= 64LL * G) ? moe::CFG_SMALL : moe::CFG_BIG;
 }
 
-int max_units(moe::GemmCfg cfg, bool fp8, int G, int R_max) {
+// Upper bound on the units the planner writes: every group of n > 0 rows makes
+// ceil(n / bm) <= n / bm + 1 units; the extra group (if any) likewise.
+int max_units(moe::GemmCfg cfg, bool fp8, int G, int R_max, int extra_rows = 0) {
   const int bm = moe::gemm_block_m(cfg, fp8);
-  return R_max / bm + std::min(G, R_max);
+  return R_max / bm + std::min(G, R_max) + (extra_rows > 0 ? extra_rows / bm + 1 : 0);
+}
+
+// The shared expert runs inside the routed grouped-GEMM launches (as one extra group
+// whose units read x and the shared weights) when it has the routed experts' shape
+// and dtype: bf16 activations and weights, I_shared == I.
+bool merge_shared(const moe_shape* s) {
+  return s->act == MOE_BF16 && s->wt == MOE_BF16 && s->I_shared == s->I;
 }
 
 struct FfnLayout {
-  size_t units, n_units, h, h_scale, total;
+  size_t units, n_units, h, h_scale, h2, total;
 };
 
-FfnLayout ffn_layout(const moe_shape* s, int G, int R_max, int I) {
+// extra_rows > 0: room for the extra group's units and its intermediate h2 [extra_rows, I].
+FfnLayout ffn_layout(const moe_shape* s, int G, int R_max, int I, int extra_rows = 0) {
   FfnLayout L{};
   size_t o = 0;
   if (s->act == MOE_F32) {
@@ -100,8 +110,9 @@ FfnLayout ffn_layout(const moe_shape* s, int G, int R_max, int I) {
   }
   const moe::GemmCfg cfg = ffn_cfg(G, R_max);
   L.units = o;
-  o += align_up(static_cast<size_t>(std::max(1, max_units(cfg, s->wt == MOE_FP8_E4M3, G, R_max))) *
-                 sizeof(Unit));
+  o += align_up(static_cast<size_t>(std::max(
+                    1, max_units(cfg, s->wt == MOE_FP8_E4M3, G, R_max, extra_rows))) *
+                sizeof(Unit));
   L.n_units = o;
   o += kAlign;
   L.h = o;
@@ -109,6 +120,8 @@ FfnLayout ffn_layout(const moe_shape* s, int G, int R_max, int I) {
   o += align_up(static_cast<size_t>(R_max) * I * (fp8 ? 1 : 2));
   L.h_scale = o;
   if (fp8) o += align_up(static_cast<size_t>(R_max) * (I / 128) * 4);
+  L.h2 = o;
+  if (extra_rows > 0) o += align_up(static_cast<size_t>(extra_rows) * I * 2);
   L.total = o;
   return L;
 }
@@ -141,11 +154,12 @@ Layout layer_layout(const moe_shape* s) {
   L.ex = o;            o += align_up(R * H * (fp8 ? 1 : ab));
   L.ex_scale = o;      if (fp8) o += align_up(R * (H / 128) * 4);
   L.y = o;             o += align_up(R * H * ab);
-  L.ffn = o;           o += ffn_layout(s, s->E, static_cast<int>(R), s->I).total;
+  const bool merged = merge_shared(s);
+  L.ffn = o;           o += ffn_layout(s, s->E, static_cast<int>(R), s->I, merged ? s->T : 0).total;
   L.sh_out = o;        o += align_up(T * H * ab);
   moe_shape sh = *s;
   sh.wt = s->act;  // the shared expert is never fp8
-  L.sh_ffn = o;        o += ffn_layout(&sh, 1, s->T, s->I_shared).total;
+  L.sh_ffn = o;        if (!merged) o += ffn_layout(&sh, 1, s->T, s->I_shared).total;
   L.total = o;
   return L;
 }
@@ -214,11 +228,15 @@ struct FfnIo {
   void* y;
 };
 
+// `alt` (bf16 only): the shared expert as group G of alt_rows rows in the same
+// launches; alt->a is x [alt_rows, H], alt->w13 / alt->w2 its weights, alt->y its
+// output [alt_rows, H].
 moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io, void* ws,
                    hipStream_t st, const Prof& prof = Prof(), int ev_plan = -1, int ev_ffn1 = -1,
-                   int ev_ffn2 = -1) {
-  if (R_max == 0) return MOE_OK;
-  const FfnLayout L = ffn_layout(s, G, R_max, I);
+                   int ev_ffn2 = -1, const FfnIo* alt = nullptr, int alt_rows = 0) {
+  if (!alt) alt_rows = 0;
+  if (R_max == 0 && alt_rows == 0) return MOE_OK;
+  const FfnLayout L = ffn_layout(s, G, R_max, I, alt_rows);
   const int H = s->H;
   if (s->act == MOE_F32) {
     return hip_status(moe::launch_grouped_ffn_f32(
@@ -233,8 +251,9 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
   int32_t* n_units = at<int32_t>(ws, L.n_units);
   int mu;
   if (io.offsets) {
-    mu = max_units(cfg, fp8, G, R_max);
-    hipError_t e = moe::launch_plan(io.offsets, G, 0, bm, std::max(1, mu), units, n_units, st);
+    mu = max_units(cfg, fp8, G, R_max, alt_rows);
+    hipError_t e = moe::launch_plan(io.offsets, G, 0, alt_rows, bm, std::max(1, mu), units,
+                                    n_units, st);
     if (e != hipSuccess) return MOE_EHIP;
   } else {
     mu = (R_max + bm - 1) / bm;
@@ -264,6 +283,14 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
   g1.n_tiles = I / 128;
   g1.splits = 1;
   g1.k_chunk = H;
+  if (alt_rows > 0) {
+    g1.alt_group = G;
+    g1.A2 = static_cast<const uint8_t*>(alt->a);
+    g1.lda2 = static_cast<long long>(H) * 2;
+    g1.B2 = static_cast<const uint8_t*>(alt->w13);
+    g1.C2 = at<uint8_t>(ws, L.h2);
+    g1.ldc2 = I;
+  }
   hipError_t e = moe::launch_gemm(cfg, fp8 ? moe::EPI_SWIGLU_FP8 : moe::EPI_SWIGLU_BF16, fp8, g1,
                                   mu, st);
   if (e != hipSuccess || prof.mark(ev_ffn1, st) != hipSuccess) return MOE_EHIP;
@@ -286,6 +313,13 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
   g2.up_off = 0;
   g2.n_tiles = (H + moe::gemm_block_n(cfg) - 1) / moe::gemm_block_n(cfg);
   g2.k_chunk = I;
+  if (alt_rows > 0) {
+    g2.A2 = at<uint8_t>(ws, L.h2);
+    g2.lda2 = static_cast<long long>(I) * 2;
+    g2.B2 = static_cast<const uint8_t*>(alt->w2);
+    g2.C2 = alt->y;
+    g2.ldc2 = H;
+  }
   e = moe::launch_gemm(cfg, moe::EPI_STORE_BF16, fp8, g2, mu, st);
   if (e != hipSuccess || prof.mark(ev_ffn2, st) != hipSuccess) return MOE_EHIP;
   return MOE_OK;
@@ -450,18 +484,22 @@ static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const voi
                          stream, prof);
   if (st != MOE_OK) return st;
   // routed experts as one grouped GEMM over the expert-sorted rows
+  // The shared expert runs on every token ([MND §Expert Parallelism]: its output is
+  // added); with the routed experts' shape it is one more group of the same launches.
   const int R = s->T * s->k;
   FfnIo io{at<void>(ws, L.ex), fp8 ? at<float>(ws, L.ex_scale) : nullptr, offs, w->w13,
            w->w13_scale, w->w2, w->w2_scale, at<void>(ws, L.y)};
-  st = run_ffn(s, s->E, R, s->I, io, at<void>(ws, L.ffn), stream, prof, MOE_EV_PLAN, MOE_EV_FFN1,
-               MOE_EV_FFN2);
-  if (st != MOE_OK) return st;
-  // shared expert on every token ([MND §Expert Parallelism]: its output is added)
-  moe_shape sh = *s;
-  sh.wt = s->act;
   FfnIo sio{x, nullptr, nullptr, w->sh_w13, nullptr, w->sh_w2, nullptr, at<void>(ws, L.sh_out)};
-  st = run_ffn(&sh, 1, s->T, s->I_shared, sio, at<void>(ws, L.sh_ffn), stream);
+  const bool merged = merge_shared(s);
+  st = run_ffn(s, s->E, R, s->I, io, at<void>(ws, L.ffn), stream, prof, MOE_EV_PLAN, MOE_EV_FFN1,
+               MOE_EV_FFN2, merged ? &sio : nullptr, merged ? s->T : 0);
   if (st != MOE_OK) return st;
+  if (!merged) {
+    moe_shape sh = *s;
+    sh.wt = s->act;
+    st = run_ffn(&sh, 1, s->T, s->I_shared, sio, at<void>(ws, L.sh_ffn), stream);
+    if (st != MOE_OK) return st;
+  }
   if (prof.mark(MOE_EV_SHARED, stream) != hipSuccess) return MOE_EHIP;
   // finalize: un-permute, weighted sum, plus the shared expert
   st = moe_finalize_routing(s, at<void>(ws, L.y), at<void>(ws, L.sh_out), tw, eri, out, stream);

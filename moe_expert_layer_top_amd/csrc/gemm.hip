@@ -480,8 +480,16 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   const int k1 = min(p.K, k0 + p.k_chunk);
   const int nsteps = (k1 - k0) / KSTEP;
 
-  const uint8_t* a_base = p.A + static_cast<long long>(un.row0) * p.lda + static_cast<long long>(k0) * EB;
-  const uint8_t* b_base = p.B + static_cast<long long>(un.group) * p.b_group + static_cast<long long>(k0) * EB;
+  // Units of the alternate group (the shared expert folded into the routed launch)
+  // read their own activations and weights and write their own output.
+  const bool alt = !UNIFORM && un.group == p.alt_group;
+  const long long lda = alt ? p.lda2 : p.lda;
+  const uint8_t* a_base = (alt ? p.A2 : p.A) + static_cast<long long>(un.row0) * lda +
+                          static_cast<long long>(k0) * EB;
+  const uint8_t* b_base = (alt ? p.B2 : p.B + static_cast<long long>(un.group) * p.b_group) +
+                          static_cast<long long>(k0) * EB;
+  void* const cptr = alt ? p.C2 : p.C;
+  const long long ldc = alt ? p.ldc2 : p.ldc;
 
   // DMA plan: chunk q = wave + i * NW; lane -> (row q*RPC + lane/CPR, physical 16-byte
   // slot lane%CPR), which holds logical K chunk (lane%CPR) ^ swz(row).  Rows past the
@@ -496,7 +504,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
     if (q < A_LD) {
       const int r = q * RPC + lrow;
       const int rc = r < rows ? r : rows - 1;
-      off = static_cast<uint32_t>(rc * p.lda + ((lphys ^ swz<ROWB>(r)) << 4));
+      off = static_cast<uint32_t>(rc * lda + ((lphys ^ swz<ROWB>(r)) << 4));
     } else if (q < LD_ALL) {
       const int j = (q - A_LD) * RPC + lrow;
       int col, grow;
@@ -631,11 +639,11 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
         for (int r = 0; r < 4; ++r) {
           const int row = rbase + r;
           if (row >= rows) continue;
-          const long long o = static_cast<long long>(un.row0 + row) * p.ldc + col;
+          const long long o = static_cast<long long>(un.row0 + row) * ldc + col;
           if constexpr (EPI == EPI_STORE_BF16) {
-            static_cast<uint16_t*>(p.C)[o] = f32_to_bf16(acc[j][i][r]);
+            static_cast<uint16_t*>(cptr)[o] = f32_to_bf16(acc[j][i][r]);
           } else {
-            static_cast<float*>(p.C)[o + split * p.c_split] = acc[j][i][r];
+            static_cast<float*>(cptr)[o + split * p.c_split] = acc[j][i][r];
           }
         }
       }
@@ -656,7 +664,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
           if (row >= rows) continue;
           const float g = acc[j][i][r];
           const float up = acc[j][i + HT][r];
-          static_cast<uint16_t*>(p.C)[static_cast<long long>(un.row0 + row) * p.ldc + col] =
+          static_cast<uint16_t*>(cptr)[static_cast<long long>(un.row0 + row) * ldc + col] =
               f32_to_bf16(g / (1.0f + __expf(-g)) * up);
         }
       }
@@ -689,24 +697,30 @@ __global__ __launch_bounds__(WM* WN * 64) void dense_gemm_kernel(GemmArgs p) {
 
 // ------------------------------------------------------------------ unit planner
 // One block: units per group = ceil(n / BM) near-equal slices (rows rounded up to
-// 16), prefix-summed over groups, then each group writes its slices.
+// 16), prefix-summed over groups, then each group writes its slices.  Group G, when
+// extra_rows > 0, is an extra group of extra_rows rows starting at row 0 of its own
+// tensor (the shared expert folded into the routed launch); its units come last.
 // Units past `cap` (only reachable if offsets[G] exceeds the rows the caller sized the
 // workspace for) are dropped rather than written out of bounds.
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int G,
-                                                    int rows_if_null, int BM, int cap,
-                                                    Unit* __restrict__ units,
+                                                    int rows_if_null, int extra_rows, int BM,
+                                                    int cap, Unit* __restrict__ units,
                                                     int32_t* __restrict__ n_units) {
   __shared__ int32_t wsum[16];
   __shared__ int32_t carry;
   if (threadIdx.x == 0) carry = 0;
   __syncthreads();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int g0 = 0; g0 < G; g0 += 1024) {
+  const int Gt = G + (extra_rows > 0 ? 1 : 0);
+  for (int g0 = 0; g0 < Gt; g0 += 1024) {
     const int g = g0 + threadIdx.x;
     int n = 0, start = 0;
     if (g < G) {
       start = offsets ? offsets[g] : 0;
       n = offsets ? offsets[g + 1] - start : rows_if_null;
+    } else if (g == G && extra_rows > 0) {
+      start = 0;
+      n = extra_rows;
     }
     const int nu = n > 0 ? (n + BM - 1) / BM : 0;
     int incl = nu;
@@ -747,9 +761,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   if (threadIdx.x == 0) *n_units = min(carry, cap);
 }
 
-hipError_t launch_plan(const int32_t* offsets, int G, int rows_if_null, int block_m, int cap,
-                       Unit* units, int32_t* n_units, hipStream_t st) {
-  plan_kernel<<<1, 1024, 0, st>>>(offsets, G, rows_if_null, block_m, cap, units, n_units);
+hipError_t launch_plan(const int32_t* offsets, int G, int rows_if_null, int extra_rows, int block_m,
+                       int cap, Unit* units, int32_t* n_units, hipStream_t st) {
+  plan_kernel<<<1, 1024, 0, st>>>(offsets, G, rows_if_null, extra_rows, block_m, cap, units,
+                                  n_units);
   return hipGetLastError();
 }
 

@@ -45,6 +45,14 @@ struct GemmArgs {
   int n_tiles;              // output tiles along N
   int splits;               // split-k factor
   int k_chunk;              // elements of K per split (multiple of the stage depth)
+  // Alternate group (bf16 DMA kernels only): units whose group equals alt_group read
+  // A2 (pitch lda2) and the single weight panel B2, and write C2 (pitch ldc2).  -1: none.
+  int alt_group = -1;
+  const uint8_t* A2 = nullptr;
+  long long lda2 = 0;
+  const uint8_t* B2 = nullptr;
+  void* C2 = nullptr;
+  long long ldc2 = 0;
 };
 
 enum GemmCfg : int {
@@ -59,9 +67,10 @@ hipError_t launch_gemm(GemmCfg cfg, Epilogue epi, bool fp8, const GemmArgs& a, i
                        hipStream_t st);
 
 // Builds the unit table of a grouped GEMM on the device.  `offsets` [G+1] or, when
-// NULL, one group of `rows_if_null` rows.
-hipError_t launch_plan(const int32_t* offsets, int G, int rows_if_null, int block_m, int cap,
-                       Unit* units, int32_t* n_units, hipStream_t st);
+// NULL, one group of `rows_if_null` rows; extra_rows > 0 appends group G of that many
+// rows (rows counted from 0 in its own tensor).
+hipError_t launch_plan(const int32_t* offsets, int G, int rows_if_null, int extra_rows, int block_m,
+                       int cap, Unit* units, int32_t* n_units, hipStream_t st);
 
 hipError_t launch_topk(const float* part, int splits, long long split_stride, int T, int E, int k,
                        const float* bias, float* logits_out, int32_t* idx, float* w,

@@ -101,6 +101,10 @@ CONFIGS = {
         name="p2b_prefill_bf16", cid=22, T=613, H=640, E=32, k=8, I=384, I_shared=384,
         act="bf16", wt="bf16",
         description="reduced prefill with H=640 (partial 256-wide N tile) and I=384"),
+    "p2c_prefill_bf16": MoEConfig(
+        name="p2c_prefill_bf16", cid=32, T=400, H=384, E=8, k=2, I=256, I_shared=384,
+        act="bf16", wt="bf16",
+        description="reduced bf16 prefill with I != I_shared (shared expert in its own launches)"),
     "p3_ep_rank_bf16": MoEConfig(
         name="p3_ep_rank_bf16", cid=13, T=1500, H=512, E=8, k=1, I=256, I_shared=256,
         act="bf16", wt="bf16", pretagged=True, e_base=24, E_total=64, T_local=200,
@@ -122,7 +126,7 @@ CONFIGS = {
 FULL_CONFIGS = ["c1_tiny_fp32", "c2_prefill_bf16", "c3_ep_rank_bf16",
                 "c4_decode_bf16", "c5_skewed_fp8"]
 SMALL_CONFIGS = ["c1_tiny_fp32", "p1_small_fp32", "p2_prefill_bf16", "p2b_prefill_bf16",
-                 "p3_ep_rank_bf16", "p4_decode_bf16", "p5_skewed_fp8"]
+                 "p2c_prefill_bf16", "p3_ep_rank_bf16", "p4_decode_bf16", "p5_skewed_fp8"]
 
 
 def get(name: str, **overrides) -> MoEConfig:
