@@ -111,14 +111,26 @@ def shared_is_merged(cfg) -> bool:
     return cfg.act == "bf16" and cfg.wt == "bf16" and cfg.I_shared == cfg.I
 
 
+def gathers_rows(cfg) -> bool:
+    """bf16 layers never write the expanded rows: the first expert GEMM reads each routed
+    row from x through the sort's slot order (32-bit offsets: T*H*2 < 4 GiB)."""
+    return cfg.act == "bf16" and cfg.wt == "bf16" and 2 * cfg.T * cfg.H < (1 << 32)
+
+
 def launch_accounting(cfg, acc: dict) -> dict:
     """Work per timed launch class: with the shared expert merged, the ffn1 / ffn2
-    launches also do the shared expert's two GEMMs and there is no shared stage."""
-    out = {k: v for k, v in acc.items() if k not in ("shared1", "shared2")}
+    launches also do the shared expert's two GEMMs and there is no shared stage; with
+    gathered rows there is no expand stage and ffn1 reads x (T rows) instead of the
+    expanded rows (R rows)."""
+    out = {k: dict(v) for k, v in acc.items() if k not in ("shared1", "shared2")}
+    if gathers_rows(cfg):
+        ab = _bytes(cfg.act)
+        out["expand"] = dict(flops=0, bytes=0, dt=None)
+        out["ffn1"]["bytes"] += cfg.T * cfg.H * ab - cfg.R * cfg.H * ab
     if shared_is_merged(cfg):
         for k, sk in (("ffn1", "shared1"), ("ffn2", "shared2")):
-            out[k] = dict(flops=acc[k]["flops"] + acc[sk]["flops"],
-                          bytes=acc[k]["bytes"] + acc[sk]["bytes"], dt=acc[k]["dt"])
+            out[k] = dict(flops=out[k]["flops"] + acc[sk]["flops"],
+                          bytes=out[k]["bytes"] + acc[sk]["bytes"], dt=out[k]["dt"])
         del out["shared"]
     return out
 
@@ -310,6 +322,7 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None
     roof["mfma_frac"] = dk.get("mfma_frac")
+    # expand is an empty stage when the rows are gathered inside ffn1
     permute_ms = r["stage_ms"]["expand"] + r["stage_ms"]["finalize"]
     permute_bytes = acc["expand"]["bytes"] + acc["finalize"]["bytes"]
     ffn_ms = r["stage_ms"]["ffn1"] + r["stage_ms"]["ffn2"]

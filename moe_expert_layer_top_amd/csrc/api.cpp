@@ -94,6 +94,12 @@ bool merge_shared(const moe_shape* s) {
   return s->act == MOE_BF16 && s->wt == MOE_BF16 && s->I_shared == s->I;
 }
 
+// bf16 layers gather the routed rows from x inside the first expert GEMM (32-bit
+// row offsets into x: T * H * 2 bytes must stay below 4 GiB).
+bool gather_rows(const moe_shape* s) {
+  return s->act == MOE_BF16 && s->wt == MOE_BF16 && 2LL * s->T * s->H < (1LL << 32);
+}
+
 struct FfnLayout {
   size_t units, n_units, h, h_scale, h2, total;
 };
@@ -151,7 +157,7 @@ Layout layer_layout(const moe_shape* s) {
   L.offsets = o;       o += align_up((E + 1) * 4);
   L.eri = o;           o += align_up(R * 4);
   L.sorted_src = o;    o += align_up(R * 4);
-  L.ex = o;            o += align_up(R * H * (fp8 ? 1 : ab));
+  L.ex = o;            if (!gather_rows(s)) o += align_up(R * H * (fp8 ? 1 : ab));
   L.ex_scale = o;      if (fp8) o += align_up(R * (H / 128) * 4);
   L.y = o;             o += align_up(R * H * ab);
   const bool merged = merge_shared(s);
@@ -226,6 +232,10 @@ struct FfnIo {
   const void* w2;
   const float* w2_scale;
   void* y;
+  // bf16 only: row r of `a` is token gather[r] / gather_div of x (a = x), so the
+  // expert-sorted copy of the tokens is never written
+  const int32_t* gather = nullptr;
+  int gather_div = 1;
 };
 
 // `alt` (bf16 only): the shared expert as group G of alt_rows rows in the same
@@ -283,6 +293,8 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
   g1.n_tiles = I / 128;
   g1.splits = 1;
   g1.k_chunk = H;
+  g1.gather = io.gather;
+  g1.gather_div = io.gather_div;
   if (alt_rows > 0) {
     g1.alt_group = G;
     g1.A2 = static_cast<const uint8_t*>(alt->a);
@@ -295,6 +307,8 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
                                   mu, st);
   if (e != hipSuccess || prof.mark(ev_ffn1, st) != hipSuccess) return MOE_EHIP;
   GemmArgs g2 = g1;
+  g2.gather = nullptr;
+  g2.gather_div = 1;
   g2.A = at<uint8_t>(ws, L.h);
   g2.lda = static_cast<long long>(I) * eb;
   g2.a_scale = fp8 ? at<float>(ws, L.h_scale) : nullptr;
@@ -475,13 +489,16 @@ static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const voi
   if (prof.mark(MOE_EV_START, stream) != hipSuccess) return MOE_EHIP;
   st = run_gate_topk(s, x, w->w_gate, w->bias, lg, idx, tw, at<float>(ws, L.part), stream, prof);
   if (st != MOE_OK) return st;
-  // first routing: expand and sort by expert  ([R1P §MoE deployment strategy optimization])
+  // first routing: expand and sort by expert  ([R1P §MoE deployment strategy optimization]).
+  // bf16 layers never materialize the expanded rows: the first expert GEMM reads each
+  // row from x through the sort's slot order.
   int32_t* eri = at<int32_t>(ws, L.eri);
   int32_t* offs = at<int32_t>(ws, L.offsets);
-  st = init_routing_impl(s, x, idx, 0, at<void>(ws, L.ex),
-                         fp8 ? at<float>(ws, L.ex_scale) : nullptr, eri,
-                         at<int32_t>(ws, L.sorted_src), at<int32_t>(ws, L.tpe), offs, ws, ws_bytes,
-                         stream, prof);
+  int32_t* ssrc = at<int32_t>(ws, L.sorted_src);
+  const bool gathered = gather_rows(s);
+  st = init_routing_impl(s, x, idx, 0, gathered ? nullptr : at<void>(ws, L.ex),
+                         fp8 ? at<float>(ws, L.ex_scale) : nullptr, eri, ssrc,
+                         at<int32_t>(ws, L.tpe), offs, ws, ws_bytes, stream, prof);
   if (st != MOE_OK) return st;
   // routed experts as one grouped GEMM over the expert-sorted rows
   // The shared expert runs on every token ([MND §Expert Parallelism]: its output is
@@ -489,6 +506,11 @@ static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const voi
   const int R = s->T * s->k;
   FfnIo io{at<void>(ws, L.ex), fp8 ? at<float>(ws, L.ex_scale) : nullptr, offs, w->w13,
            w->w13_scale, w->w2, w->w2_scale, at<void>(ws, L.y)};
+  if (gathered) {
+    io.a = x;
+    io.gather = ssrc;
+    io.gather_div = s->k;
+  }
   FfnIo sio{x, nullptr, nullptr, w->sh_w13, nullptr, w->sh_w2, nullptr, at<void>(ws, L.sh_out)};
   const bool merged = merge_shared(s);
   st = run_ffn(s, s->E, R, s->I, io, at<void>(ws, L.ffn), stream, prof, MOE_EV_PLAN, MOE_EV_FFN1,

@@ -484,7 +484,9 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   // read their own activations and weights and write their own output.
   const bool alt = !UNIFORM && un.group == p.alt_group;
   const long long lda = alt ? p.lda2 : p.lda;
-  const uint8_t* a_base = (alt ? p.A2 : p.A) + static_cast<long long>(un.row0) * lda +
+  const int32_t* gather = (!UNIFORM && !alt) ? p.gather : nullptr;
+  const uint8_t* a_base = (alt ? p.A2 : p.A) +
+                          (gather ? 0LL : static_cast<long long>(un.row0) * lda) +
                           static_cast<long long>(k0) * EB;
   const uint8_t* b_base = (alt ? p.B2 : p.B + static_cast<long long>(un.group) * p.b_group) +
                           static_cast<long long>(k0) * EB;
@@ -504,7 +506,8 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
     if (q < A_LD) {
       const int r = q * RPC + lrow;
       const int rc = r < rows ? r : rows - 1;
-      off = static_cast<uint32_t>(rc * lda + ((lphys ^ swz<ROWB>(r)) << 4));
+      const long long src = gather ? gather[un.row0 + rc] / p.gather_div : rc;
+      off = static_cast<uint32_t>(src * lda + ((lphys ^ swz<ROWB>(r)) << 4));
     } else if (q < LD_ALL) {
       const int j = (q - A_LD) * RPC + lrow;
       int col, grow;

@@ -47,6 +47,11 @@ struct GemmArgs {
   int k_chunk;              // elements of K per split (multiple of the stage depth)
   // Alternate group (bf16 DMA kernels only): units whose group equals alt_group read
   // A2 (pitch lda2) and the single weight panel B2, and write C2 (pitch ldc2).  -1: none.
+  // Gathered activations (bf16 DMA kernels only): when set, row r of a unit of the
+  // primary groups is row gather[row0 + r] / gather_div of A (x indexed by token,
+  // through the slot order of the expert sort) instead of row row0 + r.
+  const int32_t* gather = nullptr;
+  int gather_div = 1;
   int alt_group = -1;
   const uint8_t* A2 = nullptr;
   long long lda2 = 0;

@@ -49,8 +49,12 @@ def test_status_strings(L):
 def test_workspace_query(L):
     c2 = M.shape(8192, 7168, 256, 8, 2048, 2048, "bf16", "bf16")
     n = M.moe_workspace_bytes(c2)
-    # at least the expanded rows and the routed outputs (2 x R x H bf16)
-    assert n >= 2 * 65536 * 7168 * 2
+    # the routed outputs (R x H bf16); a bf16 layer gathers its routed rows from x and
+    # keeps no expanded copy of them
+    assert 65536 * 7168 * 2 <= n < 2 * 65536 * 7168 * 2
+    # an fp8 layer keeps the quantized expanded rows (R x H bytes) as well
+    c5 = M.shape(8192, 7168, 256, 8, 2048, 2048, "bf16", "fp8")
+    assert M.moe_workspace_bytes(c5) >= 65536 * 7168 * (2 + 1)
     small = M.shape(100, 7168, 256, 8, 2048, 2048, "bf16", "bf16")
     assert 0 < M.moe_workspace_bytes(small) < n
     assert M.moe_workspace_bytes(M.shape(8, 128, 4, 5, 128, 128)) == 0          # k > E
