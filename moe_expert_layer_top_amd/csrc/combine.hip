@@ -11,79 +11,114 @@
 namespace moe {
 
 // out[t] = skip[t] + sum_j w[t, j] * y[eri[t*k + j]], fp32 accumulation, one rounding.
-// One block per token, 16-byte vectors; the k source rows are independent HBM streams.
-template <bool BF16>
+// One thread per (token, 16-byte vector of the row): the k routed rows and the skip row
+// are loaded before the first FMA (all k + 1 loads in flight per thread), then
+// accumulated in slot order j = 0 .. k-1 starting from the skip value.  KC > 0 fixes
+// k at compile time (fully unrolled); KC = 0 handles any k in chunks of 8.
+template <bool BF16, int KC>
 __global__ __launch_bounds__(256) void finalize_kernel(const uint8_t* __restrict__ y,
                                                        const uint8_t* __restrict__ skip,
                                                        const float* __restrict__ w,
                                                        const int32_t* __restrict__ eri,
-                                                       uint8_t* __restrict__ out, int H, int k) {
+                                                       uint8_t* __restrict__ out, int T, int H,
+                                                       int k_rt) {
   constexpr int EB = BF16 ? 2 : 4;
   constexpr int PER = 16 / EB;  // elements per 16-byte vector
-  const int t = blockIdx.x;
+  const int k = KC > 0 ? KC : k_rt;
   const long long row_bytes = static_cast<long long>(H) * EB;
   const int nvec = static_cast<int>(row_bytes / 16);
-  for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
-    float acc[PER];
-    if (skip) {
-      const uint4 s = reinterpret_cast<const uint4*>(skip + t * row_bytes)[v];
-      const uint32_t sw[4] = {s.x, s.y, s.z, s.w};
-      if constexpr (BF16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] = __uint_as_float(sw[i] << 16);
-          acc[2 * i + 1] = __uint_as_float(sw[i] & 0xffff0000u);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = __uint_as_float(sw[i]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-    }
-    for (int j = 0; j < k; ++j) {
-      const int32_t r = eri[static_cast<long long>(t) * k + j];
-      if (r < 0) continue;
-      const float wj = w ? w[static_cast<long long>(t) * k + j] : 1.0f;
-      const uint4 yv = reinterpret_cast<const uint4*>(y + r * row_bytes)[v];
-      const uint32_t yw[4] = {yv.x, yv.y, yv.z, yv.w};
-      if constexpr (BF16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] = fmaf(wj, __uint_as_float(yw[i] << 16), acc[2 * i]);
-          acc[2 * i + 1] = fmaf(wj, __uint_as_float(yw[i] & 0xffff0000u), acc[2 * i + 1]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = fmaf(wj, __uint_as_float(yw[i]), acc[i]);
-      }
-    }
-    uint4 o;
+  const long long id = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (id >= static_cast<long long>(T) * nvec) return;
+  const int t = static_cast<int>(id / nvec);
+  const int v = static_cast<int>(id % nvec);
+
+  float acc[PER];
+  auto unpack_add = [&](uint4 q, float wj, bool first_skip) __attribute__((always_inline)) {
+    const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
     if constexpr (BF16) {
-      o = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = __uint_as_float(qw[i] << 16), hi = __uint_as_float(qw[i] & 0xffff0000u);
+        if (first_skip) { acc[2 * i] = lo; acc[2 * i + 1] = hi; }
+        else { acc[2 * i] = fmaf(wj, lo, acc[2 * i]); acc[2 * i + 1] = fmaf(wj, hi, acc[2 * i + 1]); }
+      }
     } else {
-      o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
-                     __float_as_uint(acc[3]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float f = __uint_as_float(qw[i]);
+        acc[i] = first_skip ? f : fmaf(wj, f, acc[i]);
+      }
     }
-    reinterpret_cast<uint4*>(out + t * row_bytes)[v] = o;
+  };
+
+  uint4 sv = make_uint4(0u, 0u, 0u, 0u);
+  if (skip) sv = reinterpret_cast<const uint4*>(skip + t * row_bytes)[v];
+  const int32_t* er = eri + static_cast<long long>(t) * k;
+  const float* wr = w ? w + static_cast<long long>(t) * k : nullptr;
+  constexpr int CH = KC > 0 ? KC : 8;
+  bool first = true;
+  for (int j0 = 0; j0 < k; j0 += CH) {
+    uint4 yv[CH];
+    float wv[CH];
+    bool ok[CH];
+#pragma unroll
+    for (int jj = 0; jj < CH; ++jj) {
+      const int j = j0 + jj;
+      const int32_t r = j < k ? er[j] : -1;
+      ok[jj] = r >= 0;
+      wv[jj] = (wr && j < k) ? wr[j] : 1.0f;
+      if (ok[jj]) {
+        const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(y + r * row_bytes) + v);
+        yv[jj] = make_uint4(q.x, q.y, q.z, q.w);
+      } else {
+        yv[jj] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    if (first) {
+      unpack_add(sv, 1.0f, true);
+      first = false;
+    }
+#pragma unroll
+    for (int jj = 0; jj < CH; ++jj)
+      if (ok[jj]) unpack_add(yv[jj], wv[jj], false);
   }
+  if (first) unpack_add(sv, 1.0f, true);
+  uint4 o;
+  if constexpr (BF16) {
+    o = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                   pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+  } else {
+    o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                   __float_as_uint(acc[3]));
+  }
+  __builtin_nontemporal_store(u32x4{o.x, o.y, o.z, o.w}, reinterpret_cast<u32x4*>(out + t * row_bytes) + v);
+}
+
+template <bool BF16>
+hipError_t finalize_go(const void* y, const void* skip, const float* w, const int32_t* eri,
+                       void* out, int T, int H, int k, hipStream_t st) {
+  const long long n = static_cast<long long>(T) * (static_cast<long long>(H) * (BF16 ? 2 : 4) / 16);
+  const unsigned grid = static_cast<unsigned>((n + 255) / 256);
+  const auto* yb = static_cast<const uint8_t*>(y);
+  const auto* sb = static_cast<const uint8_t*>(skip);
+  auto* ob = static_cast<uint8_t*>(out);
+  switch (k) {
+    case 1: finalize_kernel<BF16, 1><<<grid, 256, 0, st>>>(yb, sb, w, eri, ob, T, H, k); break;
+    case 2: finalize_kernel<BF16, 2><<<grid, 256, 0, st>>>(yb, sb, w, eri, ob, T, H, k); break;
+    case 4: finalize_kernel<BF16, 4><<<grid, 256, 0, st>>>(yb, sb, w, eri, ob, T, H, k); break;
+    case 6: finalize_kernel<BF16, 6><<<grid, 256, 0, st>>>(yb, sb, w, eri, ob, T, H, k); break;
+    case 8: finalize_kernel<BF16, 8><<<grid, 256, 0, st>>>(yb, sb, w, eri, ob, T, H, k); break;
+    default: finalize_kernel<BF16, 0><<<grid, 256, 0, st>>>(yb, sb, w, eri, ob, T, H, k); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_finalize(const void* y, const void* skip, const float* w, const int32_t* eri,
                            void* out, int T, int H, int k, int act_bytes, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  if (act_bytes == 2) {
-    finalize_kernel<true><<<T, 256, 0, st>>>(static_cast<const uint8_t*>(y),
-                                             static_cast<const uint8_t*>(skip), w, eri,
-                                             static_cast<uint8_t*>(out), H, k);
-  } else {
-    finalize_kernel<false><<<T, 256, 0, st>>>(static_cast<const uint8_t*>(y),
-                                              static_cast<const uint8_t*>(skip), w, eri,
-                                              static_cast<uint8_t*>(out), H, k);
-  }
-  return hipGetLastError();
+  if (static_cast<long long>(T) * H * act_bytes / 16 >= (1LL << 31) * 256LL) return hipErrorInvalidValue;
+  return act_bytes == 2 ? finalize_go<true>(y, skip, w, eri, out, T, H, k, st)
+                        : finalize_go<false>(y, skip, w, eri, out, T, H, k, st);
 }
 
 // ------------------------------------------------------------------ fp32 path
