@@ -135,6 +135,33 @@ def launch_accounting(cfg, acc: dict) -> dict:
     return out
 
 
+def measured_traffic(workload: str, stage: str):
+    """HBM bytes per launch of `stage` measured by the rocprofv3 FETCH_SIZE / WRITE_SIZE
+    passes recorded in profiles/<stage>_<workload>_hbm_traffic.txt, scaled by the copy
+    calibration; None when there is no record or when the kernel sources listed in it
+    have changed since (the sha256 no longer matches), so a stale count is never shown."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{stage}_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if line.startswith("#") or ":" not in line:
+            continue
+        k, v = line.split(":", 1)
+        rec[k.strip()] = v.strip()
+    try:
+        h = hashlib.sha256()
+        for f in rec["sources"].split():
+            with open(os.path.join(ROOT, f), "rb") as fh:
+                h.update(fh.read())
+        if h.hexdigest() != rec["source_sha256"]:
+            return None
+        return int(rec["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
 def roofline_entry(acc_k: dict, ms: float) -> dict:
     t = ms / 1e3
     gbs = acc_k["bytes"] / t / 1e9 if t > 0 else 0.0
@@ -320,7 +347,9 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(cfg.name, dom)
+    roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    roof["algorithmic_bytes"] = acc[dom]["bytes"]
     roof["mfma_frac"] = dk.get("mfma_frac")
     # expand is an empty stage when the rows are gathered inside ffn1
     permute_ms = r["stage_ms"]["expand"] + r["stage_ms"]["finalize"]

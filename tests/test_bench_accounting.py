@@ -55,3 +55,39 @@ def test_activated_experts_per_gpu_example():
     on average 2*8/8 = 2 activated experts per GPU."""
     ex = GOLD["activated_experts"]
     assert ex["tokens"] * ex["topk"] / ex["gpus"] == ex["per_gpu"]
+
+
+def test_launch_accounting_merged_and_gathered():
+    """The c2 launches fold the shared expert into ffn1/ffn2 and gather the routed rows
+    from x: ffn1 then reads x (T rows) instead of R expanded rows, plus the shared GEMM1."""
+    cfg = configs.get("c2_prefill_bf16")
+    tpe = np.full(cfg.E, cfg.T * cfg.k // cfg.E)
+    acc = bench.account(cfg, tpe)
+    la = bench.launch_accounting(cfg, acc)
+    assert bench.shared_is_merged(cfg) and bench.gathers_rows(cfg)
+    assert "shared" not in la and la["expand"]["bytes"] == 0
+    T, H, I = cfg.T, cfg.H, cfg.I
+    assert la["ffn1"]["flops"] == acc["ffn1"]["flops"] + 2 * T * H * 2 * I
+    w_routed = cfg.E * 2 * I * H * 2
+    shared1 = 2 * I * H * 2 + T * H * 2 + T * I * 2
+    assert la["ffn1"]["bytes"] == w_routed + T * H * 2 + cfg.R * I * 2 + shared1
+    assert la["ffn2"]["flops"] == acc["ffn2"]["flops"] + 2 * T * I * H
+    # fp8 layers keep the expanded rows and the separate shared stage
+    c5 = configs.get("c5_skewed_fp8")
+    l5 = bench.launch_accounting(c5, bench.account(c5, np.full(c5.E, c5.T * c5.k // c5.E)))
+    assert "shared" in l5 and l5["expand"]["bytes"] > 0
+
+
+def test_measured_traffic_requires_matching_sources(tmp_path, monkeypatch):
+    import hashlib
+    src = tmp_path / "k.hip"
+    src.write_text("kernel v1\n")
+    (tmp_path / "profiles").mkdir()
+    sha = hashlib.sha256(src.read_bytes()).hexdigest()
+    (tmp_path / "profiles" / "ffn1_wl_hbm_traffic.txt").write_text(
+        f"# record\nsources: k.hip\nsource_sha256: {sha}\ntraffic_bytes_per_launch: 1234\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_traffic("wl", "ffn1") == 1234
+    assert bench.measured_traffic("other", "ffn1") is None
+    src.write_text("kernel v2\n")   # the kernel changed since the counters were taken
+    assert bench.measured_traffic("wl", "ffn1") is None
