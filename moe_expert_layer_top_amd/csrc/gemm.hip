@@ -700,11 +700,14 @@ __global__ __launch_bounds__(WM* WN * 64) void dense_gemm_kernel(GemmArgs p) {
 
 // ------------------------------------------------------------------ unit planner
 // One block: units per group = ceil(n / BM) near-equal slices (rows rounded up to
-// 16), prefix-summed over groups, then each group writes its slices.  Group G, when
-// extra_rows > 0, is an extra group of extra_rows rows starting at row 0 of its own
-// tensor (the shared expert folded into the routed launch); its units come last.
-// Units past `cap` (only reachable if offsets[G] exceeds the rows the caller sized the
-// workspace for) are dropped rather than written out of bounds.
+// 16), prefix-summed over groups, then each group writes its slices.  When
+// extra_rows > 0 there is one more group, index G, of extra_rows rows starting at row
+// 0 of its own tensor (the shared expert folded into the routed launch).  Its n_x
+// slices are spread evenly through the table -- slice i goes right before the units of
+// group floor(i * G / n_x) -- so every stretch of consecutive units (the workgroups
+// that run together) mixes the compute-heavy shared slices with weight-streaming
+// routed ones.  Units past `cap` (only reachable if offsets[G] exceeds the rows the
+// caller sized the workspace for) are dropped rather than written out of bounds.
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int G,
                                                     int rows_if_null, int extra_rows, int BM,
                                                     int cap, Unit* __restrict__ units,
@@ -714,16 +717,20 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   if (threadIdx.x == 0) carry = 0;
   __syncthreads();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int Gt = G + (extra_rows > 0 ? 1 : 0);
-  for (int g0 = 0; g0 < Gt; g0 += 1024) {
+  const int nx = extra_rows > 0 ? (extra_rows + BM - 1) / BM : 0;
+  const int per_x = nx > 0 ? (((extra_rows + nx - 1) / nx + 15) & ~15) : 0;
+  // extra slices placed before the units of groups 0..g: min(nx, ceil((g + 1) * nx / G))
+  auto extra_upto = [&](int g) -> int {
+    if (nx == 0 || g < 0) return 0;
+    const long long c = (static_cast<long long>(g + 1) * nx + G - 1) / G;
+    return static_cast<int>(c < nx ? c : nx);
+  };
+  for (int g0 = 0; g0 < G; g0 += 1024) {
     const int g = g0 + threadIdx.x;
     int n = 0, start = 0;
     if (g < G) {
       start = offsets ? offsets[g] : 0;
       n = offsets ? offsets[g + 1] - start : rows_if_null;
-    } else if (g == G && extra_rows > 0) {
-      start = 0;
-      n = extra_rows;
     }
     const int nu = n > 0 ? (n + BM - 1) / BM : 0;
     int incl = nu;
@@ -745,23 +752,35 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
       if (lane < 16) wsum[lane] = inc - v;
     }
     __syncthreads();
-    const int base = carry + wsum[w] + incl - nu;
-    if (nu > 0) {
-      const int per = ((n + nu - 1) / nu + 15) & ~15;
-      for (int i = 0; i < nu; ++i) {
+    const int base = carry + wsum[w] + incl - nu;  // routed units of groups < g
+    if (g < G) {
+      // the extra slices that go right before this group, then the group's own units
+      const int x0 = extra_upto(g - 1), x1 = extra_upto(g);
+      for (int i = x0; i < x1; ++i) {
         Unit un;
-        un.group = g;
-        un.row0 = start + i * per;
-        un.rows = min(per, n - i * per);
+        un.group = G;
+        un.row0 = i * per_x;
+        un.rows = min(per_x, extra_rows - i * per_x);
         un.pad = 0;
         if (base + i < cap) units[base + i] = un;
+      }
+      if (nu > 0) {
+        const int per = ((n + nu - 1) / nu + 15) & ~15;
+        for (int i = 0; i < nu; ++i) {
+          Unit un;
+          un.group = g;
+          un.row0 = start + i * per;
+          un.rows = min(per, n - i * per);
+          un.pad = 0;
+          if (base + x1 + i < cap) units[base + x1 + i] = un;
+        }
       }
     }
     __syncthreads();
     if (threadIdx.x == 1023) carry = base + nu;
     __syncthreads();
   }
-  if (threadIdx.x == 0) *n_units = min(carry, cap);
+  if (threadIdx.x == 0) *n_units = min(carry + nx, cap);
 }
 
 hipError_t launch_plan(const int32_t* offsets, int G, int rows_if_null, int extra_rows, int block_m,
