@@ -493,50 +493,49 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   void* const cptr = alt ? p.C2 : p.C;
   const long long ldc = alt ? p.ldc2 : p.ldc;
 
-  // DMA plan: chunk q = wave + i * NW; lane -> (row q*RPC + lane/CPR, physical 16-byte
+  // DMA plan.  Every wavefront issues A_PER activation chunks (q = wave + i * NW) and
+  // B_PER weight chunks (q = wave + i * NW) per stage; both counts are compile-time, so
+  // the issue sequence has no branches.  Lane -> (row q*RPC + lane/CPR, physical 16-byte
   // slot lane%CPR), which holds logical K chunk (lane%CPR) ^ swz(row).  Rows past the
   // unit and columns past N re-load a valid row; their results are never stored.
+  static_assert(A_LD % NW == 0 && B_LD % NW == 0, "chunks split evenly over the wavefronts");
+  constexpr int A_PER = A_LD / NW, B_PER = B_LD / NW;
+  static_assert(A_PER + B_PER == LMAX && LREM == 0, "uniform per-wave DMA count");
   uint32_t goff[LMAX];
   const int lrow = lane / CPR;
   const int lphys = lane % CPR;
 #pragma unroll
-  for (int i = 0; i < LMAX; ++i) {
+  for (int i = 0; i < A_PER; ++i) {
     const int q = wave + i * NW;
-    uint32_t off = 0;
-    if (q < A_LD) {
-      const int r = q * RPC + lrow;
-      const int rc = r < rows ? r : rows - 1;
-      const long long src = gather ? gather[un.row0 + rc] / p.gather_div : rc;
-      off = static_cast<uint32_t>(src * lda + ((lphys ^ swz<ROWB>(r)) << 4));
-    } else if (q < LD_ALL) {
-      const int j = (q - A_LD) * RPC + lrow;
-      int col, grow;
-      if constexpr (SWIGLU) {
-        constexpr int WCOLS = TN * 16, HALF = TN * 8;
-        const int wn2 = j / WCOLS, jj = j % WCOLS;
-        col = nt * (BN / 2) + wn2 * HALF + (jj % HALF);
-        grow = (jj < HALF ? 0 : p.up_off) + col;
-      } else {
-        col = nt * BN + j;
-        grow = col;
-      }
-      if (col >= p.N) grow -= col - (p.N - 1);
-      off = static_cast<uint32_t>(static_cast<long long>(grow) * p.ldb + ((lphys ^ swz<ROWB>(j)) << 4));
+    const int r = q * RPC + lrow;
+    const int rc = r < rows ? r : rows - 1;
+    const long long src = gather ? gather[un.row0 + rc] / p.gather_div : rc;
+    goff[i] = static_cast<uint32_t>(src * lda + ((lphys ^ swz<ROWB>(r)) << 4));
+  }
+#pragma unroll
+  for (int i = 0; i < B_PER; ++i) {
+    const int j = (wave + i * NW) * RPC + lrow;
+    int col, grow;
+    if constexpr (SWIGLU) {
+      constexpr int WCOLS = TN * 16, HALF = TN * 8;
+      const int wn2 = j / WCOLS, jj = j % WCOLS;
+      col = nt * (BN / 2) + wn2 * HALF + (jj % HALF);
+      grow = (jj < HALF ? 0 : p.up_off) + col;
+    } else {
+      col = nt * BN + j;
+      grow = col;
     }
-    goff[i] = off;
+    if (col >= p.N) grow -= col - (p.N - 1);
+    goff[A_PER + i] = static_cast<uint32_t>(static_cast<long long>(grow) * p.ldb + ((lphys ^ swz<ROWB>(j)) << 4));
   }
 
   auto issue = [&](int step, uint8_t* buf) __attribute__((always_inline)) {
     const long long kb = static_cast<long long>(step) * ROWB;
 #pragma unroll
-    for (int i = 0; i < LMAX; ++i) {
-      const int q = wave + i * NW;
-      if (q < A_LD) {
-        dma16(a_base + goff[i] + kb, buf + q * 1024);
-      } else if (q < LD_ALL) {
-        dma16(b_base + goff[i] + kb, buf + BM * ROWB + (q - A_LD) * 1024);
-      }
-    }
+    for (int i = 0; i < A_PER; ++i) dma16(a_base + goff[i] + kb, buf + (wave + i * NW) * 1024);
+#pragma unroll
+    for (int i = 0; i < B_PER; ++i)
+      dma16(b_base + goff[A_PER + i] + kb, buf + BM * ROWB + (wave + i * NW) * 1024);
   };
 
   f32x4 acc[TM][TN];
