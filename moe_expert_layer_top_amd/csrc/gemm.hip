@@ -573,7 +573,10 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
       for (int j = 0; j < J; ++j)
 #pragma unroll
         for (int i = 0; i < TN; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[j], bfr[i], acc[j][i], 0, 0, 0);
+          // weights as the MFMA's A operand and tokens as its B operand: the result tile is
+          // [output column][token], so each lane ends up with 4 consecutive output
+          // columns of one token row (stored as one 8- or 16-byte vector)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[i], afr[j], acc[j][i], 0, 0, 0);
     }
   };
 
@@ -626,26 +629,38 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
     default: mainloop(std::integral_constant<int, 0>{}); break;
   }
 
-  // ---- epilogue (C fragment: lane holds column lane & 15, rows 4 * (lane >> 4) + r)
-  const int ccol = lane & 15;
+  // ---- epilogue.  Transposed C fragment of a 16x16 tile: lane holds token row
+  // lane & 15 and output columns 4 * (lane >> 4) + r, r = 0..3.
+  const int crow = lane & 15;
+  const int ccol4 = 4 * kgrp;
   if constexpr (EPI == EPI_STORE_BF16 || EPI == EPI_STORE_F32) {
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       if (j >= jcount) continue;
-      const int rbase = 16 * (j * WM + wm) + 4 * kgrp;
+      const int row = 16 * (j * WM + wm) + crow;
+      if (row >= rows) continue;
 #pragma unroll
       for (int i = 0; i < TN; ++i) {
-        const int col = nt * BN + wn * TN * 16 + 16 * i + ccol;
-        if (col >= p.N) continue;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = rbase + r;
-          if (row >= rows) continue;
-          const long long o = static_cast<long long>(un.row0 + row) * ldc + col;
+        const int col = nt * BN + wn * TN * 16 + 16 * i + ccol4;
+        const long long o = static_cast<long long>(un.row0 + row) * ldc + col;
+        // bf16 rows are 8-byte aligned (ldc is a multiple of 128); fp32 partials only
+        // take the 16-byte store when the address allows it
+        const bool vec = col + 3 < p.N &&
+                         (EPI == EPI_STORE_BF16 ||
+                          (reinterpret_cast<uintptr_t>(static_cast<float*>(cptr) + o + split * p.c_split) & 15) == 0);
+        if (vec) {
           if constexpr (EPI == EPI_STORE_BF16) {
-            static_cast<uint16_t*>(cptr)[o] = f32_to_bf16(acc[j][i][r]);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(cptr) + o) =
+                make_uint2(pack_bf16x2(acc[j][i][0], acc[j][i][1]), pack_bf16x2(acc[j][i][2], acc[j][i][3]));
           } else {
-            static_cast<float*>(cptr)[o + split * p.c_split] = acc[j][i][r];
+            *reinterpret_cast<f32x4*>(static_cast<float*>(cptr) + o + split * p.c_split) = acc[j][i];
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (col + r >= p.N) continue;
+            if constexpr (EPI == EPI_STORE_BF16) static_cast<uint16_t*>(cptr)[o + r] = f32_to_bf16(acc[j][i][r]);
+            else static_cast<float*>(cptr)[o + r + split * p.c_split] = acc[j][i][r];
           }
         }
       }
@@ -655,19 +670,25 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       if (j >= jcount) continue;
-      const int rbase = 16 * (j * WM + wm) + 4 * kgrp;
+      const int row = 16 * (j * WM + wm) + crow;
+      if (row >= rows) continue;
 #pragma unroll
       for (int i = 0; i < HT; ++i) {
-        const int col = nt * (BN / 2) + wn * (TN * 8) + 16 * i + ccol;
-        if (col >= p.N) continue;
+        const int col = nt * (BN / 2) + wn * (TN * 8) + 16 * i + ccol4;
+        float hv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = rbase + r;
-          if (row >= rows) continue;
           const float g = acc[j][i][r];
           const float up = acc[j][i + HT][r];
-          static_cast<uint16_t*>(cptr)[static_cast<long long>(un.row0 + row) * ldc + col] =
-              f32_to_bf16(g / (1.0f + __expf(-g)) * up);
+          hv[r] = g / (1.0f + __expf(-g)) * up;
+        }
+        uint16_t* hp = static_cast<uint16_t*>(cptr) + static_cast<long long>(un.row0 + row) * ldc + col;
+        if (col + 3 < p.N) {
+          *reinterpret_cast<uint2*>(hp) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (col + r < p.N) hp[r] = f32_to_bf16(hv[r]);
         }
       }
     }
