@@ -415,19 +415,55 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* lds_chunk) {
                : "memory", "m0");
 }
 
+// Same as dma16 with the address split into a wave-uniform 64-bit base (scalar
+// registers) and a 32-bit per-lane byte offset: the per-lane address needs one VGPR
+// instead of two and no 64-bit add.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint8_t* lds_chunk) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+          (__attribute__((address_space(3))) uint8_t*)lds_chunk)));
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(m0)
+               : "memory", "m0");
+}
+
+// 4 bytes per lane (global_load_lds_dword) into lds_chunk + 4 * lane; base/offset form.
+__device__ __forceinline__ void dma4s(const void* base, uint32_t off, uint8_t* lds_chunk) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+          (__attribute__((address_space(3))) uint8_t*)lds_chunk)));
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(m0)
+               : "memory", "m0");
+}
+
+// 4 bytes per lane from `g` into lds_chunk + 4 * lane (global_load_lds_dword); same
+// ordering rules as dma16.
+__device__ __forceinline__ void dma4(const void* g, uint8_t* lds_chunk) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+          (__attribute__((address_space(3))) uint8_t*)lds_chunk)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(g), "s"(m0)
+               : "memory", "m0");
+}
+
 template <int ROWB>
 __device__ __forceinline__ int swz(int row) {
   if constexpr (ROWB == 128) return row & 7;
   else return (row >> 1) & 3;
 }
 
-template <int WM, int WN, int TM, int TN, int EPI, bool UNIFORM, int ROWB, int NST>
+template <int WM, int WN, int TM, int TN, int EPI, bool UNIFORM, int ROWB, int NST, bool FP8>
 __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   constexpr int NT = WM * WN * 64;
   constexpr int NW = NT / 64;
   constexpr int BM = WM * TM * 16;
   constexpr int BN = WN * TN * 16;
-  constexpr int EB = 2;
+  constexpr int EB = FP8 ? 1 : 2;       // operand element bytes
   constexpr int KSTEP = ROWB / EB;       // elements per stage
   constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
   constexpr int RPC = 64 / CPR;          // rows per 1 KB DMA (one wave instruction)
@@ -436,7 +472,13 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   constexpr int LMAX = (LD_ALL + NW - 1) / NW;   // DMA instructions per wave per stage
   constexpr int LREM = LD_ALL % NW;              // waves < LREM issue LMAX, others LMAX-1
   constexpr int STAGE = (BM + BN) * ROWB;
-  constexpr bool SWIGLU = (EPI == EPI_SWIGLU_BF16);
+  constexpr bool SWIGLU = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_FP8);
+  // fp8: one stage = one 128-wide K block of e4m3 codes; its 1x128 activation scales and
+  // the two 128x128 weight-block scales of the tile come into LDS with the stage.
+  static_assert(!FP8 || (NST == 2 && ROWB == kQBlock && BM % 64 == 0 && BM / 64 < WM * WN &&
+                         EPI != EPI_STORE_F32 && !UNIFORM),
+                "fp8 tiles: 2-deep ring of one scale block per stage");
+  static_assert(FP8 == (EPI == EPI_SWIGLU_FP8) || EPI == EPI_STORE_BF16, "epilogue matches operands");
   static_assert(BM % RPC == 0 && BN % RPC == 0, "tiles are whole DMA chunks");
   static_assert(NST >= 2 && NST <= 4, "ring depth");
   static_assert(!SWIGLU || TN % 2 == 0, "swiglu needs gate/up tile pairs");
@@ -445,6 +487,12 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st2[NST > 2 ? STAGE : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t st3[NST > 3 ? STAGE : 16];
+  __shared__ __attribute__((aligned(16))) float sa_st[2][FP8 ? BM : 1];   // activation scales
+  __shared__ __attribute__((aligned(16))) float sb_st[2][FP8 ? 64 : 1];   // weight-block scales
+  // fp8: the per-lane DMA offsets live in LDS and are re-read (volatile) at each issue;
+  // in registers they would be spilled, and a scratch reload waits on vmcnt(0), which
+  // would drain the DMAs in flight.
+  __shared__ uint32_t off_tab[FP8 ? (LMAX + 1) : 1][FP8 ? NT : 1];
 
   const int bid = blockIdx.x;
   const int xcd = bid % kXcds;
@@ -529,13 +577,55 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
     goff[A_PER + i] = static_cast<uint32_t>(static_cast<long long>(grow) * p.ldb + ((lphys ^ swz<ROWB>(j)) << 4));
   }
 
-  auto issue = [&](int step, uint8_t* buf) __attribute__((always_inline)) {
+  // fp8 scale sources of this lane: wavefronts 0 .. BM/64-1 fetch the activation
+  // scales of rows 64 * wave + lane, wavefront BM/64 the two weight-block scales.
+  // (base: wave-uniform pointer at the first K block of the split; off: lane byte offset)
+  const float* sc_base = nullptr;
+  uint32_t sc_off = 0;
+  if constexpr (FP8) {
+    const int kb0 = k0 / kQBlock;
+    if (wave < BM / 64) {
+      const int r = 64 * wave + lane;
+      const int rc = r < rows ? r : rows - 1;
+      sc_base = p.a_scale + static_cast<long long>(un.row0) * p.a_scale_ld + kb0;
+      sc_off = static_cast<uint32_t>(static_cast<long long>(rc) * p.a_scale_ld * 4);
+    } else {
+      int blk;
+      if constexpr (SWIGLU) {
+        blk = (lane == 1) ? p.up_off / kQBlock + nt : nt;          // gate, up block
+      } else {
+        const int nb = (p.N + kQBlock - 1) / kQBlock;
+        blk = min(2 * nt + (lane == 1 ? 1 : 0), nb - 1);           // two column blocks
+      }
+      sc_base = p.b_scale + static_cast<long long>(un.group) * p.b_scale_group + kb0;
+      sc_off = static_cast<uint32_t>(static_cast<long long>(blk) * p.b_scale_ld * 4);
+    }
+  }
+  if constexpr (FP8) {
+#pragma unroll
+    for (int i = 0; i < LMAX; ++i) off_tab[i][tid] = goff[i];
+    off_tab[LMAX][tid] = sc_off;
+    // visible to this lane's own later reads; no other lane reads it
+  }
+  auto lane_off_of = [&](int i) __attribute__((always_inline)) {
+    if constexpr (FP8) {
+      using vlds = volatile __attribute__((address_space(3))) uint32_t*;
+      return ((vlds)&off_tab[i][0])[tid];
+    }
+    else return i < LMAX ? goff[i] : 0u;
+  };
+  auto issue = [&](int step, uint8_t* buf, int b) __attribute__((always_inline)) {
     const long long kb = static_cast<long long>(step) * ROWB;
+    const uint8_t* ak = a_base + kb;   // wave-uniform bases of this K step
+    const uint8_t* bk = b_base + kb;
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i) dma16(a_base + goff[i] + kb, buf + (wave + i * NW) * 1024);
+    for (int i = 0; i < A_PER; ++i) dma16s(ak, lane_off_of(i), buf + (wave + i * NW) * 1024);
 #pragma unroll
-    for (int i = 0; i < B_PER; ++i)
-      dma16(b_base + goff[A_PER + i] + kb, buf + BM * ROWB + (wave + i * NW) * 1024);
+    for (int i = 0; i < B_PER; ++i) dma16s(bk, lane_off_of(A_PER + i), buf + BM * ROWB + (wave + i * NW) * 1024);
+    if constexpr (FP8) {
+      if (wave < BM / 64) dma4s(sc_base + step, lane_off_of(LMAX), reinterpret_cast<uint8_t*>(&sa_st[b & 1][64 * wave]));
+      else if (wave == BM / 64) dma4s(sc_base + step, lane_off_of(LMAX), reinterpret_cast<uint8_t*>(&sb_st[b & 1][0]));
+    }
   };
 
   f32x4 acc[TM][TN];
@@ -551,24 +641,73 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   // compile-time constant (the main loop is instantiated per row-tile count), so
   // every fragment read of a K slice is issued before its first MFMA and no
   // branch separates them.
-  auto compute = [&](const uint8_t* buf, auto Jc) __attribute__((always_inline)) {
+  // Fragment rows are 16 * tile + frag_row, and the row swizzle of such a row is a
+  // function of frag_row alone (tile rows are multiples of 8), so every fragment address
+  // is a per-lane offset (computed once) plus a compile-time tile offset.
+  auto lane_off = [&](int c) __attribute__((always_inline)) {
+    return frag_row * ROWB + ((c ^ swz<ROWB>(frag_row)) << 4);
+  };
+  auto compute = [&](const uint8_t* buf, int b, auto Jc) __attribute__((always_inline)) {
     constexpr int J = decltype(Jc)::value;
     const uint8_t* lb = buf + BM * ROWB;
-#pragma unroll
-    for (int kk = 0; kk < ROWB / 64; ++kk) {
-      const int c = kk * 4 + kgrp;
-      bf16x8 bfr[TN];
-      bf16x8 afr[J > 0 ? J : 1];
+    if constexpr (FP8) {
+      // one v_mfma_scale_f32_16x16x128_f8f6f4 (unit hardware scales) per tile pair and
+      // K block, promoted into the fp32 accumulator with s_a(token) * s_w(column block)
+      // ([MND §Quantization]: activation scales vary only along K).  Lane holds 32
+      // codes (16-byte chunks 2 * kgrp and 2 * kgrp + 1) of its fragment row.  Weight
+      // fragments of the TN column tiles stay in registers; each row tile's activation
+      // fragment is read once and used TN times.
+      // One LDS pointer per operand and chunk (stage base + lane offset), made opaque so
+      // that every tile's read uses it with an immediate tile offset instead of a
+      // precomputed address register per tile and stage.
+      using lptr = __attribute__((address_space(3))) const uint8_t*;
+      lptr a_lo = (lptr)(buf + lane_off(2 * kgrp));
+      lptr a_hi = (lptr)(buf + lane_off(2 * kgrp + 1));
+      lptr b_lo = (lptr)(lb + lane_off(2 * kgrp));
+      lptr b_hi = (lptr)(lb + lane_off(2 * kgrp + 1));
+      asm volatile("" : "+v"(a_lo), "+v"(a_hi), "+v"(b_lo), "+v"(b_hi));
+      auto frag = [&](lptr lo_p, lptr hi_p, int tile) __attribute__((always_inline)) {
+        const u32x4 lo = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(lo_p + tile * 16 * ROWB);
+        const u32x4 hi = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(hi_p + tile * 16 * ROWB);
+        return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      };
+      i32x8 bw[TN];
+      float sb[TN];
+      const float sb0 = sb_st[b & 1][0];
+      const float sb1 = sb_st[b & 1][1];
 #pragma unroll
       for (int i = 0; i < TN; ++i) {
-        const int rb_ = wn * TN * 16 + 16 * i + frag_row;
-        bfr[i] = *reinterpret_cast<const bf16x8*>(lb + rb_ * ROWB + ((c ^ swz<ROWB>(rb_)) << 4));
+        bw[i] = frag(b_lo, b_hi, wn * TN + i);
+        // SwiGLU: tiles i < TN/2 are gate columns (block 0), the rest up columns
+        // (block 1); plain store: the first 128 columns of the tile are block 0
+        sb[i] = SWIGLU ? (i < TN / 2 ? sb0 : sb1) : (wn * TN * 16 < kQBlock ? sb0 : sb1);
       }
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        const int ra_ = 16 * (j * WM + wm) + frag_row;
-        afr[j] = *reinterpret_cast<const bf16x8*>(buf + ra_ * ROWB + ((c ^ swz<ROWB>(ra_)) << 4));
+        const i32x8 at = frag(a_lo, a_hi, j * WM + wm);
+        const float sa = sa_st[b & 1][16 * (j * WM + wm) + (lane & 15)];
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+          const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              bw[i], at, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+          const float f = sa * sb[i];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[j][i][r] = fmaf(part[r], f, acc[j][i][r]);
+        }
       }
+      return;
+    }
+#pragma unroll
+    for (int kk = 0; kk < ROWB / 64; ++kk) {
+      const int o = lane_off(kk * 4 + kgrp);
+      bf16x8 bfr[TN];
+      bf16x8 afr[J > 0 ? J : 1];
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+        bfr[i] = *reinterpret_cast<const bf16x8*>(lb + (wn * TN + i) * 16 * ROWB + o);
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        afr[j] = *reinterpret_cast<const bf16x8*>(buf + (j * WM + wm) * 16 * ROWB + o);
 #pragma unroll
       for (int j = 0; j < J; ++j)
 #pragma unroll
@@ -598,7 +737,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   // prologue: steps 0 .. NST-2
 #pragma unroll
   for (int b = 0; b < NST - 1; ++b) {
-    if (b < nsteps) issue(b, b == 0 ? st0 : b == 1 ? st1 : b == 2 ? st2 : st3);
+    if (b < nsteps) issue(b, b == 0 ? st0 : b == 1 ? st1 : b == 2 ? st2 : st3, b);
   }
   auto mainloop = [&](auto Jc) __attribute__((always_inline)) {
     for (int s0 = 0; s0 < nsteps; s0 += NST) {
@@ -611,16 +750,21 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
           lds_barrier();
           // refill the buffer consumed at step s - 1 with step s + NST - 1
           const int nb = (b + NST - 1) % NST;
-          if (s + NST - 1 < nsteps) issue(s + NST - 1, nb == 0 ? st0 : nb == 1 ? st1 : nb == 2 ? st2 : st3);
-          compute(b == 0 ? st0 : b == 1 ? st1 : b == 2 ? st2 : st3, Jc);
+          if (s + NST - 1 < nsteps) issue(s + NST - 1, nb == 0 ? st0 : nb == 1 ? st1 : nb == 2 ? st2 : st3, nb);
+          compute(b == 0 ? st0 : b == 1 ? st1 : b == 2 ? st2 : st3, b, Jc);
         }
       }
     }
   };
   // jcount is wave-uniform and at most TM; every instantiation runs the same
   // sequence of barriers, so wavefronts with different counts stay in step.
-  static_assert(TM <= 5, "row-tile dispatch covers TM <= 5");
+  static_assert(TM <= 10, "row-tile dispatch covers TM <= 10");
   switch (jcount) {
+    case 10: if constexpr (TM >= 10) mainloop(std::integral_constant<int, (TM >= 10 ? 10 : 0)>{}); break;
+    case 9: if constexpr (TM >= 9) mainloop(std::integral_constant<int, (TM >= 9 ? 9 : 0)>{}); break;
+    case 8: if constexpr (TM >= 8) mainloop(std::integral_constant<int, (TM >= 8 ? 8 : 0)>{}); break;
+    case 7: if constexpr (TM >= 7) mainloop(std::integral_constant<int, (TM >= 7 ? 7 : 0)>{}); break;
+    case 6: if constexpr (TM >= 6) mainloop(std::integral_constant<int, (TM >= 6 ? 6 : 0)>{}); break;
     case 5: if constexpr (TM >= 5) mainloop(std::integral_constant<int, (TM >= 5 ? 5 : 0)>{}); break;
     case 4: if constexpr (TM >= 4) mainloop(std::integral_constant<int, (TM >= 4 ? 4 : 0)>{}); break;
     case 3: if constexpr (TM >= 3) mainloop(std::integral_constant<int, (TM >= 3 ? 3 : 0)>{}); break;
@@ -631,6 +775,12 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
 
   // ---- epilogue.  Transposed C fragment of a 16x16 tile: lane holds token row
   // lane & 15 and output columns 4 * (lane >> 4) + r, r = 0..3.
+  // The epilogue's base values pass through an empty asm statement here, so no output
+  // address can be formed before the main loop and held in registers across it.
+  int row0_e = un.row0;
+  long long ldc_e = ldc;
+  void* cptr_e = cptr;
+  asm volatile("" : "+s"(row0_e), "+s"(ldc_e), "+s"(cptr_e));
   const int crow = lane & 15;
   const int ccol4 = 4 * kgrp;
   if constexpr (EPI == EPI_STORE_BF16 || EPI == EPI_STORE_F32) {
@@ -642,30 +792,30 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
 #pragma unroll
       for (int i = 0; i < TN; ++i) {
         const int col = nt * BN + wn * TN * 16 + 16 * i + ccol4;
-        const long long o = static_cast<long long>(un.row0 + row) * ldc + col;
+        const long long o = static_cast<long long>(row0_e + row) * ldc_e + col;
         // bf16 rows are 8-byte aligned (ldc is a multiple of 128); fp32 partials only
         // take the 16-byte store when the address allows it
         const bool vec = col + 3 < p.N &&
                          (EPI == EPI_STORE_BF16 ||
-                          (reinterpret_cast<uintptr_t>(static_cast<float*>(cptr) + o + split * p.c_split) & 15) == 0);
+                          (reinterpret_cast<uintptr_t>(static_cast<float*>(cptr_e) + o + split * p.c_split) & 15) == 0);
         if (vec) {
           if constexpr (EPI == EPI_STORE_BF16) {
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(cptr) + o) =
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(cptr_e) + o) =
                 make_uint2(pack_bf16x2(acc[j][i][0], acc[j][i][1]), pack_bf16x2(acc[j][i][2], acc[j][i][3]));
           } else {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(cptr) + o + split * p.c_split) = acc[j][i];
+            *reinterpret_cast<f32x4*>(static_cast<float*>(cptr_e) + o + split * p.c_split) = acc[j][i];
           }
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             if (col + r >= p.N) continue;
-            if constexpr (EPI == EPI_STORE_BF16) static_cast<uint16_t*>(cptr)[o + r] = f32_to_bf16(acc[j][i][r]);
-            else static_cast<float*>(cptr)[o + r + split * p.c_split] = acc[j][i][r];
+            if constexpr (EPI == EPI_STORE_BF16) static_cast<uint16_t*>(cptr_e)[o + r] = f32_to_bf16(acc[j][i][r]);
+            else static_cast<float*>(cptr_e)[o + r + split * p.c_split] = acc[j][i][r];
           }
         }
       }
     }
-  } else {
+  } else if constexpr (EPI == EPI_SWIGLU_BF16) {
     constexpr int HT = TN / 2;
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
@@ -682,7 +832,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
           const float up = acc[j][i + HT][r];
           hv[r] = g / (1.0f + __expf(-g)) * up;
         }
-        uint16_t* hp = static_cast<uint16_t*>(cptr) + static_cast<long long>(un.row0 + row) * ldc + col;
+        uint16_t* hp = static_cast<uint16_t*>(cptr_e) + static_cast<long long>(row0_e + row) * ldc_e + col;
         if (col + 3 < p.N) {
           *reinterpret_cast<uint2*>(hp) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
         } else {
@@ -692,17 +842,75 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
         }
       }
     }
+  } else {
+    // EPI_SWIGLU_FP8: h = silu(gate) * up, quantized per 1x128 block (the workgroup's
+    // 128 h columns) with scale = amax / 448 and codes e4m3(h * 448 / amax)
+    // ([MND §Quantization]: the SiLU output is block-quantized in the same kernel).
+    // Row amax: lane-local over its 4 * HT values, across the four lanes of the row
+    // (lane ^ 16, lane ^ 32), then across the WN wavefronts through LDS.
+    constexpr int HT = TN / 2;
+    static_assert(BN / 2 == kQBlock, "h tile must be one scale block");
+    float* xch = reinterpret_cast<float*>(st0);   // [WN][BM] row maxima
+    lds_barrier();                                 // every wavefront is done with the ring
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      if (j >= jcount) continue;
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < HT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float g = acc[j][i][r];
+          const float hv = g / (1.0f + __expf(-g)) * acc[j][i + HT][r];
+          acc[j][i][r] = hv;
+          m = fmaxf(m, fabsf(hv));
+        }
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      if (kgrp == 0) xch[wn * BM + 16 * (j * WM + wm) + crow] = m;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f & ~(15 << 8));   // LDS writes done (lgkmcnt 0)
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      if (j >= jcount) continue;
+      const int row = 16 * (j * WM + wm) + crow;
+      if (row >= rows) continue;
+      float amax = 0.f;
+#pragma unroll
+      for (int w = 0; w < WN; ++w) amax = fmaxf(amax, xch[w * BM + row]);
+      const bool zero = amax == 0.f;
+      const float scale = zero ? 1.0f : amax / 448.0f;
+      const float inv = zero ? 0.0f : 448.0f / amax;
+      uint8_t* hrow = static_cast<uint8_t*>(cptr_e) + static_cast<long long>(row0_e + row) * ldc_e;
+#pragma unroll
+      for (int i = 0; i < HT; ++i) {
+        const int col = nt * (BN / 2) + wn * (TN * 8) + 16 * i + ccol4;
+        uint32_t q = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) q |= (zero ? 0u : f32_to_e4m3(acc[j][i][r] * inv)) << (8 * r);
+        if (col + 3 < p.N) {
+          *reinterpret_cast<uint32_t*>(hrow + col) = q;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (col + r < p.N) hrow[col + r] = static_cast<uint8_t>(q >> (8 * r));
+        }
+      }
+      if (wn == 0 && kgrp == 0)
+        p.c_scale[static_cast<long long>(row0_e + row) * p.c_scale_ld + nt] = scale;
+    }
   }
 }
 
-template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST>
+template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST, bool FP8>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs p) {
-  gemm_dma_body<WM, WN, TM, TN, EPI, false, ROWB, NST>(p);
+  gemm_dma_body<WM, WN, TM, TN, EPI, false, ROWB, NST, FP8>(p);
 }
 
 template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST>
 __global__ __launch_bounds__(WM* WN * 64) void dense_gemm_dma_kernel(GemmArgs p) {
-  gemm_dma_body<WM, WN, TM, TN, EPI, true, ROWB, NST>(p);
+  gemm_dma_body<WM, WN, TM, TN, EPI, true, ROWB, NST, false>(p);
 }
 
 // Experts: units come from the device-built table.
@@ -829,7 +1037,7 @@ hipError_t go(const GemmArgs& a, int max_units, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST>
+template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST, bool FP8 = false>
 hipError_t go_dma(const GemmArgs& a, int max_units, hipStream_t st) {
   const long long per_unit = static_cast<long long>(a.n_tiles) * a.splits;
   const long long slots = (static_cast<long long>(max_units) + kXcds - 1) / kXcds;
@@ -837,10 +1045,14 @@ hipError_t go_dma(const GemmArgs& a, int max_units, hipStream_t st) {
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (a.uniform_rows > 0) {
-    dense_gemm_dma_kernel<WM, WN, TM, TN, EPI, ROWB, NST>
-        <<<static_cast<unsigned>(blocks), WM * WN * 64, 0, st>>>(a);
+    if constexpr (FP8) {
+      return hipErrorInvalidValue;  // fp8 operands come only from the grouped (routed) path
+    } else {
+      dense_gemm_dma_kernel<WM, WN, TM, TN, EPI, ROWB, NST>
+          <<<static_cast<unsigned>(blocks), WM * WN * 64, 0, st>>>(a);
+    }
   } else {
-    grouped_gemm_dma_kernel<WM, WN, TM, TN, EPI, ROWB, NST>
+    grouped_gemm_dma_kernel<WM, WN, TM, TN, EPI, ROWB, NST, FP8>
         <<<static_cast<unsigned>(blocks), WM * WN * 64, 0, st>>>(a);
   }
   return hipGetLastError();
@@ -865,7 +1077,7 @@ hipError_t go_epi(Epilogue epi, bool fp8, const GemmArgs& a, int max_units, hipS
 
 int gemm_block_m(GemmCfg cfg, bool fp8) {
   switch (cfg) {
-    case CFG_BIG: return fp8 ? 128 : 320;
+    case CFG_BIG: return fp8 ? 256 : 320;
     case CFG_SMALL: return 32;
     default: return 64;
   }
@@ -877,8 +1089,15 @@ hipError_t launch_gemm(GemmCfg cfg, Epilogue epi, bool fp8, const GemmArgs& a, i
                        hipStream_t st) {
   switch (cfg) {
     case CFG_BIG:
-      // fp8 keeps a per-K-block product next to the accumulators: shorter row tile
-      if (fp8) return go_epi<4, 2, 2, 8>(epi, fp8, a, max_units, st);
+      if (fp8) {
+        if (a.uniform_rows > 0) return hipErrorInvalidValue;
+        // fp8 fragments are 32 bytes per lane and the promotion needs the scales next to
+        // the accumulators: 256 x 256 tiles, 2 x 4 wavefronts of 128 x 64 that keep four
+        // weight fragments resident and stream the activation fragments
+        if (epi == EPI_SWIGLU_FP8) return go_dma<2, 4, 8, 4, EPI_SWIGLU_FP8, 128, 2, true>(a, max_units, st);
+        if (epi == EPI_STORE_BF16) return go_dma<2, 4, 8, 4, EPI_STORE_BF16, 128, 2, true>(a, max_units, st);
+        return hipErrorInvalidValue;
+      }
       if (epi == EPI_SWIGLU_BF16) return go_dma<4, 2, 5, 8, EPI_SWIGLU_BF16, 128, 2>(a, max_units, st);
       if (epi == EPI_STORE_BF16) return go_dma<4, 2, 5, 8, EPI_STORE_BF16, 128, 2>(a, max_units, st);
       return hipErrorInvalidValue;
