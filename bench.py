@@ -179,7 +179,7 @@ def roofline_entry(acc_k: dict, ms: float) -> dict:
 
 # ----------------------------------------------------------------------------- GPU run
 
-def run_gpu(cfg, steps, warmup):
+def run_gpu(cfg, steps, warmup, two_streams=True):
     import torch
 
     import moe_expert_layer_top_amd as M
@@ -205,8 +205,11 @@ def run_gpu(cfg, steps, warmup):
     for row in events:              # create the underlying HIP events
         for e in row:
             e.record(stream)
+    # the shared expert's own launches (when it is not a group of the routed launches)
+    # go to a second stream, where they overlap the routing kernels
+    side = torch.cuda.Stream() if two_streams else None
     for _ in range(warmup):
-        M.moe_layer(s, W, g["x"], out, idx, w, logits, ws)
+        M.moe_layer_overlap(s, W, g["x"], out, idx, w, logits, ws, side)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -214,7 +217,7 @@ def run_gpu(cfg, steps, warmup):
     wall0 = time.perf_counter()
     start.record(stream)
     for i in range(steps):
-        M.moe_layer_profiled(s, W, g["x"], out, idx, w, logits, ws, events[i])
+        M.moe_layer_profiled(s, W, g["x"], out, idx, w, logits, ws, events[i], side=side)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -316,6 +319,8 @@ def main():
     ap.add_argument("--config", default="c2_prefill_bf16")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--one-stream", action="store_true",
+                    help="run the shared expert's own launches on the layer's stream")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (scales the HBM byte counters)")
     args = ap.parse_args()
@@ -329,13 +334,21 @@ def main():
 
     from synth import configs
     cfg = configs.get(args.config)
-    r = run_gpu(cfg, args.steps, args.warmup)
+    r = run_gpu(cfg, args.steps, args.warmup, two_streams=not args.one_stream)
     ms = r["total_ms"] / args.steps
     tokens = cfg.shared_rows
     acc = launch_accounting(cfg, account(cfg, r["tpe"]))
     kern = {name: roofline_entry(acc[name], r["stage_ms"][name]) for name in acc}
     if shared_is_merged(cfg):
         kern["shared"] = {"ms": r["stage_ms"]["shared"], "merged_into": ["ffn1", "ffn2"]}
+        shared_mode = "merged into the routed launches"
+    elif not args.one_stream:
+        # the shared stage is only the wait for the side stream: no rates for it
+        kern["shared"] = {"ms": r["stage_ms"]["shared"], "side_stream": True,
+                          "note": "ms = time the layer's stream waited for the shared expert"}
+        shared_mode = "side stream"
+    else:
+        shared_mode = "in line"
     dom = max(("ffn1", "ffn2"), key=lambda n: r["stage_ms"][n])
     dk = kern[dom]
     if dk["bound"] == "mfma":
@@ -375,6 +388,7 @@ def main():
         "ffn_mfma_frac": ffn_flops / (ffn_ms / 1e3) / 1e12 / PEAK_TFLOPS[acc["ffn1"]["dt"]],
         "permute_combine_hbm_frac": permute_bytes / (permute_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
         "kernels": kern,
+        "shared_expert": shared_mode,
         "active_experts": int(np.count_nonzero(r["tpe"])),
         "max_rows_per_expert": int(r["tpe"].max()),
         "wall_ms_per_step": r["wall_s"] * 1e3 / args.steps,

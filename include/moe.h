@@ -12,6 +12,7 @@
  *         deployment" (Perplexity, 2025-04-18).
  *   [R1P] page "CANN/cann-recipes-infer: DeepSeek-R1 prefill optimization"
  *         (DeepSeek-R1 prefill on Atlas A3).
+ *   [V32] page "NPU DeepSeek-V3.2-Exp inference optimization practice".
  *
  * Conventions shared by every call
  *   - Tensor pointers are DEVICE pointers, row-major, 16-byte aligned.  The
@@ -176,6 +177,22 @@ moe_status moe_layer(const moe_shape* s, const moe_weights* w, const void* x, vo
                      int32_t* topk_idx, float* topk_w, float* logits, void* ws,
                      size_t ws_bytes, hipStream_t stream);
 
+/* moe_layer with the shared expert on a second stream.  [V32 §multi-stream parallel
+ * optimization] and [MND §Computation and communication overlap] (Dispatch Overlap):
+ * the shared expert needs neither the gate nor the routing, so it can run beside them.
+ * When the shared expert runs in launches of its own (fp8 or fp32 experts, or
+ * I_shared != I; otherwise it is already a group of the routed launches and `side` is
+ * not used), its two GEMMs are enqueued on `side` behind an event recorded on `stream`
+ * at entry, and `stream` waits for them before finalize.  On return, all of the call's
+ * work is ordered before anything enqueued later on `stream`, as with moe_layer; the
+ * results are bit-identical to moe_layer's.  side == NULL or side == stream: same as
+ * moe_layer.  The call creates two events and releases them before returning.  Both
+ * streams must belong to the current device.  On an error return, work already
+ * enqueued on `side` may still run and `stream` does not wait for it.                 */
+moe_status moe_layer_overlap(const moe_shape* s, const moe_weights* w, const void* x,
+                             void* out, int32_t* topk_idx, float* topk_w, float* logits,
+                             void* ws, size_t ws_bytes, hipStream_t stream, hipStream_t side);
+
 /* Launch boundaries at which moe_layer_profiled records events. */
 enum {
   MOE_EV_START = 0,      /* before the gate projection                          */
@@ -191,13 +208,16 @@ enum {
   MOE_EV_COUNT = 10
 };
 
-/* moe_layer, additionally recording events[i] on `stream` at launch boundary i
- * (i < n_events; NULL entries are skipped), so a profiler can time every kernel
- * class of one layer from the host ([MND §Latency breakdown]: the time of one
- * MoE layer split by kernel class).  Same arguments and behaviour as moe_layer. */
+/* moe_layer_overlap (side may be NULL: moe_layer), additionally recording events[i] on
+ * `stream` at launch boundary i (i < n_events; NULL entries are skipped), so a
+ * profiler can time every kernel class of one layer from the host ([MND §Latency
+ * breakdown]: the time of one MoE layer split by kernel class).  When the shared expert
+ * runs on `side`, MOE_EV_SHARED follows the wait for it, so the FFN2 -> SHARED
+ * interval is the part of the shared expert that the routed work did not hide.  Same
+ * arguments and behaviour as moe_layer_overlap otherwise. */
 moe_status moe_layer_profiled(const moe_shape* s, const moe_weights* w, const void* x,
                               void* out, int32_t* topk_idx, float* topk_w, float* logits,
-                              void* ws, size_t ws_bytes, hipStream_t stream,
+                              void* ws, size_t ws_bytes, hipStream_t stream, hipStream_t side,
                               hipEvent_t* events, int32_t n_events);
 
 /* Waits for `stream`, then reads and clears the device error word of `ws`:

@@ -6,6 +6,7 @@ from ._lib import (  # noqa: F401
     MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP, MOE_EDEVICE,
     MOE_F32, MOE_BF16, MOE_FP8_E4M3, MoEError, moe_shape, moe_weights, shape, shape_of, weights,
     lib, moe_workspace_bytes, moe_grouped_ffn_workspace_bytes, moe_gate_topk, moe_init_routing,
-    moe_grouped_ffn, moe_finalize_routing, moe_layer, moe_layer_profiled, moe_get_error,
+    moe_grouped_ffn, moe_finalize_routing, moe_layer, moe_layer_overlap, moe_layer_profiled,
+    moe_get_error,
     moe_status_str, EV_NAMES,
 )

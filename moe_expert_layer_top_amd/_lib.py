@@ -21,8 +21,8 @@ DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 
 EXPORTS = [
     "moe_workspace_bytes", "moe_grouped_ffn_workspace_bytes", "moe_gate_topk", "moe_init_routing",
-    "moe_grouped_ffn", "moe_finalize_routing", "moe_layer", "moe_layer_profiled", "moe_get_error",
-    "moe_status_str",
+    "moe_grouped_ffn", "moe_finalize_routing", "moe_layer", "moe_layer_overlap", "moe_layer_profiled",
+    "moe_get_error", "moe_status_str",
 ]
 EV_NAMES = ["start", "gate", "topk", "route", "expand", "plan", "ffn1", "ffn2", "shared", "finalize"]
 
@@ -65,7 +65,8 @@ def lib() -> ctypes.CDLL:
             "moe_grouped_ffn": (I32, [S, I32, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
             "moe_finalize_routing": (I32, [S, P, P, P, P, P, P]),
             "moe_layer": (I32, [S, ctypes.POINTER(moe_weights), P, P, P, P, P, P, SZ, P]),
-            "moe_layer_profiled": (I32, [S, ctypes.POINTER(moe_weights), P, P, P, P, P, P, SZ, P,
+            "moe_layer_overlap": (I32, [S, ctypes.POINTER(moe_weights), P, P, P, P, P, P, SZ, P, P]),
+            "moe_layer_profiled": (I32, [S, ctypes.POINTER(moe_weights), P, P, P, P, P, P, SZ, P, P,
                                          ctypes.POINTER(ctypes.c_void_p), I32]),
             "moe_get_error": (I32, [P, P]),
             "moe_status_str": (ctypes.c_char_p, [I32]),
@@ -163,14 +164,23 @@ def moe_layer(s, w: moe_weights, x, out, topk_idx, topk_w, logits, ws, stream=No
                            _stream(stream)), "moe_layer")
 
 
+def moe_layer_overlap(s, w: moe_weights, x, out, topk_idx, topk_w, logits, ws, side, stream=None):
+    """moe_layer with the shared expert's own launches on `side` (a torch.cuda.Stream)."""
+    _check(lib().moe_layer_overlap(ctypes.byref(s), ctypes.byref(w), _ptr(x), _ptr(out),
+                                   _ptr(topk_idx), _ptr(topk_w), _ptr(logits), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream),
+                                   None if side is None else _stream(side)), "moe_layer_overlap")
+
+
 def moe_layer_profiled(s, w: moe_weights, x, out, topk_idx, topk_w, logits, ws, events,
-                       stream=None):
-    """moe_layer recording `events` (torch.cuda.Event, already created) at its launch
-    boundaries, in the order of EV_NAMES."""
+                       side=None, stream=None):
+    """moe_layer_overlap (side=None: moe_layer) recording `events` (torch.cuda.Event,
+    already created) at its launch boundaries, in the order of EV_NAMES."""
     arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
     _check(lib().moe_layer_profiled(ctypes.byref(s), ctypes.byref(w), _ptr(x), _ptr(out),
                                     _ptr(topk_idx), _ptr(topk_w), _ptr(logits), _ptr(ws),
-                                    ws.numel() * ws.element_size(), _stream(stream), arr,
+                                    ws.numel() * ws.element_size(), _stream(stream),
+                                    None if side is None else _stream(side), arr,
                                     len(events)), "moe_layer_profiled")
 
 

@@ -448,7 +448,8 @@ moe_status moe_finalize_routing(const moe_shape* s, const void* y, const void* s
 
 static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const void* x, void* out,
                              int32_t* topk_idx, float* topk_w, float* logits, void* ws,
-                             size_t ws_bytes, hipStream_t stream, const Prof& prof);
+                             size_t ws_bytes, hipStream_t stream, const Prof& prof,
+                             hipStream_t side = nullptr);
 
 moe_status moe_layer(const moe_shape* s, const moe_weights* w, const void* x, void* out,
                      int32_t* topk_idx, float* topk_w, float* logits, void* ws, size_t ws_bytes,
@@ -456,19 +457,39 @@ moe_status moe_layer(const moe_shape* s, const moe_weights* w, const void* x, vo
   return layer_impl(s, w, x, out, topk_idx, topk_w, logits, ws, ws_bytes, stream, Prof());
 }
 
+moe_status moe_layer_overlap(const moe_shape* s, const moe_weights* w, const void* x, void* out,
+                             int32_t* topk_idx, float* topk_w, float* logits, void* ws,
+                             size_t ws_bytes, hipStream_t stream, hipStream_t side) {
+  return layer_impl(s, w, x, out, topk_idx, topk_w, logits, ws, ws_bytes, stream, Prof(),
+                    side == stream ? nullptr : side);
+}
+
 moe_status moe_layer_profiled(const moe_shape* s, const moe_weights* w, const void* x, void* out,
                               int32_t* topk_idx, float* topk_w, float* logits, void* ws,
-                              size_t ws_bytes, hipStream_t stream, hipEvent_t* events,
-                              int32_t n_events) {
+                              size_t ws_bytes, hipStream_t stream, hipStream_t side,
+                              hipEvent_t* events, int32_t n_events) {
   Prof p;
   p.ev = events;
   p.n = events ? n_events : 0;
-  return layer_impl(s, w, x, out, topk_idx, topk_w, logits, ws, ws_bytes, stream, p);
+  return layer_impl(s, w, x, out, topk_idx, topk_w, logits, ws, ws_bytes, stream, p,
+                    side == stream ? nullptr : side);
 }
+
+// Fork/join of the shared expert onto a second stream: two events, created for this call
+// and released once enqueued (a recorded event that streams still wait on is freed by the
+// runtime when it completes).
+struct SideFork {
+  hipEvent_t fork = nullptr, join = nullptr;
+  ~SideFork() {
+    if (fork) (void)hipEventDestroy(fork);
+    if (join) (void)hipEventDestroy(join);
+  }
+};
 
 static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const void* x, void* out,
                              int32_t* topk_idx, float* topk_w, float* logits, void* ws,
-                             size_t ws_bytes, hipStream_t stream, const Prof& prof) {
+                             size_t ws_bytes, hipStream_t stream, const Prof& prof,
+                             hipStream_t side) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if ((st = check_inter(s, s->I)) != MOE_OK) return st;
@@ -485,8 +506,29 @@ static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const voi
   float* lg = logits ? logits : at<float>(ws, L.logits);
   int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
   float* tw = topk_w ? topk_w : at<float>(ws, L.w);
-  // gate + router  ([MND §Expert Parallelism], [MND §MoE Router])
   if (prof.mark(MOE_EV_START, stream) != hipSuccess) return MOE_EHIP;
+  // The shared expert depends on x alone, not on the gate, the routing or the routed
+  // experts ([V32 §multi-stream parallel optimization]; [MND §Computation and
+  // communication overlap], Dispatch Overlap).  When it runs in launches of its own and
+  // the caller gives a second stream, it starts there at once and overlaps the routing
+  // kernels, which leave most of the machine idle; finalize waits for it.
+  const bool merged = merge_shared(s);
+  FfnIo sio{x, nullptr, nullptr, w->sh_w13, nullptr, w->sh_w2, nullptr, at<void>(ws, L.sh_out)};
+  moe_shape sh = *s;
+  sh.wt = s->act;
+  SideFork sf;
+  const bool forked = side && !merged;
+  if (forked) {
+    if (hipEventCreateWithFlags(&sf.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&sf.join, hipEventDisableTiming) != hipSuccess ||
+        hipEventRecord(sf.fork, stream) != hipSuccess ||
+        hipStreamWaitEvent(side, sf.fork, 0) != hipSuccess)
+      return MOE_EHIP;
+    st = run_ffn(&sh, 1, s->T, s->I_shared, sio, at<void>(ws, L.sh_ffn), side);
+    if (st != MOE_OK) return st;
+    if (hipEventRecord(sf.join, side) != hipSuccess) return MOE_EHIP;
+  }
+  // gate + router  ([MND §Expert Parallelism], [MND §MoE Router])
   st = run_gate_topk(s, x, w->w_gate, w->bias, lg, idx, tw, at<float>(ws, L.part), stream, prof);
   if (st != MOE_OK) return st;
   // first routing: expand and sort by expert  ([R1P §MoE deployment strategy optimization]).
@@ -511,14 +553,12 @@ static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const voi
     io.gather = ssrc;
     io.gather_div = s->k;
   }
-  FfnIo sio{x, nullptr, nullptr, w->sh_w13, nullptr, w->sh_w2, nullptr, at<void>(ws, L.sh_out)};
-  const bool merged = merge_shared(s);
   st = run_ffn(s, s->E, R, s->I, io, at<void>(ws, L.ffn), stream, prof, MOE_EV_PLAN, MOE_EV_FFN1,
                MOE_EV_FFN2, merged ? &sio : nullptr, merged ? s->T : 0);
   if (st != MOE_OK) return st;
-  if (!merged) {
-    moe_shape sh = *s;
-    sh.wt = s->act;
+  if (forked) {
+    if (hipStreamWaitEvent(stream, sf.join, 0) != hipSuccess) return MOE_EHIP;
+  } else if (!merged) {
     st = run_ffn(&sh, 1, s->T, s->I_shared, sio, at<void>(ws, L.sh_ffn), stream);
     if (st != MOE_OK) return st;
   }
