@@ -44,8 +44,17 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
     float l = -INFINITY;
     if (e < E) {
       const float* p = part + static_cast<long long>(t) * E + e;
+      // partials are loaded 8 at a time (all in flight together) and added strictly in
+      // split order, so the sum does not depend on the batching
       l = p[0];
-      for (int s = 1; s < splits; ++s) l += p[s * split_stride];
+      for (int s0 = 1; s0 < splits; s0 += 8) {
+        float q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = s0 + i < splits ? p[(s0 + i) * split_stride] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (s0 + i < splits) l += q[i];
+      }
       if (logits_out) logits_out[static_cast<long long>(t) * E + e] = l;
       if (bias) l += bias[e];
     }
@@ -159,9 +168,14 @@ __global__ __launch_bounds__(256) void route_count_kernel(const int32_t* __restr
   if (seg >= nseg) return;
   int err = 0;
   const long long s0 = static_cast<long long>(seg) * kSegSlots;
+  // every key of the segment is loaded before the first ballot (all loads in flight)
+  uint32_t keys[kSegSlots / 64];
+#pragma unroll
+  for (int it = 0; it < kSegSlots / 64; ++it) keys[it] = local_key(ids, s0 + it * 64 + lane, R, e_base, E, &err);
+#pragma unroll
   for (int it = 0; it < kSegSlots / 64; ++it) {
     const long long s = s0 + it * 64 + lane;
-    const uint32_t key = local_key(ids, s, R, e_base, E, &err);
+    const uint32_t key = keys[it];
     const uint64_t active = __ballot(s < R);
     if (active == 0) break;
     const uint64_t peers = peer_mask(key, bits, active);
@@ -190,10 +204,16 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
     if (seg_err[s]) any_err = 1;  // benign race: every writer stores 1
   int32_t run = 0;
   if (e < E) {
-    for (int s = 0; s < nseg; ++s) {
-      const int32_t c = counts[static_cast<long long>(s) * E + e];
-      counts[static_cast<long long>(s) * E + e] = run;
-      run += c;
+    // segment counts 16 at a time (loads in flight together), prefix in segment order
+    for (int s0 = 0; s0 < nseg; s0 += 16) {
+      int32_t c[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] = s0 + i < nseg ? counts[static_cast<long long>(s0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (s0 + i < nseg) counts[static_cast<long long>(s0 + i) * E + e] = run;
+        run += c[i];
+      }
     }
   }
   // exclusive scan of `run` over experts (block of 1024 threads, 16 waves)
@@ -226,7 +246,14 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
   }
   __syncthreads();
   if (e < E) {
-    for (int s = 0; s < nseg; ++s) counts[static_cast<long long>(s) * E + e] += excl;
+    for (int s0 = 0; s0 < nseg; s0 += 16) {
+      int32_t c[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] = s0 + i < nseg ? counts[static_cast<long long>(s0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (s0 + i < nseg) counts[static_cast<long long>(s0 + i) * E + e] = c[i] + excl;
+    }
   }
 }
 
@@ -243,11 +270,15 @@ __global__ __launch_bounds__(256) void route_place_kernel(const int32_t* __restr
   for (int e = lane; e < E; e += 64) cnt[e] = base[static_cast<long long>(seg) * E + e];
   int err = 0;
   const long long s0 = static_cast<long long>(seg) * kSegSlots;
+  uint32_t keys[kSegSlots / 64];
+#pragma unroll
+  for (int it = 0; it < kSegSlots / 64; ++it) keys[it] = local_key(ids, s0 + it * 64 + lane, R, e_base, E, &err);
+#pragma unroll
   for (int it = 0; it < kSegSlots / 64; ++it) {
     const long long s = s0 + it * 64 + lane;
     const uint64_t active = __ballot(s < R);
     if (active == 0) break;
-    const uint32_t key = local_key(ids, s, R, e_base, E, &err);
+    const uint32_t key = keys[it];
     const uint64_t peers = peer_mask(key, bits, active);
     const bool valid = (s < R) && key < static_cast<uint32_t>(E);
     int32_t pos = -1;
