@@ -25,7 +25,9 @@ notes): ties in the top-k go to the lower expert id; slots are flattened
 token-major (s = t*k + j); rows of one expert keep ascending s; no routed
 scaling factor; the expert bias is added to the logits and used for both
 selection and weights; invalid expert ids are dropped from the routing and
-reported; fp8 is OCP e4m3fn (max 448, round-to-nearest-even, saturating).
+reported; fp8 is OCP e4m3fn (max 448, round-to-nearest-even, saturating).  The
+router's variants (route_grouped: group-limited selection, softmax weights, no
+renormalization, a routed scaling factor) state their readings where they are defined.
 """
 from __future__ import annotations
 
@@ -177,6 +179,69 @@ def route_topk(logits32: np.ndarray, bias32, k: int):
     return idx, w.astype(np.float32)
 
 
+# The router's variants.  [MND §MoE Router]: one router serves every MoE model, since
+# Mixtral's routing is DeepSeek's with the top-K group equal to the group of all experts.
+# The pages name the top-K group but not its scoring; the readings taken here: experts
+# form n_group groups of E / n_group consecutive ids; a group's score is the sum of its
+# group_topn largest scores (1: its best expert; 2: its best two), added in float32; the
+# topk_group best groups are kept (ties to the lower group id); the k experts are the
+# best of the kept groups' experts.  Scores z = logit + bias decide both steps.  Weights:
+# sigmoid(z) of the selected (the workload's scoring) or softmax(z) over all E experts
+# taken at the selected (Mixtral's), optionally renormalized over the k selected, then
+# multiplied by a routed scaling factor.
+DEFAULT_ROUTER = dict(scoring="sigmoid", renormalize=True, n_group=1, topk_group=1, group_topn=1,
+                      scale=1.0)
+
+
+def route_grouped(logits32: np.ndarray, bias32, k: int, router=None):
+    """General top-k router (group-limited selection, sigmoid or softmax weights).
+
+    With the default router this is route_topk.  Returns (idx int32 [T, k], w float32
+    [T, k]); idx lists each token's experts by z descending, ties to the lower id.
+    """
+    r = dict(DEFAULT_ROUTER, **(router or {}))
+    z = np.asarray(logits32, dtype=np.float32)
+    if bias32 is not None:
+        z = (z + np.asarray(bias32, dtype=np.float32)[None, :]).astype(np.float32)
+    if not np.isfinite(z).all():
+        raise ValueError("non-finite router score")
+    T, E = z.shape
+    G, TG, GN = int(r["n_group"]), int(r["topk_group"]), int(r["group_topn"])
+    if G < 1 or E % G or not 1 <= TG <= G or GN not in (1, 2) or GN > E // G:
+        raise ValueError("bad expert grouping")
+    gsz = E // G
+    if not 1 <= k <= TG * gsz:
+        raise ValueError("k must be in [1, topk_group * E / n_group]")
+    if r["scoring"] not in ("sigmoid", "softmax"):
+        raise ValueError("scoring is sigmoid or softmax")
+    idx = np.empty((T, k), dtype=np.int32)
+    for t in range(T):
+        # group scores, in float32: the largest score plus (group_topn = 2) the second
+        gscore = np.empty(G, dtype=np.float32)
+        for g in range(G):
+            vals = sorted(z[t, g * gsz:(g + 1) * gsz].tolist(), reverse=True)
+            acc = np.float32(vals[0])
+            if GN == 2:
+                acc = np.float32(acc + np.float32(vals[1]))
+            gscore[g] = acc
+        kept = np.argsort(-gscore, kind="stable")[:TG]          # ties: lower group id first
+        cand = np.sort(np.concatenate([np.arange(g * gsz, (g + 1) * gsz) for g in kept]))
+        order = cand[np.argsort(-z[t, cand], kind="stable")]    # ties: lower expert id first
+        idx[t] = order[:k]
+    zsel = np.take_along_axis(z, idx, axis=1).astype(np.float64)
+    if r["scoring"] == "sigmoid":
+        s = sigmoid(zsel)
+    else:
+        z64 = z.astype(np.float64)
+        e = np.exp(z64 - z64.max(axis=1, keepdims=True))
+        p_all = e / e.sum(axis=1, keepdims=True)
+        s = np.take_along_axis(p_all, idx, axis=1)
+    if r["renormalize"]:
+        s = s / s.sum(axis=1, keepdims=True)
+    w = s * float(r["scale"])
+    return idx, w.astype(np.float32)
+
+
 def init_routing(ids: np.ndarray, E: int, e_base: int = 0) -> dict:
     """Expand-and-sort routing (the first routing of double routing, and re-routing).
 
@@ -295,7 +360,7 @@ def expert_weights_f64(inp: dict):
     return get
 
 
-def moe_layer(inp: dict, logits32_override=None) -> dict:
+def moe_layer(inp: dict, logits32_override=None, router=None) -> dict:
     """The whole layer on one GPU's share, step by step.
 
     Token path ([MND §Expert Parallelism], [R1P §MoE deployment strategy
@@ -306,7 +371,8 @@ def moe_layer(inp: dict, logits32_override=None) -> dict:
     order, and the shared expert on the rank's local tokens.
 
     ``logits32_override`` lets a test route on another float32 logit matrix
-    (the routing policy is exact only given identical float32 logits).
+    (the routing policy is exact only given identical float32 logits); ``router``
+    selects a variant of the router (route_grouped), default the workload's.
     """
     cfg = inp["cfg"]
     fp8 = cfg.wt == "fp8"
@@ -320,7 +386,10 @@ def moe_layer(inp: dict, logits32_override=None) -> dict:
         logits = gate_logits(x, to_f64(inp["w_gate"], cfg.act))
         res["logits"] = logits
         l32 = logits.astype(np.float32) if logits32_override is None else logits32_override
-        idx, w = route_topk(l32, inp.get("bias"), k)
+        if router is None:
+            idx, w = route_topk(l32, inp.get("bias"), k)
+        else:
+            idx, w = route_grouped(l32, inp.get("bias"), k, router)
         res["topk_idx"], res["topk_w"] = idx, w
         ids = idx
     rt = init_routing(ids, cfg.E, cfg.e_base)

@@ -170,6 +170,113 @@ def test_topk_bias_shifts_selection():
     assert np.allclose(w[0], np.array(s) / sum(s), atol=1e-7)
 
 
+# ----------------------------------------------------------------------------- router variants
+
+def test_router_default_is_the_workload_router():
+    """Default router (sigmoid, renormalized, one group) = route_topk bit for bit."""
+    rng = np.random.default_rng(11)
+    z = rng.standard_normal((40, 16)).astype(np.float32)
+    b = rng.standard_normal(16).astype(np.float32) * 0.3
+    for k in (1, 3, 8, 16):
+        i0, w0 = moe.route_topk(z, b, k)
+        i1, w1 = moe.route_grouped(z, b, k)
+        assert np.array_equal(i0, i1) and np.array_equal(w0, w1)
+
+
+@pytest.mark.parametrize("scoring", ["sigmoid", "softmax"])
+def test_router_all_groups_kept_is_ungrouped(scoring):
+    """[MND §MoE Router]: the ungrouped (Mixtral) routing is the special case in which the
+    top-K group is every expert: keeping all G groups selects like one group."""
+    rng = np.random.default_rng(12)
+    z = rng.standard_normal((30, 24)).astype(np.float32)
+    flat = moe.route_grouped(z, None, 5, dict(scoring=scoring))
+    for G, GN in ((4, 1), (6, 2), (24, 1)):
+        grp = moe.route_grouped(z, None, 5, dict(scoring=scoring, n_group=G, topk_group=G, group_topn=GN))
+        assert np.array_equal(flat[0], grp[0]) and np.array_equal(flat[1], grp[1])
+
+
+def _brute_grouped(z, k, G, TG, GN):
+    """Group scores by explicit sorting; the kept groups are the TG-subset whose every
+    member beats every other group (higher score, or equal and lower id); the experts are
+    the brute-force top-k of the kept groups' experts."""
+    E = len(z)
+    gsz = E // G
+    score = []
+    for g in range(G):
+        vals = sorted((np.float32(v) for v in z[g * gsz:(g + 1) * gsz]), reverse=True)
+        score.append(vals[0] if GN == 1 else np.float32(vals[0] + vals[1]))
+    beats = lambda a, b: score[a] > score[b] or (score[a] == score[b] and a < b)
+    kept = [S for S in itertools.combinations(range(G), TG)
+            if all(beats(a, b) for a in S for b in range(G) if b not in S)]
+    assert len(kept) == 1
+    cand = [e for g in kept[0] for e in range(g * gsz, (g + 1) * gsz)]
+    sub = [z[e] for e in cand]
+    return [cand[i] for i in _brute_topk(sub, k)]
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.sampled_from([(4, 2), (6, 3), (6, 2), (8, 4), (8, 2), (9, 3)]), st.data())
+def test_grouped_selection_brute_force(EG, data):
+    E, G = EG
+    gsz = E // G
+    TG = data.draw(st.integers(1, G))
+    GN = data.draw(st.integers(1, min(2, gsz)))
+    k = data.draw(st.integers(1, TG * gsz))
+    vals = data.draw(st.lists(st.sampled_from([-1.5, -0.25, 0.0, 0.25, 0.5, 2.0]), min_size=E, max_size=E))
+    z = np.array([vals], dtype=np.float32)
+    idx, w = moe.route_grouped(z, None, k, dict(n_group=G, topk_group=TG, group_topn=GN))
+    assert list(idx[0]) == _brute_grouped(list(z[0]), k, G, TG, GN)
+    assert abs(float(w.sum()) - 1.0) <= 1e-6
+
+
+def test_group_score_top1_vs_top2():
+    """Groups of 2: [3, -5], [2, 1.9], [0, 0], [1, 0.5].  By the best expert, group 0 wins;
+    by the best two, group 1 (3.9 > 1.5 > 0 > -2)."""
+    z = np.array([[3.0, -5.0, 2.0, 1.9, 0.0, 0.0, 1.0, 0.5]], dtype=np.float32)
+    i1, _ = moe.route_grouped(z, None, 2, dict(n_group=4, topk_group=1, group_topn=1))
+    i2, _ = moe.route_grouped(z, None, 2, dict(n_group=4, topk_group=1, group_topn=2))
+    assert list(i1[0]) == [0, 1] and list(i2[0]) == [2, 3]
+    i3, _ = moe.route_grouped(z, None, 3, dict(n_group=4, topk_group=2, group_topn=2))
+    assert list(i3[0]) == [2, 3, 6]
+
+
+def test_softmax_weights_library_and_closed_form():
+    from scipy.special import softmax
+    rng = np.random.default_rng(13)
+    z = rng.standard_normal((20, 10)).astype(np.float32)
+    # k = E without renormalization: the weights are the softmax over all experts
+    idx, w = moe.route_grouped(z, None, 10, dict(scoring="softmax", renormalize=False))
+    ref = softmax(z.astype(np.float64), axis=1)
+    assert np.allclose(w, np.take_along_axis(ref, idx, axis=1), rtol=0, atol=1e-7)
+    # top-2 renormalized (Mixtral): w0 = 1 / (1 + exp(z1 - z0))
+    idx, w = moe.route_grouped(z, None, 2, dict(scoring="softmax"))
+    z0 = np.take_along_axis(z, idx[:, :1], 1)[:, 0].astype(np.float64)
+    z1 = np.take_along_axis(z, idx[:, 1:2], 1)[:, 0].astype(np.float64)
+    assert np.allclose(w[:, 0], 1.0 / (1.0 + np.exp(z1 - z0)), atol=1e-7)
+    assert np.allclose(w.sum(axis=1), 1.0, atol=1e-6)
+    # without renormalization the selected mass is below 1
+    _, w = moe.route_grouped(z, None, 3, dict(scoring="softmax", renormalize=False))
+    assert (w.sum(axis=1) < 1.0).all()
+
+
+def test_sigmoid_without_renormalization_and_scale():
+    z = np.array([[0.0, math.log(3.0), -5.0, 1.0]], dtype=np.float32)
+    idx, w = moe.route_grouped(z, None, 2, dict(renormalize=False, scale=2.0))
+    assert list(idx[0]) == [1, 3]
+    assert abs(w[0, 0] - 2.0 * 0.75) < 1e-6
+    assert abs(w[0, 1] - 2.0 / (1.0 + math.exp(-1.0))) < 1e-6
+    _, w = moe.route_grouped(z, None, 3, dict(scale=2.5))
+    assert abs(float(w.sum()) - 2.5) < 1e-6
+
+
+def test_router_rejects_bad_grouping():
+    z = np.zeros((1, 8), dtype=np.float32)
+    for r, k in ((dict(n_group=3), 1), (dict(n_group=4, topk_group=5), 1), (dict(n_group=8, group_topn=2), 1),
+                 (dict(n_group=4, topk_group=1), 3), (dict(scoring="tanh"), 1)):
+        with pytest.raises(ValueError):
+            moe.route_grouped(z, None, k, r)
+
+
 # ----------------------------------------------------------------------------- routing
 
 def _brute_routing(ids, E, e_base):
