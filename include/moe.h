@@ -91,6 +91,35 @@ moe_status moe_gate_topk(const moe_shape* s, const void* x, const void* w_gate,
                          const float* bias, float* logits, int32_t* topk_idx,
                          float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Router variants.  [MND §MoE Router]: one router serves every MoE model, the
+ * ungrouped (Mixtral-style) routing being the case in which the top-K group is
+ * every expert.  Experts form n_group groups of E / n_group consecutive ids; a
+ * group's score is the sum of its group_topn largest z (added in fp32); the
+ * topk_group best groups are kept (equal scores -> lower group id); the k best z
+ * of the kept groups' experts are selected (equal z -> lower id).  Weights: the
+ * selected sigmoid(z) (MOE_SCORE_SIGMOID) or softmax(z) over all E experts taken
+ * at the selected (MOE_SCORE_SOFTMAX); divided by their sum if renormalize; times
+ * scale.  z = logit + bias throughout.  A NULL router means {SIGMOID, 1, 1, 1, 1,
+ * 1.0f}, the plain router of moe_gate_topk.  Valid: scoring 0 or 1, renormalize 0
+ * or 1, 1 <= n_group <= 64 dividing E, 1 <= topk_group <= n_group, group_topn 1 or
+ * 2 and at most E / n_group, k <= topk_group * E / n_group, scale finite and > 0;
+ * anything else is MOE_EINVAL.                                                     */
+typedef enum { MOE_SCORE_SIGMOID = 0, MOE_SCORE_SOFTMAX = 1 } moe_scoring;
+typedef struct {
+  int32_t scoring;      /* moe_scoring                                              */
+  int32_t renormalize;  /* 1: the k weights are divided by their sum                */
+  int32_t n_group;      /* expert groups; 1 = no grouping                           */
+  int32_t topk_group;   /* groups kept per token                                    */
+  int32_t group_topn;   /* a group scores the sum of its group_topn best z (1 or 2) */
+  float scale;          /* routed scaling factor applied to the weights             */
+} moe_router;
+
+/* moe_gate_topk with a router variant (NULL router: moe_gate_topk). */
+moe_status moe_gate_topk_ex(const moe_shape* s, const moe_router* router, const void* x,
+                            const void* w_gate, const float* bias, float* logits,
+                            int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
 /* Expand-and-sort routing.  [R1P §MoE deployment strategy optimization]:
  * init-routing expands every token once per chosen expert and sorts the copies
  * by expert, giving expanded_x, tokens_per_expert and expanded_row_idx (the
@@ -192,6 +221,13 @@ moe_status moe_layer(const moe_shape* s, const moe_weights* w, const void* x, vo
 moe_status moe_layer_overlap(const moe_shape* s, const moe_weights* w, const void* x,
                              void* out, int32_t* topk_idx, float* topk_w, float* logits,
                              void* ws, size_t ws_bytes, hipStream_t stream, hipStream_t side);
+
+/* The most general layer call: moe_layer_overlap with a router variant (NULL
+ * router: the plain router; side NULL: one stream). */
+moe_status moe_layer_ex(const moe_shape* s, const moe_router* router, const moe_weights* w,
+                        const void* x, void* out, int32_t* topk_idx, float* topk_w,
+                        float* logits, void* ws, size_t ws_bytes, hipStream_t stream,
+                        hipStream_t side);
 
 /* Launch boundaries at which moe_layer_profiled records events. */
 enum {

@@ -20,10 +20,11 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 
 EXPORTS = [
-    "moe_workspace_bytes", "moe_grouped_ffn_workspace_bytes", "moe_gate_topk", "moe_init_routing",
-    "moe_grouped_ffn", "moe_finalize_routing", "moe_layer", "moe_layer_overlap", "moe_layer_profiled",
-    "moe_get_error", "moe_status_str",
+    "moe_workspace_bytes", "moe_grouped_ffn_workspace_bytes", "moe_gate_topk", "moe_gate_topk_ex",
+    "moe_init_routing", "moe_grouped_ffn", "moe_finalize_routing", "moe_layer", "moe_layer_ex",
+    "moe_layer_overlap", "moe_layer_profiled", "moe_get_error", "moe_status_str",
 ]
+SCORING = {"sigmoid": 0, "softmax": 1}
 EV_NAMES = ["start", "gate", "topk", "route", "expand", "plan", "ffn1", "ffn2", "shared", "finalize"]
 
 
@@ -46,6 +47,16 @@ class moe_weights(ctypes.Structure):
                 ("bias", ctypes.c_void_p)]
 
 
+class moe_router(ctypes.Structure):
+    _fields_ = [("scoring", ctypes.c_int32), ("renormalize", ctypes.c_int32), ("n_group", ctypes.c_int32),
+                ("topk_group", ctypes.c_int32), ("group_topn", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+def router(scoring="sigmoid", renormalize=True, n_group=1, topk_group=1, group_topn=1, scale=1.0) -> moe_router:
+    """A router variant (include/moe.h); the defaults are the plain router."""
+    return moe_router(SCORING[scoring], int(bool(renormalize)), n_group, topk_group, group_topn, scale)
+
+
 _lib = None
 
 
@@ -61,11 +72,14 @@ def lib() -> ctypes.CDLL:
             "moe_workspace_bytes": (SZ, [S]),
             "moe_grouped_ffn_workspace_bytes": (SZ, [S, I32, I32]),
             "moe_gate_topk": (I32, [S, P, P, P, P, P, P, P, SZ, P]),
+            "moe_gate_topk_ex": (I32, [S, ctypes.POINTER(moe_router), P, P, P, P, P, P, P, SZ, P]),
             "moe_init_routing": (I32, [S, P, P, I32, P, P, P, P, P, P, P, SZ, P]),
             "moe_grouped_ffn": (I32, [S, I32, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
             "moe_finalize_routing": (I32, [S, P, P, P, P, P, P]),
             "moe_layer": (I32, [S, ctypes.POINTER(moe_weights), P, P, P, P, P, P, SZ, P]),
             "moe_layer_overlap": (I32, [S, ctypes.POINTER(moe_weights), P, P, P, P, P, P, SZ, P, P]),
+            "moe_layer_ex": (I32, [S, ctypes.POINTER(moe_router), ctypes.POINTER(moe_weights), P, P, P, P, P,
+                                   P, SZ, P, P]),
             "moe_layer_profiled": (I32, [S, ctypes.POINTER(moe_weights), P, P, P, P, P, P, SZ, P, P,
                                          ctypes.POINTER(ctypes.c_void_p), I32]),
             "moe_get_error": (I32, [P, P]),
@@ -130,6 +144,14 @@ def moe_gate_topk(s, x, w_gate, bias, logits, topk_idx, topk_w, ws, stream=None)
                                ws.numel() * ws.element_size(), _stream(stream)), "moe_gate_topk")
 
 
+def moe_gate_topk_ex(s, rt, x, w_gate, bias, logits, topk_idx, topk_w, ws, stream=None):
+    """moe_gate_topk with a router variant `rt` (moe_router or None)."""
+    _check(lib().moe_gate_topk_ex(ctypes.byref(s), None if rt is None else ctypes.byref(rt), _ptr(x),
+                                  _ptr(w_gate), _ptr(bias), _ptr(logits), _ptr(topk_idx), _ptr(topk_w),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_gate_topk_ex")
+
+
 def moe_init_routing(s, x, ids, e_base, expanded_x, expanded_scale, expanded_row_idx, sorted_src,
                      tokens_per_expert, expert_offsets, ws, stream=None):
     _check(lib().moe_init_routing(ctypes.byref(s), _ptr(x), _ptr(ids), int(e_base), _ptr(expanded_x),
@@ -162,6 +184,14 @@ def moe_layer(s, w: moe_weights, x, out, topk_idx, topk_w, logits, ws, stream=No
     _check(lib().moe_layer(ctypes.byref(s), ctypes.byref(w), _ptr(x), _ptr(out), _ptr(topk_idx),
                            _ptr(topk_w), _ptr(logits), _ptr(ws), ws.numel() * ws.element_size(),
                            _stream(stream)), "moe_layer")
+
+
+def moe_layer_ex(s, rt, w: moe_weights, x, out, topk_idx, topk_w, logits, ws, side=None, stream=None):
+    """The general layer call: router variant `rt` (or None) and an optional side stream."""
+    _check(lib().moe_layer_ex(ctypes.byref(s), None if rt is None else ctypes.byref(rt), ctypes.byref(w),
+                              _ptr(x), _ptr(out), _ptr(topk_idx), _ptr(topk_w), _ptr(logits), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(stream),
+                              None if side is None else _stream(side)), "moe_layer_ex")
 
 
 def moe_layer_overlap(s, w: moe_weights, x, out, topk_idx, topk_w, logits, ws, side, stream=None):

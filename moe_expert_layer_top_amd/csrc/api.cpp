@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <climits>
 #include <cstdint>
 
@@ -53,6 +54,30 @@ moe_status check_inter(const moe_shape* s, int I) {
   // weight panels are addressed with 32-bit offsets inside one expert
   if (2LL * I * s->H * elem_bytes(s->wt) >= (1LL << 31)) return MOE_EUNSUPPORTED;
   return MOE_OK;
+}
+
+// Router variant -> kernel arguments; false if it breaks the rules stated in moe.h.
+bool router_args(const moe_shape* s, const moe_router* r, moe::RouterArgs* out) {
+  moe::RouterArgs a;
+  if (r) {
+    if ((r->scoring != MOE_SCORE_SIGMOID && r->scoring != MOE_SCORE_SOFTMAX) ||
+        (r->renormalize != 0 && r->renormalize != 1))
+      return false;
+    if (r->n_group < 1 || r->n_group > 64 || s->E % r->n_group) return false;
+    const int gsz = s->E / r->n_group;
+    if (r->topk_group < 1 || r->topk_group > r->n_group) return false;
+    if ((r->group_topn != 1 && r->group_topn != 2) || r->group_topn > gsz) return false;
+    if (static_cast<long long>(s->k) > static_cast<long long>(r->topk_group) * gsz) return false;
+    if (!(r->scale > 0.0f) || !std::isfinite(r->scale)) return false;
+    a.scoring = r->scoring;
+    a.renormalize = r->renormalize;
+    a.n_group = r->n_group;
+    a.topk_group = r->topk_group;
+    a.group_topn = r->group_topn;
+    a.scale = r->scale;
+  }
+  *out = a;
+  return true;
 }
 
 int nseg_of(long long R) { return static_cast<int>((R + moe::kSegSlots - 1) / moe::kSegSlots); }
@@ -189,7 +214,7 @@ struct Prof {
 // ------------------------------------------------------------------ launch sequences
 moe_status run_gate_topk(const moe_shape* s, const void* x, const void* w_gate, const float* bias,
                          float* logits, int32_t* idx, float* w, float* part, hipStream_t st,
-                         const Prof& prof = Prof()) {
+                         const Prof& prof = Prof(), const moe::RouterArgs& router = moe::RouterArgs()) {
   const GatePlan gp = gate_plan(s);
   hipError_t e;
   if (s->act == MOE_F32) {
@@ -218,7 +243,7 @@ moe_status run_gate_topk(const moe_shape* s, const void* x, const void* w_gate, 
   }
   if (e != hipSuccess || prof.mark(MOE_EV_GATE, st) != hipSuccess) return MOE_EHIP;
   e = moe::launch_topk(part, gp.splits, static_cast<long long>(s->T) * s->E, s->T, s->E, s->k, bias,
-                       logits, idx, w, st);
+                       logits, idx, w, st, router);
   if (e != hipSuccess || prof.mark(MOE_EV_TOPK, st) != hipSuccess) return MOE_EHIP;
   return MOE_OK;
 }
@@ -359,8 +384,18 @@ size_t moe_grouped_ffn_workspace_bytes(const moe_shape* s, int32_t G, int32_t R_
 moe_status moe_gate_topk(const moe_shape* s, const void* x, const void* w_gate, const float* bias,
                          float* logits, int32_t* topk_idx, float* topk_w, void* ws,
                          size_t ws_bytes, hipStream_t stream) {
+  return moe_gate_topk_ex(s, nullptr, x, w_gate, bias, logits, topk_idx, topk_w, ws, ws_bytes,
+                          stream);
+}
+
+moe_status moe_gate_topk_ex(const moe_shape* s, const moe_router* router, const void* x,
+                            const void* w_gate, const float* bias, float* logits,
+                            int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
+  moe::RouterArgs ra;
+  if (!router_args(s, router, &ra)) return MOE_EINVAL;
   if (s->T > 0 && (!x || !w_gate || !logits || !topk_idx || !topk_w)) return MOE_EINVAL;
   if (!ws) return MOE_EINVAL;
   const size_t need = moe_workspace_bytes(s);
@@ -368,7 +403,8 @@ moe_status moe_gate_topk(const moe_shape* s, const void* x, const void* w_gate, 
   if (ws_bytes < need) return MOE_EWORKSPACE;
   if (s->T == 0) return MOE_OK;
   const Layout L = layer_layout(s);
-  return run_gate_topk(s, x, w_gate, bias, logits, topk_idx, topk_w, at<float>(ws, L.part), stream);
+  return run_gate_topk(s, x, w_gate, bias, logits, topk_idx, topk_w, at<float>(ws, L.part), stream,
+                       Prof(), ra);
 }
 
 static moe_status init_routing_impl(const moe_shape* s, const void* x, const int32_t* ids,
@@ -449,12 +485,20 @@ moe_status moe_finalize_routing(const moe_shape* s, const void* y, const void* s
 static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const void* x, void* out,
                              int32_t* topk_idx, float* topk_w, float* logits, void* ws,
                              size_t ws_bytes, hipStream_t stream, const Prof& prof,
-                             hipStream_t side = nullptr);
+                             hipStream_t side = nullptr, const moe_router* router = nullptr);
 
 moe_status moe_layer(const moe_shape* s, const moe_weights* w, const void* x, void* out,
                      int32_t* topk_idx, float* topk_w, float* logits, void* ws, size_t ws_bytes,
                      hipStream_t stream) {
   return layer_impl(s, w, x, out, topk_idx, topk_w, logits, ws, ws_bytes, stream, Prof());
+}
+
+moe_status moe_layer_ex(const moe_shape* s, const moe_router* router, const moe_weights* w,
+                        const void* x, void* out, int32_t* topk_idx, float* topk_w,
+                        float* logits, void* ws, size_t ws_bytes, hipStream_t stream,
+                        hipStream_t side) {
+  return layer_impl(s, w, x, out, topk_idx, topk_w, logits, ws, ws_bytes, stream, Prof(),
+                    side == stream ? nullptr : side, router);
 }
 
 moe_status moe_layer_overlap(const moe_shape* s, const moe_weights* w, const void* x, void* out,
@@ -489,9 +533,11 @@ struct SideFork {
 static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const void* x, void* out,
                              int32_t* topk_idx, float* topk_w, float* logits, void* ws,
                              size_t ws_bytes, hipStream_t stream, const Prof& prof,
-                             hipStream_t side) {
+                             hipStream_t side, const moe_router* router) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
+  moe::RouterArgs ra;
+  if (!router_args(s, router, &ra)) return MOE_EINVAL;
   if ((st = check_inter(s, s->I)) != MOE_OK) return st;
   if (!w || !ws) return MOE_EINVAL;
   const bool fp8 = s->wt == MOE_FP8_E4M3;
@@ -529,7 +575,7 @@ static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const voi
     if (hipEventRecord(sf.join, side) != hipSuccess) return MOE_EHIP;
   }
   // gate + router  ([MND §Expert Parallelism], [MND §MoE Router])
-  st = run_gate_topk(s, x, w->w_gate, w->bias, lg, idx, tw, at<float>(ws, L.part), stream, prof);
+  st = run_gate_topk(s, x, w->w_gate, w->bias, lg, idx, tw, at<float>(ws, L.part), stream, prof, ra);
   if (st != MOE_OK) return st;
   // first routing: expand and sort by expert  ([R1P §MoE deployment strategy optimization]).
   // bf16 layers never materialize the expanded rows: the first expert GEMM reads each

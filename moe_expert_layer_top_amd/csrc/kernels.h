@@ -77,9 +77,20 @@ hipError_t launch_gemm(GemmCfg cfg, Epilogue epi, bool fp8, const GemmArgs& a, i
 hipError_t launch_plan(const int32_t* offsets, int G, int rows_if_null, int extra_rows, int block_m,
                        int cap, Unit* units, int32_t* n_units, hipStream_t st);
 
+// Router variant (the plain router: {0, 1, 1, 1, 1, 1.0f}); validated by the caller.
+struct RouterArgs {
+  int scoring = 0;       // 0 sigmoid, 1 softmax over all experts
+  int renormalize = 1;
+  int n_group = 1;
+  int topk_group = 1;
+  int group_topn = 1;
+  float scale = 1.0f;
+};
+
 hipError_t launch_topk(const float* part, int splits, long long split_stride, int T, int E, int k,
                        const float* bias, float* logits_out, int32_t* idx, float* w,
-                       hipStream_t st);
+                       hipStream_t st,
+                       const RouterArgs& router = RouterArgs());
 
 // counts_ws: [nseg * E] int32, seg_err: [nseg] int32 with nseg = ceil(R / kSegSlots).
 // err_word is overwritten with 1 if any id fell outside [e_base, e_base + E), else 0.

@@ -27,13 +27,16 @@ namespace moe {
 // ceil(E/64) scores; k rounds of a wave-wide (score desc, id asc) arg-max.
 // The gate GEMM may have split the reduction into `splits` partial sums, added
 // here in split order so the float32 logits are reproducible run to run.
+// Router variants ([MND §MoE Router]: the ungrouped routing is the grouped one with
+// every expert in the top-K group): group-limited candidates, softmax weights, no
+// renormalization, a scaling factor.
 template <int VPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ part, int splits,
                                                    long long split_stride, int T, int E, int k,
                                                    const float* __restrict__ bias,
                                                    float* __restrict__ logits_out,
                                                    int32_t* __restrict__ idx_out,
-                                                   float* __restrict__ w_out) {
+                                                   float* __restrict__ w_out, RouterArgs r) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -59,6 +62,80 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
       if (bias) l += bias[e];
     }
     z[v] = l;
+  }
+  // softmax statistics over all E experts, before any candidate is masked
+  float zmax = 0.f, zsum = 1.f;
+  if (r.scoring == 1) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      if (v * 64 + lane < E) m = fmaxf(m, z[v]);
+    zmax = wave_max(m);
+    float sum = 0.f;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      if (v * 64 + lane < E) sum += expf(z[v] - zmax);
+    zsum = wave_sum(sum);
+  }
+  // group-limited candidates: lane g holds group g's score (its best z, plus its second
+  // best when group_topn == 2, added in fp32); the topk_group best groups are kept
+  // (equal scores: lower group id) and the other groups' experts leave the selection
+  if (r.topk_group < r.n_group) {
+    const int gsz = E / r.n_group;
+    float gscore = -INFINITY;
+    for (int g = 0; g < r.n_group; ++g) {
+      float b1 = -INFINITY;
+      int e1 = 0x7fffffff;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const int e = v * 64 + lane;
+        if (e < E && e / gsz == g && (z[v] > b1 || (z[v] == b1 && e < e1))) {
+          b1 = z[v];
+          e1 = e;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ob = __shfl_xor(b1, o, 64);
+        const int oe = __shfl_xor(e1, o, 64);
+        if (ob > b1 || (ob == b1 && oe < e1)) {
+          b1 = ob;
+          e1 = oe;
+        }
+      }
+      float sc = b1;
+      if (r.group_topn == 2) {
+        float b2 = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+          const int e = v * 64 + lane;
+          if (e < E && e / gsz == g && e != e1) b2 = fmaxf(b2, z[v]);
+        }
+        sc = b1 + wave_max(b2);
+      }
+      if (lane == g) gscore = sc;
+    }
+    uint64_t kept = 0;
+    for (int j = 0; j < r.topk_group; ++j) {
+      const bool open = lane < r.n_group && !((kept >> lane) & 1ull);
+      float bz = open ? gscore : -INFINITY;
+      int bg = open ? lane : 0x7fffffff;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float oz = __shfl_xor(bz, o, 64);
+        const int og = __shfl_xor(bg, o, 64);
+        if (oz > bz || (oz == bz && og < bg)) {
+          bz = oz;
+          bg = og;
+        }
+      }
+      kept |= 1ull << bg;
+    }
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int e = v * 64 + lane;
+      if (e < E && !((kept >> (e / gsz)) & 1ull)) z[v] = -INFINITY;
+    }
   }
   float sel_z = 0.f;  // score of the expert this lane records (lanes 0..k-1)
   int sel_e = 0;
@@ -91,25 +168,30 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
     for (int v = 0; v < VPL; ++v)
       if (v * 64 + lane == be) z[v] = -INFINITY;  // remove the winner
   }
-  // sigmoid of the selected scores, renormalized over the k selected experts
-  const float sg = lane < k ? 1.0f / (1.0f + expf(-sel_z)) : 0.0f;
-  const float tot = wave_sum(sg);
+  // sigmoid of the selected scores, or their softmax over all experts; renormalized
+  // over the k selected (the workload's router) or not; times the scaling factor
+  float sg = 0.f;
+  if (lane < k) sg = r.scoring == 1 ? expf(sel_z - zmax) / zsum : 1.0f / (1.0f + expf(-sel_z));
+  const float tot = r.renormalize ? wave_sum(sg) : 1.0f;
   if (lane < k) {
     idx_out[static_cast<long long>(t) * k + lane] = sel_e;
-    w_out[static_cast<long long>(t) * k + lane] = sg / tot;
+    w_out[static_cast<long long>(t) * k + lane] = sg / tot * r.scale;
   }
 }
 
 hipError_t launch_topk(const float* part, int splits, long long split_stride, int T, int E, int k,
                        const float* bias, float* logits_out, int32_t* idx, float* w,
-                       hipStream_t st) {
+                       hipStream_t st, const RouterArgs& router) {
+  if (router.n_group < 1 || router.n_group > 64 || E % router.n_group ||
+      router.topk_group < 1 || router.topk_group > router.n_group)
+    return hipErrorInvalidValue;
   if (T == 0) return hipSuccess;
   const dim3 block(256), grid((T + 3) / 4);
   const int vpl = (E + 63) / 64;
 #define MOE_TOPK_CASE(N)                                                                   \
   case N:                                                                                  \
     topk_kernel<N><<<grid, block, 0, st>>>(part, splits, split_stride, T, E, k, bias,      \
-                                           logits_out, idx, w);                            \
+                                           logits_out, idx, w, router);                            \
     break;
   switch (vpl) {
     MOE_TOPK_CASE(1)
@@ -121,10 +203,10 @@ hipError_t launch_topk(const float* part, int splits, long long split_stride, in
     default:
       if (vpl <= 8) {
         topk_kernel<8><<<grid, block, 0, st>>>(part, splits, split_stride, T, E, k, bias,
-                                               logits_out, idx, w);
+                                               logits_out, idx, w, router);
       } else {
         topk_kernel<16><<<grid, block, 0, st>>>(part, splits, split_stride, T, E, k, bias,
-                                                logits_out, idx, w);
+                                                logits_out, idx, w, router);
       }
   }
 #undef MOE_TOPK_CASE

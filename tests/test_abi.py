@@ -92,3 +92,27 @@ def test_validation_errors_enqueue_nothing(L):
     assert L.moe_layer(ctypes.byref(s), ctypes.byref(w), DUMMY, DUMMY, None, None, None, DUMMY, 1 << 30,
                        None) == M.MOE_EINVAL
     assert L.moe_get_error(None, None) == M.MOE_EINVAL
+
+
+def test_router_validation_enqueues_nothing(L):
+    """Invalid router variants are rejected on the host (MOE_EINVAL) before any launch."""
+    s = M.shape(16, 256, 16, 4, 128, 128)
+    ws_big = 1 << 30
+    bad = [M.router(n_group=3),                       # does not divide E
+           M.router(n_group=4, topk_group=5),         # more groups kept than exist
+           M.router(n_group=16, group_topn=2),        # groups of one expert have no second best
+           M.router(n_group=8, topk_group=1),         # k = 4 > 1 group of 2 experts
+           M.router(n_group=128),                     # above 64 groups
+           M.router(scale=0.0), M.router(scale=float("inf")),
+           M.moe_router(7, 1, 1, 1, 1, 1.0),          # unknown scoring
+           M.moe_router(0, 2, 1, 1, 1, 1.0)]          # renormalize not 0/1
+    for r in bad:
+        assert L.moe_gate_topk_ex(ctypes.byref(s), ctypes.byref(r), DUMMY, DUMMY, None, DUMMY, DUMMY, DUMMY,
+                                  DUMMY, ws_big, None) == M.MOE_EINVAL
+        w = M.moe_weights(DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, None, None, None)
+        assert L.moe_layer_ex(ctypes.byref(s), ctypes.byref(r), ctypes.byref(w), DUMMY, DUMMY, None, None,
+                              None, DUMMY, ws_big, None, None) == M.MOE_EINVAL
+    good = M.router(scoring="softmax", n_group=4, topk_group=2, group_topn=2, scale=2.5)
+    # a valid router reaches the workspace check (still nothing launched)
+    assert L.moe_gate_topk_ex(ctypes.byref(s), ctypes.byref(good), DUMMY, DUMMY, None, DUMMY, DUMMY, DUMMY,
+                              DUMMY, 16, None) == M.MOE_EWORKSPACE
