@@ -16,6 +16,8 @@ Sources (cited by short name throughout):
   deployment" (Perplexity, 2025-04-18).
 * [R1P] page "CANN/cann-recipes-infer: DeepSeek-R1 prefill optimization"
   (DeepSeek-R1 prefill on Atlas A3).
+* [V32] page "NPU DeepSeek-V3.2-Exp inference optimization practice" (W8A8: static
+  per-channel int8 weights, dynamic per-token int8 activations).
 * The workload statement that accompanies them fixes what the pages leave
   open: sigmoid gate scores, top-k renormalized to sum to 1, SwiGLU experts
   with gate/up/down projections.
@@ -128,6 +130,34 @@ def dequant_block128(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
     N, K = q.shape
     v = fp8_e4m3fn_decode(q).reshape(N // QBLOCK, QBLOCK, K // QBLOCK, QBLOCK)
     return (v * scale.astype(np.float64)[:, None, :, None]).reshape(N, K)
+
+
+INT8_MAX = 127.0
+
+
+def quant_per_token_int8(x32: np.ndarray):
+    """Dynamic per-token int8 quantization, the A8 of W8A8 ([V32 §quantization
+    strategy]: activations are quantized per token on the fly, weights per channel
+    offline).  Arithmetic, all float32: amax = max|x| over the row, scale = amax / 127,
+    q = round-half-even(x * (127 / amax)) clipped to [-127, 127]; a row of zeros gets
+    scale 1 and codes 0.  Returns (codes int8 [M, K], scale float32 [M]).
+    """
+    x = np.asarray(x32, dtype=np.float32)
+    amax = np.abs(x).max(axis=1)                                     # float32, exact
+    zero = amax == 0
+    safe = np.where(zero, np.float32(1.0), amax).astype(np.float32)
+    scale = np.where(zero, np.float32(1.0), safe / np.float32(INT8_MAX)).astype(np.float32)
+    inv = (np.float32(INT8_MAX) / safe).astype(np.float32)
+    v = (x * inv[:, None]).astype(np.float32)
+    q = np.clip(np.rint(v), -INT8_MAX, INT8_MAX).astype(np.int8)
+    q[zero] = 0
+    return q, scale
+
+
+def dequant_rows(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """int8 codes with one fp32 scale per row -> float64 (per-token activations, and
+    per-output-channel weights [N, K] with one scale per row N)."""
+    return np.asarray(q, dtype=np.float64) * np.asarray(scale, dtype=np.float64)[:, None]
 
 
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
@@ -283,19 +313,23 @@ def expand_rows(x: np.ndarray, sorted_src: np.ndarray, k: int) -> np.ndarray:
     return x[np.asarray(sorted_src) // k]
 
 
-def swiglu_ffn(a: np.ndarray, w13: np.ndarray, w2: np.ndarray, quant_h: bool = False) -> np.ndarray:
+def swiglu_ffn(a: np.ndarray, w13: np.ndarray, w2: np.ndarray, quant_h=False) -> np.ndarray:
     """One SwiGLU expert: y = (silu(a W1^T) * (a W3^T)) W2^T, float64.
 
     w13 stacks W1 (gate, rows 0..I-1) over W3 (up, rows I..2I-1); w2 is [H, I].
     [MND §Quantization]: the SiLU output is quantized per 1x128 block for the
-    fp8 down projection; ``quant_h`` applies that quantization (float32 values,
-    then :func:`quant_1x128`) before the down projection.
+    fp8 down projection; ``quant_h`` True (or "fp8") applies that quantization
+    (float32 values, then :func:`quant_1x128`) before the down projection, and
+    "int8" the per-token int8 quantization of W8A8 (:func:`quant_per_token_int8`).
     """
     I = w13.shape[0] // 2
     g = a @ w13[:I].T
     u = a @ w13[I:].T
     h = g * sigmoid(g) * u
-    if quant_h:
+    if quant_h == "int8":
+        q, s = quant_per_token_int8(h.astype(np.float32))
+        h = dequant_rows(q, s)
+    elif quant_h:
         q, s = quant_1x128(h.astype(np.float32))
         h = dequant_1x128(q, s)
     return h @ w2.T
@@ -356,6 +390,9 @@ def expert_weights_f64(inp: dict):
         if cfg.wt == "fp8":
             return (dequant_block128(inp["w13"][e], inp["w13_scale"][e]),
                     dequant_block128(inp["w2"][e], inp["w2_scale"][e]))
+        if cfg.wt == "int8":
+            return (dequant_rows(inp["w13"][e], inp["w13_scale"][e]),
+                    dequant_rows(inp["w2"][e], inp["w2_scale"][e]))
         return to_f64(inp["w13"][e], cfg.wt), to_f64(inp["w2"][e], cfg.wt)
     return get
 
@@ -376,6 +413,7 @@ def moe_layer(inp: dict, logits32_override=None, router=None) -> dict:
     """
     cfg = inp["cfg"]
     fp8 = cfg.wt == "fp8"
+    int8 = cfg.wt == "int8"
     x = to_f64(inp["x"], cfg.act)
     res = {}
     if cfg.pretagged:
@@ -400,10 +438,18 @@ def moe_layer(inp: dict, logits32_override=None, router=None) -> dict:
         res["expanded_x"] = expand_rows(xq, rt["sorted_src"], k)
         res["expanded_scale"] = expand_rows(xs, rt["sorted_src"], k)
         a = dequant_1x128(res["expanded_x"], res["expanded_scale"])
+    elif int8:
+        # W8A8 ([V32 §quantization strategy]): each token quantized once, then copied
+        xq, xs = quant_per_token_int8(x.astype(np.float32))
+        res["x_q"], res["x_scale"] = xq, xs
+        res["expanded_x"] = expand_rows(xq, rt["sorted_src"], k)
+        res["expanded_scale"] = expand_rows(xs[:, None], rt["sorted_src"], k)[:, 0]
+        a = dequant_rows(res["expanded_x"], res["expanded_scale"])
     else:
         res["expanded_x"] = expand_rows(inp["x"], rt["sorted_src"], k)
         a = expand_rows(x, rt["sorted_src"], k)
-    y = grouped_ffn(a, rt["expert_offsets"], expert_weights_f64(inp), quant_h=fp8)
+    y = grouped_ffn(a, rt["expert_offsets"], expert_weights_f64(inp),
+                    quant_h="int8" if int8 else fp8)
     res["y_sorted"] = y
     sx = to_f64(inp["x_local"], cfg.act) if cfg.pretagged else x
     s = swiglu_ffn(sx, to_f64(inp["sh_w13"], cfg.act), to_f64(inp["sh_w2"], cfg.act))

@@ -35,7 +35,7 @@ class MoEConfig:
     I: int                   # routed SwiGLU intermediate size
     I_shared: int            # shared-expert intermediate size
     act: str                 # activation dtype: "f32" | "bf16"
-    wt: str                  # expert-weight dtype: "f32" | "bf16" | "fp8"
+    wt: str                  # expert-weight dtype: "f32" | "bf16" | "fp8" | "int8"
     x_std: float = 1.0
     wg_std: Optional[float] = None   # None -> 1/sqrt(H) (logits ~ N(0,1))
     w_std: float = 0.02
@@ -92,6 +92,16 @@ CONFIGS = {
         act="bf16", wt="fp8", zipf_s=1.2, bias_alpha=C5_BIAS_ALPHA,
         description="skewed long prefill, fp8 e4m3 experts with 128x128 scales, "
                     "bf16 activations quantized 1x128 per token"),
+    # ---- W8A8 experts (int8 weights per output channel, int8 activations per token) --
+    "c6_prefill_w8a8": MoEConfig(
+        name="c6_prefill_w8a8", cid=6, T=8192, H=7168, E=256, k=8, I=2048, I_shared=2048,
+        act="bf16", wt="int8",
+        description="the c2 prefill layer with W8A8 experts (static per-channel int8 weights, "
+                    "dynamic per-token int8 activations); bf16 shared expert"),
+    "c7_decode_w8a8": MoEConfig(
+        name="c7_decode_w8a8", cid=7, T=128, H=7168, E=256, k=8, I=2048, I_shared=2048,
+        act="bf16", wt="int8", zipf_s=1.1, bias_alpha=0.5,
+        description="the c4 decode batch with W8A8 experts"),
     # ---- reduced parity workloads -------------------------------------------------
     "p2_prefill_bf16": MoEConfig(
         name="p2_prefill_bf16", cid=12, T=1000, H=512, E=16, k=6, I=256, I_shared=256,
@@ -117,6 +127,14 @@ CONFIGS = {
         name="p5_skewed_fp8", cid=15, T=700, H=512, E=16, k=4, I=256, I_shared=256,
         act="bf16", wt="fp8", zipf_s=1.2, bias_alpha=1.0,
         description="reduced skewed fp8 layer"),
+    "p6_prefill_w8a8": MoEConfig(
+        name="p6_prefill_w8a8", cid=16, T=700, H=512, E=16, k=4, I=256, I_shared=256,
+        act="bf16", wt="int8", zipf_s=1.2, bias_alpha=1.0,
+        description="reduced skewed W8A8 layer (experts split into several units)"),
+    "p7_decode_w8a8": MoEConfig(
+        name="p7_decode_w8a8", cid=17, T=24, H=512, E=64, k=8, I=256, I_shared=256,
+        act="bf16", wt="int8", zipf_s=1.1, bias_alpha=0.5,
+        description="reduced W8A8 decode: many experts with 0-2 rows"),
     "p1_small_fp32": MoEConfig(
         name="p1_small_fp32", cid=11, T=150, H=384, E=12, k=3, I=256, I_shared=128,
         act="f32", wt="f32", x_std=0.02, wg_std=0.02, w_std=0.02,
@@ -124,9 +142,10 @@ CONFIGS = {
 }
 
 FULL_CONFIGS = ["c1_tiny_fp32", "c2_prefill_bf16", "c3_ep_rank_bf16",
-                "c4_decode_bf16", "c5_skewed_fp8"]
+                "c4_decode_bf16", "c5_skewed_fp8", "c6_prefill_w8a8", "c7_decode_w8a8"]
 SMALL_CONFIGS = ["c1_tiny_fp32", "p1_small_fp32", "p2_prefill_bf16", "p2b_prefill_bf16",
-                 "p2c_prefill_bf16", "p3_ep_rank_bf16", "p4_decode_bf16", "p5_skewed_fp8"]
+                 "p2c_prefill_bf16", "p3_ep_rank_bf16", "p4_decode_bf16", "p5_skewed_fp8",
+                 "p6_prefill_w8a8", "p7_decode_w8a8"]
 
 
 def get(name: str, **overrides) -> MoEConfig:

@@ -29,23 +29,27 @@ def upload_small(d: dict, device="cuda") -> dict:
 
 
 def _dtype_of(kind: str):
-    return {"f32": torch.float32, "bf16": torch.int16, "fp8": torch.uint8}[kind]
+    return {"f32": torch.float32, "bf16": torch.int16, "fp8": torch.uint8, "int8": torch.int8}[kind]
 
 
 def upload_experts(cfg: MoEConfig, device="cuda", workers=None) -> dict:
     """Routed expert weights drawn expert by expert on a thread pool and copied into
-    [E, 2I, H] / [E, H, I] device tensors (plus fp8 block scales)."""
+    [E, 2I, H] / [E, H, I] device tensors (plus fp8 block scales or int8 channel scales)."""
     E, I, H = cfg.E, cfg.I, cfg.H
     dt = _dtype_of(cfg.wt)
     out = {"w13": torch.empty((E, 2 * I, H), dtype=dt, device=device),
            "w2": torch.empty((E, H, I), dtype=dt, device=device)}
     fp8 = cfg.wt == "fp8"
+    scaled = cfg.wt in ("fp8", "int8")
     if fp8:
         out["w13_scale"] = torch.empty((E, 2 * I // 128, H // 128), dtype=torch.float32, device=device)
         out["w2_scale"] = torch.empty((E, H // 128, I // 128), dtype=torch.float32, device=device)
+    elif scaled:
+        out["w13_scale"] = torch.empty((E, 2 * I), dtype=torch.float32, device=device)
+        out["w2_scale"] = torch.empty((E, H), dtype=torch.float32, device=device)
     for name, fn in (("w13", inputs.expert_w13), ("w2", inputs.expert_w2)):
         for e, v in inputs.for_each_expert(cfg, fn, workers=workers):
-            if fp8:
+            if scaled:
                 codes, scales = v
                 out[name][e].copy_(torch.from_numpy(codes))
                 out[name + "_scale"][e].copy_(torch.from_numpy(scales))

@@ -17,13 +17,16 @@ Recipe
   e4m3fn codes of the quantile grid scaled so the +-4.2 sigma extreme maps
   below 448, times one fp32 scale per 128x128 block drawn as
   ``std * 4.2 / 448 * 2**U(-0.5, 0.5)``.
+* int8 expert weights (static per-output-channel quantization, the W8 of W8A8):
+  codes round(Phi^-1(u) * 127 / 4.2) of the same 16-bit quantile grid (|code| <= 127),
+  times one fp32 scale per output channel drawn as ``std * 4.2 / 127 * 2**U(-0.5, 0.5)``.
 * Expert-popularity bias (decode / skewed workloads): a seeded permutation ranks
   the experts, p_e is proportional to rank_e**-s, and b_e = alpha * ln p_e.
 * Pretagged rows (expert-parallel rank share): ids i.i.d. uniform over the
   rank's experts [e_base, e_base + E).
 
 bf16 tensors are returned as ``uint16`` bit patterns, fp8 tensors as ``uint8``
-codes, fp32 tensors as ``float32``.
+codes, int8 tensors as ``int8`` codes, fp32 tensors as ``float32``.
 """
 from __future__ import annotations
 
@@ -107,6 +110,23 @@ def normal_fp8_blocks(gen_codes: np.random.Generator, gen_scales: np.random.Gene
     return codes, scales.astype(np.float32).reshape(sshape)
 
 
+@lru_cache(maxsize=None)
+def _int8_table() -> np.ndarray:
+    return np.clip(np.rint(_quantiles16() * (127.0 / _FP8_RANGE_SIGMA)), -127, 127).astype(np.int8)
+
+
+def normal_int8_channels(gen_codes: np.random.Generator, gen_scales: np.random.Generator,
+                         shape, std: float):
+    """int8 codes [..., N, K] and fp32 scales [..., N] (one per output channel)."""
+    *lead, N, K = shape
+    n = int(np.prod(shape))
+    codes = _int8_table()[_u16(gen_codes, n)].reshape(shape)
+    sshape = tuple(lead) + (N,)
+    u = gen_scales.random(int(np.prod(sshape)))
+    scales = (std * _FP8_RANGE_SIGMA / 127.0) * np.exp2(u - 0.5)
+    return codes, scales.astype(np.float32).reshape(sshape)
+
+
 def _normal(cfg: MoEConfig, dtype: str, gen, shape, std):
     if dtype == "f32":
         return normal_f32(gen, shape, std)
@@ -153,18 +173,23 @@ def pretagged_ids(cfg: MoEConfig) -> np.ndarray:
 def expert_w13(cfg: MoEConfig, e: int):
     """Stacked gate (rows 0..I-1) and up (rows I..2I-1) projections [2I, H].
 
-    fp8: returns (codes, scales [2I/128, H/128])."""
+    fp8: returns (codes, scales [2I/128, H/128]); int8: (codes, scales [2I])."""
     shape = (2 * cfg.I, cfg.H)
     if cfg.wt == "fp8":
         return normal_fp8_blocks(stream(cfg, W13, e), stream(cfg, W13S, e), shape, cfg.w_std)
+    if cfg.wt == "int8":
+        return normal_int8_channels(stream(cfg, W13, e), stream(cfg, W13S, e), shape, cfg.w_std)
     return _normal(cfg, cfg.wt, stream(cfg, W13, e), shape, cfg.w_std)
 
 
 def expert_w2(cfg: MoEConfig, e: int):
-    """Down projection [H, I]. fp8: returns (codes, scales [H/128, I/128])."""
+    """Down projection [H, I]. fp8: returns (codes, scales [H/128, I/128]); int8:
+    (codes, scales [H])."""
     shape = (cfg.H, cfg.I)
     if cfg.wt == "fp8":
         return normal_fp8_blocks(stream(cfg, W2, e), stream(cfg, W2S, e), shape, cfg.w_std)
+    if cfg.wt == "int8":
+        return normal_int8_channels(stream(cfg, W2, e), stream(cfg, W2S, e), shape, cfg.w_std)
     return _normal(cfg, cfg.wt, stream(cfg, W2, e), shape, cfg.w_std)
 
 
@@ -210,7 +235,7 @@ def layer_inputs(cfg: MoEConfig, with_experts: bool = True) -> dict:
             w13[e] = v
         for e, v in for_each_expert(cfg, expert_w2):
             w2[e] = v
-        if cfg.wt == "fp8":
+        if cfg.wt in ("fp8", "int8"):
             d["w13"] = np.stack([c for c, _ in w13])
             d["w13_scale"] = np.stack([s for _, s in w13])
             d["w2"] = np.stack([c for c, _ in w2])

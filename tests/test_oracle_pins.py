@@ -456,6 +456,70 @@ def test_fp8_layer_dequantized_operands_close_to_exact():
     assert np.all(np.abs(a - x) <= 2.0 ** -4 * np.abs(x) + 2.0 ** -9 * np.repeat(r["expanded_scale"], 128, 1))
 
 
+def test_int8_quant_amax_maps_to_127_and_zero_row():
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((6, 300)).astype(np.float32)
+    x[3] = 0.0
+    q, s = moe.quant_per_token_int8(x)
+    assert q.dtype == np.int8 and s.dtype == np.float32 and s.shape == (6,)
+    assert s[3] == 1.0 and (q[3] == 0).all()
+    for m in (0, 1, 2, 4, 5):
+        i = int(np.argmax(np.abs(x[m])))
+        assert int(q[m, i]) == (127 if x[m, i] > 0 else -127)
+    assert np.abs(q.astype(np.int32)).max() <= 127
+
+
+def test_int8_quant_round_half_even_closed_form():
+    """amax 127 gives scale 1 and factor 1: the codes are the values rounded half to even."""
+    x = np.array([[127.0, 0.5, 1.5, 2.5, -2.5, -0.49, 3.5]], dtype=np.float32)
+    q, s = moe.quant_per_token_int8(x)
+    assert s[0] == 1.0
+    assert q[0].tolist() == [127, 0, 2, 2, -2, 0, 4]
+
+
+def test_int8_quant_error_bound():
+    """Round to nearest: |q * scale - x| <= scale / 2 (plus float32 rounding of x * inv)."""
+    rng = np.random.default_rng(22)
+    x = (rng.standard_normal((50, 512)) * np.exp(rng.uniform(-8, 8, (50, 1)))).astype(np.float32)
+    q, s = moe.quant_per_token_int8(x)
+    err = np.abs(moe.dequant_rows(q, s) - x.astype(np.float64))
+    assert (err <= s[:, None].astype(np.float64) * (0.5 + 1e-6)).all()
+
+
+def test_int8_gemm_is_integer_product_times_scales():
+    """The identity a W8A8 GEMM relies on: with per-row activation and per-channel weight
+    scales, the dequantized product equals the exact integer product times s_a s_w."""
+    rng = np.random.default_rng(23)
+    qa = rng.integers(-127, 128, (9, 640)).astype(np.int8)
+    qw = rng.integers(-127, 128, (13, 640)).astype(np.int8)
+    sa = rng.uniform(0.001, 0.1, 9).astype(np.float32)
+    sw = rng.uniform(0.001, 0.1, 13).astype(np.float32)
+    deq = moe.dequant_rows(qa, sa) @ moe.dequant_rows(qw, sw).T
+    exact = qa.astype(np.int64) @ qw.astype(np.int64).T          # integers, no rounding
+    assert np.abs(exact).max() < 2 ** 31                             # fits an int32 accumulator
+    assert np.allclose(deq, exact * sa.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :],
+                       rtol=1e-13, atol=0)
+
+
+def test_w8a8_layer_expanded_rows_and_tolerance():
+    """The W8A8 layer's expanded rows are each token's per-token codes, and the layer's
+    output stays within the int8 tolerance of the same layer on unquantized
+    activations (only the activation and h quantizations differ)."""
+    cfg = configs.get("p6_prefill_w8a8")
+    d = inputs.layer_inputs(cfg)
+    r = moe.moe_layer(d)
+    xq, xs = moe.quant_per_token_int8(moe.to_f64(d["x"], cfg.act).astype(np.float32))
+    tok = r["sorted_src"] // cfg.k
+    assert np.array_equal(r["expanded_x"], xq[tok]) and np.array_equal(r["expanded_scale"], xs[tok])
+    # the same layer with exact activations (dequantized int8 weights, no quantization)
+    x = moe.to_f64(d["x"], cfg.act)
+    a = x[tok]
+    y = moe.grouped_ffn(a, r["expert_offsets"], moe.expert_weights_f64(d), quant_h=False)
+    out = moe.finalize(y, r["expanded_row_idx"], cfg.k, r["topk_w"], r["shared"])
+    rel = (np.abs(out - r["out"]).max(axis=1) / np.abs(out).max(axis=1)).max()
+    assert rel < 6e-2, rel
+
+
 def test_gate_logits_is_plain_product():
     rng = np.random.default_rng(10)
     x, wg = rng.standard_normal((3, 4)), rng.standard_normal((5, 4))
