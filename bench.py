@@ -27,7 +27,7 @@ if ROOT not in sys.path:
 
 # MI355X published peaks
 PEAK_HBM_GBS = 8000.0
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "int8": 5000.0, "f32": 157.3}   # int8: TOP/s
 
 METRIC = "MoE-layer tokens/sec on 1 MI355X; % MFMA peak (FFN), % HBM BW (permute)"
 
@@ -59,7 +59,7 @@ def rows_per_expert(batch, qlen, topk, ep, experts):
 
 
 def _bytes(dt):
-    return {"f32": 4, "bf16": 2, "fp8": 1}[dt]
+    return {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}[dt]
 
 
 def account(cfg, tpe) -> dict:
@@ -73,14 +73,15 @@ def account(cfg, tpe) -> dict:
     active = int(np.count_nonzero(tpe))
     ab = _bytes(cfg.act)
     fp8 = cfg.wt == "fp8"
+    i8 = cfg.wt == "int8"                         # W8A8: per-row and per-channel scales
     wb = _bytes(cfg.wt)
-    eb = 1 if fp8 else ab                         # expanded-row bytes
-    hb = 1 if fp8 else ab
-    sc_a = R * (H // 128) * 4 if fp8 else 0       # 1x128 activation scales
-    sc_h = R * (I // 128) * 4 if fp8 else 0
-    sc_w13 = active * (2 * I // 128) * (H // 128) * 4 if fp8 else 0
-    sc_w2 = active * (H // 128) * (I // 128) * 4 if fp8 else 0
-    mfma_dt = "fp8" if fp8 else ("f32" if cfg.act == "f32" else "bf16")
+    eb = 1 if (fp8 or i8) else ab                 # expanded-row bytes
+    hb = 1 if (fp8 or i8) else ab
+    sc_a = R * (H // 128) * 4 if fp8 else R * 4 if i8 else 0
+    sc_h = R * (I // 128) * 4 if fp8 else R * 4 if i8 else 0
+    sc_w13 = active * (2 * I // 128) * (H // 128) * 4 if fp8 else active * 2 * I * 4 if i8 else 0
+    sc_w2 = active * (H // 128) * (I // 128) * 4 if fp8 else active * H * 4 if i8 else 0
+    mfma_dt = "fp8" if fp8 else "int8" if i8 else ("f32" if cfg.act == "f32" else "bf16")
     acc = {
         "gate": dict(flops=gemm_flops(T, H, E), bytes=T * H * ab + E * H * ab + T * E * 4, dt=cfg.act),
         "topk": dict(flops=0, bytes=T * E * 4 + T * E * 4 + T * k * 8, dt=None),
@@ -267,17 +268,17 @@ def cpu_baseline(cfg, target_s=15.0, max_tokens=None):
         experts = sorted(set(idx.reshape(-1).tolist()))
         w13, w2, w13s, w2s = {}, {}, {}, {}
         for e, v in inputs.for_each_expert(cfg, inputs.expert_w13, experts):
-            if cfg.wt == "fp8":
+            if cfg.wt in ("fp8", "int8"):
                 w13[e], w13s[e] = v
             else:
                 w13[e] = v
         for e, v in inputs.for_each_expert(cfg, inputs.expert_w2, experts):
-            if cfg.wt == "fp8":
+            if cfg.wt in ("fp8", "int8"):
                 w2[e], w2s[e] = v
             else:
                 w2[e] = v
         d.update(w13=w13, w2=w2)
-        if cfg.wt == "fp8":
+        if cfg.wt in ("fp8", "int8"):
             d.update(w13_scale=w13s, w2_scale=w2s)
         return d
 
@@ -354,7 +355,7 @@ def main():
     if dk["bound"] == "mfma":
         achieved = acc[dom]["flops"] / (r["stage_ms"][dom] / 1e3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": achieved,
-                "peak": PEAK_TFLOPS[acc[dom]["dt"]], "unit": "TFLOP/s"}
+                "peak": PEAK_TFLOPS[acc[dom]["dt"]], "unit": "TOP/s" if acc[dom]["dt"] == "int8" else "TFLOP/s"}
     else:
         achieved = acc[dom]["bytes"] / (r["stage_ms"][dom] / 1e3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
@@ -380,7 +381,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if cfg.wt == "fp8" else cfg.act,
+        "dtype": cfg.wt if cfg.wt in ("fp8", "int8") else cfg.act,
         "data": "synthetic (seeded; see DESIGN.md input recipe)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
                    "I_shared": cfg.I_shared, "act": cfg.act, "wt": cfg.wt},

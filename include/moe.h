@@ -52,7 +52,7 @@ typedef enum {
   MOE_EDEVICE = -5        /* device-detected bad input (see moe_get_error) */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_INT8 = 3 } moe_dtype;
 
 /* Problem shape of one call.
  *   T        tokens (for re-routing: received rows)
@@ -63,8 +63,12 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
  *   I_shared shared-expert intermediate size (multiple of 128 for bf16/fp8)
  *   act      activation dtype: MOE_F32 or MOE_BF16
  *   wt       expert-weight dtype: MOE_F32 (with act F32), MOE_BF16 (with act
- *            BF16) or MOE_FP8_E4M3 (with act BF16; the expert inputs are then
- *            quantized to fp8 with one fp32 scale per 1x128 vector)           */
+ *            BF16), MOE_FP8_E4M3 (with act BF16; the expert inputs are then
+ *            quantized to fp8 with one fp32 scale per 1x128 vector) or
+ *            MOE_INT8 (with act BF16: W8A8, [V32 §quantization strategy]; int8
+ *            weights with one fp32 scale per output channel, the expert inputs
+ *            and h quantized to int8 with one fp32 scale per row: scale =
+ *            amax/127, code = round-half-even(x * 127/amax))               */
 typedef struct {
   int32_t T, H, E, k, I, I_shared;
   int32_t act, wt;
@@ -129,8 +133,10 @@ moe_status moe_gate_topk_ex(const moe_shape* s, const moe_router* router, const 
  *                                    expanded_x is NULL (routing only)
  *   ids               [T, k] int32   global expert ids; local id = id - e_base
  *   expanded_x        [T*k, H]       OUT or NULL: row r = x[sorted_src[r] / k];
- *                                    act dtype, or fp8 codes when s->wt is fp8
- *   expanded_scale    [T*k, H/128]   OUT fp32 1x128 scales (fp8 only, else NULL)
+ *                                    act dtype, or fp8 / int8 codes when s->wt
+ *                                    is fp8 / int8
+ *   expanded_scale    OUT fp32: [T*k, H/128] 1x128 scales (fp8), [T*k] row
+ *                                    scales (int8), else NULL
  *   expanded_row_idx  [T*k] int32    OUT: slot s = t*k + j -> destination row, -1
  *                                    for an invalid id
  *   sorted_src        [T*k] int32    OUT or NULL: destination row -> slot s
@@ -153,13 +159,13 @@ moe_status moe_init_routing(const moe_shape* s, const void* x, const int32_t* id
  * counts instead of sizing work by the buffer bound).
  *   G              number of groups (experts)
  *   R_max          rows in a and y (>= group_offsets[G], which the kernels read)
- *   a              [R_max, H]  act, or fp8 codes when s->wt is fp8
- *   a_scale        [R_max, H/128] fp32 (fp8 only, else NULL)
+ *   a              [R_max, H]  act, or fp8 / int8 codes when s->wt is fp8 / int8
+ *   a_scale        fp32 [R_max, H/128] (fp8), [R_max] (int8), else NULL
  *   group_offsets  [G+1] int32 device array, non-decreasing, offsets[0] = 0
  *   w13            [G, 2I, H]  wt: rows 0..I-1 = W1 (gate), I..2I-1 = W3 (up)
- *   w13_scale      [G, 2I/128, H/128] fp32 (fp8 only, else NULL)
+ *   w13_scale      fp32 [G, 2I/128, H/128] (fp8), [G, 2I] per channel (int8), else NULL
  *   w2             [G, H, I]   wt
- *   w2_scale       [G, H/128, I/128] fp32 (fp8 only, else NULL)
+ *   w2_scale       fp32 [G, H/128, I/128] (fp8), [G, H] per channel (int8), else NULL
  *   y              [R_max, H]  act  OUT (rows past offsets[G] are not written)
  *   ws             workspace of moe_grouped_ffn_workspace_bytes(s, G, R_max)  */
 moe_status moe_grouped_ffn(const moe_shape* s, int32_t G, int32_t R_max, const void* a,
@@ -190,8 +196,8 @@ typedef struct {
   const void* w2;          /* [E, H, I] wt                                     */
   const void* sh_w13;      /* [2*I_shared, H] act (shared expert, never fp8)   */
   const void* sh_w2;       /* [H, I_shared] act                                */
-  const float* w13_scale;  /* [E, 2I/128, H/128] (fp8 only, else NULL)         */
-  const float* w2_scale;   /* [E, H/128, I/128]  (fp8 only, else NULL)         */
+  const float* w13_scale;  /* fp8 [E, 2I/128, H/128]; int8 [E, 2I]; else NULL  */
+  const float* w2_scale;   /* fp8 [E, H/128, I/128]; int8 [E, H]; else NULL    */
   const float* bias;       /* [E] gate-logit bias or NULL                      */
 } moe_weights;
 

@@ -31,7 +31,7 @@ int elem_bytes(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 2 : 1; }
 
 bool dtypes_ok(const moe_shape* s) {
   if (s->act == MOE_F32) return s->wt == MOE_F32;
-  if (s->act == MOE_BF16) return s->wt == MOE_BF16 || s->wt == MOE_FP8_E4M3;
+  if (s->act == MOE_BF16) return s->wt == MOE_BF16 || s->wt == MOE_FP8_E4M3 || s->wt == MOE_INT8;
   return false;
 }
 
@@ -40,7 +40,8 @@ moe_status check_shape(const moe_shape* s) {
   if (!s) return MOE_EINVAL;
   if (s->T < 0 || s->H <= 0 || s->E < 1 || s->k < 1 || s->k > s->E) return MOE_EINVAL;
   if (s->act != MOE_F32 && s->act != MOE_BF16) return MOE_EUNSUPPORTED;
-  if (s->wt != MOE_F32 && s->wt != MOE_BF16 && s->wt != MOE_FP8_E4M3) return MOE_EUNSUPPORTED;
+  if (s->wt != MOE_F32 && s->wt != MOE_BF16 && s->wt != MOE_FP8_E4M3 && s->wt != MOE_INT8)
+    return MOE_EUNSUPPORTED;
   if (!dtypes_ok(s)) return MOE_EUNSUPPORTED;
   if (s->E > kMaxE || s->k > kMaxK) return MOE_EUNSUPPORTED;
   if (s->act == MOE_F32 ? (s->H % 4) : (s->H % 128)) return MOE_EUNSUPPORTED;
@@ -126,7 +127,7 @@ bool gather_rows(const moe_shape* s) {
 }
 
 struct FfnLayout {
-  size_t units, n_units, h, h_scale, h2, total;
+  size_t units, n_units, h, h_scale, hq, h2, total;
 };
 
 // extra_rows > 0: room for the extra group's units and its intermediate h2 [extra_rows, I].
@@ -148,9 +149,13 @@ FfnLayout ffn_layout(const moe_shape* s, int G, int R_max, int I, int extra_rows
   o += kAlign;
   L.h = o;
   const bool fp8 = s->wt == MOE_FP8_E4M3;
+  const bool i8 = s->wt == MOE_INT8;
   o += align_up(static_cast<size_t>(R_max) * I * (fp8 ? 1 : 2));
   L.h_scale = o;
   if (fp8) o += align_up(static_cast<size_t>(R_max) * (I / 128) * 4);
+  if (i8) o += align_up(static_cast<size_t>(R_max) * 4);   // one scale per row of h
+  L.hq = o;
+  if (i8) o += align_up(static_cast<size_t>(R_max) * I);   // h quantized per row
   L.h2 = o;
   if (extra_rows > 0) o += align_up(static_cast<size_t>(extra_rows) * I * 2);
   L.total = o;
@@ -182,8 +187,10 @@ Layout layer_layout(const moe_shape* s) {
   L.offsets = o;       o += align_up((E + 1) * 4);
   L.eri = o;           o += align_up(R * 4);
   L.sorted_src = o;    o += align_up(R * 4);
-  L.ex = o;            if (!gather_rows(s)) o += align_up(R * H * (fp8 ? 1 : ab));
+  const bool i8 = s->wt == MOE_INT8;
+  L.ex = o;            if (!gather_rows(s)) o += align_up(R * H * (fp8 || i8 ? 1 : ab));
   L.ex_scale = o;      if (fp8) o += align_up(R * (H / 128) * 4);
+                       if (i8) o += align_up(R * 4);
   L.y = o;             o += align_up(R * H * ab);
   const bool merged = merge_shared(s);
   L.ffn = o;           o += ffn_layout(s, s->E, static_cast<int>(R), s->I, merged ? s->T : 0).total;
@@ -279,7 +286,8 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
         static_cast<const float*>(io.w2), at<float>(ws, L.h), static_cast<float*>(io.y), H, I, st));
   }
   const bool fp8 = s->wt == MOE_FP8_E4M3;
-  const int eb = fp8 ? 1 : 2;
+  const bool i8 = s->wt == MOE_INT8;
+  const int eb = (fp8 || i8) ? 1 : 2;
   const moe::GemmCfg cfg = ffn_cfg(G, R_max);
   const int bm = moe::gemm_block_m(cfg, fp8);
   Unit* units = at<Unit>(ws, L.units);
@@ -328,9 +336,26 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
     g1.C2 = at<uint8_t>(ws, L.h2);
     g1.ldc2 = I;
   }
-  hipError_t e = moe::launch_gemm(cfg, fp8 ? moe::EPI_SWIGLU_FP8 : moe::EPI_SWIGLU_BF16, fp8, g1,
-                                  mu, st);
-  if (e != hipSuccess || prof.mark(ev_ffn1, st) != hipSuccess) return MOE_EHIP;
+  if (i8) {
+    // W8A8: per-row activation scales, per-channel weight scales [G, 2I]; h comes out in
+    // bf16 and is quantized per row (its amax spans all I columns, which no single
+    // workgroup holds) before the down projection
+    g1.a_scale_ld = 1;
+    g1.b_scale_group = 2LL * I;
+    g1.b_scale_ld = 1;
+    g1.c_scale = nullptr;
+  }
+  hipError_t e = i8 ? moe::launch_gemm_i8(cfg, moe::EPI_SWIGLU_BF16, g1, mu, st)
+                    : moe::launch_gemm(cfg, fp8 ? moe::EPI_SWIGLU_FP8 : moe::EPI_SWIGLU_BF16, fp8,
+                                       g1, mu, st);
+  if (e != hipSuccess) return MOE_EHIP;
+  if (i8) {
+    e = moe::launch_quant_rows_i8(at<uint8_t>(ws, L.h), R_max, I, 1, nullptr,
+                                  io.offsets ? io.offsets + G : nullptr, at<int8_t>(ws, L.hq),
+                                  at<float>(ws, L.h_scale), st);
+    if (e != hipSuccess) return MOE_EHIP;
+  }
+  if (prof.mark(ev_ffn1, st) != hipSuccess) return MOE_EHIP;
   GemmArgs g2 = g1;
   g2.gather = nullptr;
   g2.gather_div = 1;
@@ -359,7 +384,15 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
     g2.C2 = alt->y;
     g2.ldc2 = H;
   }
-  e = moe::launch_gemm(cfg, moe::EPI_STORE_BF16, fp8, g2, mu, st);
+  if (i8) {
+    g2.A = at<uint8_t>(ws, L.hq);
+    g2.a_scale = at<float>(ws, L.h_scale);
+    g2.a_scale_ld = 1;
+    g2.b_scale_group = H;
+    g2.b_scale_ld = 1;
+  }
+  e = i8 ? moe::launch_gemm_i8(cfg, moe::EPI_STORE_BF16, g2, mu, st)
+         : moe::launch_gemm(cfg, moe::EPI_STORE_BF16, fp8, g2, mu, st);
   if (e != hipSuccess || prof.mark(ev_ffn2, st) != hipSuccess) return MOE_EHIP;
   return MOE_OK;
 }
@@ -431,10 +464,11 @@ static moe_status init_routing_impl(const moe_shape* s, const void* x, const int
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   const bool fp8 = s->wt == MOE_FP8_E4M3;
+  const bool i8 = s->wt == MOE_INT8;
   if (!tokens_per_expert || !expert_offsets || !ws) return MOE_EINVAL;
   if (s->T > 0 && (!ids || !expanded_row_idx)) return MOE_EINVAL;
   if (expanded_x && s->T > 0 && !x) return MOE_EINVAL;
-  if (expanded_x && fp8 && !expanded_scale) return MOE_EINVAL;
+  if (expanded_x && (fp8 || i8) && !expanded_scale) return MOE_EINVAL;
   const size_t need = moe_workspace_bytes(s);
   if (need == 0) return MOE_EINVAL;
   if (ws_bytes < need) return MOE_EWORKSPACE;
@@ -446,8 +480,11 @@ static moe_status init_routing_impl(const moe_shape* s, const void* x, const int
                                      expert_offsets, stream);
   if (e != hipSuccess || prof.mark(MOE_EV_ROUTE, stream) != hipSuccess) return MOE_EHIP;
   if (expanded_x && s->T > 0) {
-    e = moe::launch_expand(x, s->T, s->H, s->k, elem_bytes(s->act), fp8, expanded_row_idx,
-                           expanded_x, expanded_scale, stream);
+    // int8 (W8A8): each token quantized once per row, its codes copied to its k rows
+    e = i8 ? moe::launch_quant_rows_i8(x, s->T, s->H, s->k, expanded_row_idx, nullptr,
+                                       static_cast<int8_t*>(expanded_x), expanded_scale, stream)
+           : moe::launch_expand(x, s->T, s->H, s->k, elem_bytes(s->act), fp8, expanded_row_idx,
+                                expanded_x, expanded_scale, stream);
     if (e != hipSuccess) return MOE_EHIP;
   }
   if (prof.mark(MOE_EV_EXPAND, stream) != hipSuccess) return MOE_EHIP;
@@ -462,10 +499,10 @@ moe_status moe_grouped_ffn(const moe_shape* s, int32_t G, int32_t R_max, const v
   if (st != MOE_OK) return st;
   if ((st = check_inter(s, s->I)) != MOE_OK) return st;
   if (G < 1 || R_max < 0) return MOE_EINVAL;
-  const bool fp8 = s->wt == MOE_FP8_E4M3;
+  const bool scaled = s->wt == MOE_FP8_E4M3 || s->wt == MOE_INT8;
   if (!group_offsets || !ws) return MOE_EINVAL;
   if (R_max > 0 && (!a || !w13 || !w2 || !y)) return MOE_EINVAL;
-  if (fp8 && R_max > 0 && (!a_scale || !w13_scale || !w2_scale)) return MOE_EINVAL;
+  if (scaled && R_max > 0 && (!a_scale || !w13_scale || !w2_scale)) return MOE_EINVAL;
   if (ws_bytes < moe_grouped_ffn_workspace_bytes(s, G, R_max)) return MOE_EWORKSPACE;
   FfnIo io{a, a_scale, group_offsets, w13, w13_scale, w2, w2_scale, y};
   return run_ffn(s, G, R_max, s->I, io, ws, stream);
@@ -543,7 +580,7 @@ static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const voi
   const bool fp8 = s->wt == MOE_FP8_E4M3;
   if (s->T > 0 && (!x || !out || !w->w_gate || !w->w13 || !w->w2 || !w->sh_w13 || !w->sh_w2))
     return MOE_EINVAL;
-  if (fp8 && (!w->w13_scale || !w->w2_scale)) return MOE_EINVAL;
+  if ((fp8 || s->wt == MOE_INT8) && (!w->w13_scale || !w->w2_scale)) return MOE_EINVAL;
   const size_t need = moe_workspace_bytes(s);
   if (need == 0) return MOE_EINVAL;
   if (ws_bytes < need) return MOE_EWORKSPACE;
@@ -585,14 +622,14 @@ static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const voi
   int32_t* ssrc = at<int32_t>(ws, L.sorted_src);
   const bool gathered = gather_rows(s);
   st = init_routing_impl(s, x, idx, 0, gathered ? nullptr : at<void>(ws, L.ex),
-                         fp8 ? at<float>(ws, L.ex_scale) : nullptr, eri, ssrc,
+                         (fp8 || s->wt == MOE_INT8) ? at<float>(ws, L.ex_scale) : nullptr, eri, ssrc,
                          at<int32_t>(ws, L.tpe), offs, ws, ws_bytes, stream, prof);
   if (st != MOE_OK) return st;
   // routed experts as one grouped GEMM over the expert-sorted rows
   // The shared expert runs on every token ([MND §Expert Parallelism]: its output is
   // added); with the routed experts' shape it is one more group of the same launches.
   const int R = s->T * s->k;
-  FfnIo io{at<void>(ws, L.ex), fp8 ? at<float>(ws, L.ex_scale) : nullptr, offs, w->w13,
+  FfnIo io{at<void>(ws, L.ex), (fp8 || s->wt == MOE_INT8) ? at<float>(ws, L.ex_scale) : nullptr, offs, w->w13,
            w->w13_scale, w->w2, w->w2_scale, at<void>(ws, L.y)};
   if (gathered) {
     io.a = x;

@@ -457,13 +457,14 @@ __device__ __forceinline__ int swz(int row) {
   else return (row >> 1) & 3;
 }
 
-template <int WM, int WN, int TM, int TN, int EPI, bool UNIFORM, int ROWB, int NST, bool FP8>
+template <int WM, int WN, int TM, int TN, int EPI, bool UNIFORM, int ROWB, int NST, bool FP8,
+          bool I8 = false>
 __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   constexpr int NT = WM * WN * 64;
   constexpr int NW = NT / 64;
   constexpr int BM = WM * TM * 16;
   constexpr int BN = WN * TN * 16;
-  constexpr int EB = FP8 ? 1 : 2;       // operand element bytes
+  constexpr int EB = (FP8 || I8) ? 1 : 2;   // operand element bytes
   constexpr int KSTEP = ROWB / EB;       // elements per stage
   constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
   constexpr int RPC = 64 / CPR;          // rows per 1 KB DMA (one wave instruction)
@@ -479,6 +480,10 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
                          EPI != EPI_STORE_F32 && !UNIFORM),
                 "fp8 tiles: 2-deep ring of one scale block per stage");
   static_assert(FP8 == (EPI == EPI_SWIGLU_FP8) || EPI == EPI_STORE_BF16, "epilogue matches operands");
+  // I8 (W8A8): int8 codes, exact int32 accumulation, one dequantization in the epilogue
+  // with the activation row's scale and the weight column's scale
+  static_assert(!I8 || (!FP8 && !UNIFORM && (EPI == EPI_SWIGLU_BF16 || EPI == EPI_STORE_BF16)),
+                "int8 operands: grouped launches with a bf16 result");
   static_assert(BM % RPC == 0 && BN % RPC == 0, "tiles are whole DMA chunks");
   static_assert(NST >= 2 && NST <= 4, "ring depth");
   static_assert(!SWIGLU || TN % 2 == 0, "swiglu needs gate/up tile pairs");
@@ -711,11 +716,21 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
 #pragma unroll
       for (int j = 0; j < J; ++j)
 #pragma unroll
-        for (int i = 0; i < TN; ++i)
+        for (int i = 0; i < TN; ++i) {
           // weights as the MFMA's A operand and tokens as its B operand: the result tile is
           // [output column][token], so each lane ends up with 4 consecutive output
           // columns of one token row (stored as one 8- or 16-byte vector)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[i], afr[j], acc[j][i], 0, 0, 0);
+          if constexpr (I8) {
+            // the same 16 bytes per lane hold 16 int8 codes of K: one 16x16x64 MFMA
+            // covers the 64-byte K slice that two bf16 steps would
+            acc[j][i] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, bfr[i]),
+                                                            __builtin_bit_cast(i32x4, afr[j]),
+                                                            __builtin_bit_cast(i32x4, acc[j][i]), 0, 0, 0));
+          } else {
+            acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[i], afr[j], acc[j][i], 0, 0, 0);
+          }
+        }
     }
   };
 
@@ -783,6 +798,42 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   asm volatile("" : "+s"(row0_e), "+s"(ldc_e), "+s"(cptr_e));
   const int crow = lane & 15;
   const int ccol4 = 4 * kgrp;
+  if constexpr (I8) {
+    // W8A8 dequantization: value = acc (exact int32) * s_a[row] * s_w[channel], with the
+    // activation scale of the unit's row and the per-output-channel weight scale
+    constexpr int HT = TN / 2;
+    const float* sw_base = p.b_scale + static_cast<long long>(un.group) * p.b_scale_group;
+    float sa[TM];
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int row = 16 * (j * WM + wm) + crow;
+      sa[j] = (j < jcount && row < rows) ? p.a_scale[row0_e + row] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+      int col, ch;   // first output column of this lane in tile i, and its weight channel
+      if constexpr (EPI == EPI_SWIGLU_BF16) {
+        col = nt * (BN / 2) + wn * (TN * 8) + 16 * (i % HT) + ccol4;
+        ch = (i < HT ? 0 : p.up_off) + col;
+      } else {
+        col = nt * BN + wn * TN * 16 + 16 * i + ccol4;
+        ch = col;
+      }
+      float sw[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sw[r] = col + r < p.N ? sw_base[ch + r] : 0.f;
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        // whole-vector reinterpretation first, then a new float vector: the integer
+        // tile is read once, before any of its lanes is overwritten
+        const i32x4 iv = __builtin_bit_cast(i32x4, acc[j][i]);
+        f32x4 fv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) fv[r] = static_cast<float>(iv[r]) * sa[j] * sw[r];
+        acc[j][i] = fv;
+      }
+    }
+  }
   if constexpr (EPI == EPI_STORE_BF16 || EPI == EPI_STORE_F32) {
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
@@ -903,9 +954,9 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   }
 }
 
-template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST, bool FP8>
+template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST, bool FP8, bool I8 = false>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs p) {
-  gemm_dma_body<WM, WN, TM, TN, EPI, false, ROWB, NST, FP8>(p);
+  gemm_dma_body<WM, WN, TM, TN, EPI, false, ROWB, NST, FP8, I8>(p);
 }
 
 template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST>
@@ -1037,7 +1088,7 @@ hipError_t go(const GemmArgs& a, int max_units, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST, bool FP8 = false>
+template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST, bool FP8 = false, bool I8 = false>
 hipError_t go_dma(const GemmArgs& a, int max_units, hipStream_t st) {
   const long long per_unit = static_cast<long long>(a.n_tiles) * a.splits;
   const long long slots = (static_cast<long long>(max_units) + kXcds - 1) / kXcds;
@@ -1045,14 +1096,14 @@ hipError_t go_dma(const GemmArgs& a, int max_units, hipStream_t st) {
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (a.uniform_rows > 0) {
-    if constexpr (FP8) {
-      return hipErrorInvalidValue;  // fp8 operands come only from the grouped (routed) path
+    if constexpr (FP8 || I8) {
+      return hipErrorInvalidValue;  // quantized operands come only from the grouped (routed) path
     } else {
       dense_gemm_dma_kernel<WM, WN, TM, TN, EPI, ROWB, NST>
           <<<static_cast<unsigned>(blocks), WM * WN * 64, 0, st>>>(a);
     }
   } else {
-    grouped_gemm_dma_kernel<WM, WN, TM, TN, EPI, ROWB, NST, FP8>
+    grouped_gemm_dma_kernel<WM, WN, TM, TN, EPI, ROWB, NST, FP8, I8>
         <<<static_cast<unsigned>(blocks), WM * WN * 64, 0, st>>>(a);
   }
   return hipGetLastError();
@@ -1111,6 +1162,23 @@ hipError_t launch_gemm(GemmCfg cfg, Epilogue epi, bool fp8, const GemmArgs& a, i
       return go_dma<1, 4, 4, 4, EPI_STORE_F32, 128, 3>(a, max_units, st);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_i8(GemmCfg cfg, Epilogue epi, const GemmArgs& a, int max_units,
+                          hipStream_t st) {
+  if (a.uniform_rows > 0 || !a.a_scale || !a.b_scale) return hipErrorInvalidValue;
+  switch (cfg) {
+    case CFG_BIG:
+      if (epi == EPI_SWIGLU_BF16) return go_dma<4, 2, 5, 8, EPI_SWIGLU_BF16, 128, 2, false, true>(a, max_units, st);
+      if (epi == EPI_STORE_BF16) return go_dma<4, 2, 5, 8, EPI_STORE_BF16, 128, 2, false, true>(a, max_units, st);
+      return hipErrorInvalidValue;
+    case CFG_SMALL:
+      if (epi == EPI_SWIGLU_BF16) return go_dma<1, 4, 2, 4, EPI_SWIGLU_BF16, 128, 4, false, true>(a, max_units, st);
+      if (epi == EPI_STORE_BF16) return go_dma<1, 4, 2, 4, EPI_STORE_BF16, 128, 4, false, true>(a, max_units, st);
+      return hipErrorInvalidValue;
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace moe

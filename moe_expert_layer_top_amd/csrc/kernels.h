@@ -23,14 +23,14 @@ enum Epilogue : int {
 struct GemmArgs {
   const uint8_t* A;         // activation rows
   long long lda;            // row pitch in bytes
-  const float* a_scale;     // fp8 only: [rows, K/128]
-  long long a_scale_ld;     // floats per row
+  const float* a_scale;     // fp8: [rows, K/128]; int8: [rows] (one per row)
+  long long a_scale_ld;     // floats per row (fp8)
   const uint8_t* B;         // weights of group 0
   long long ldb;            // row pitch in bytes
   long long b_group;        // bytes between groups
-  const float* b_scale;     // fp8 only: [Brows/128, K/128] per group
+  const float* b_scale;     // fp8: [Brows/128, K/128] per group; int8: [Brows] per group
   long long b_scale_group;  // floats between groups
-  long long b_scale_ld;     // floats per scale row
+  long long b_scale_ld;     // floats per scale row (fp8)
   void* C;                  // output
   long long ldc;            // elements per output row
   long long c_split;        // elements between split-k partial outputs
@@ -61,7 +61,7 @@ struct GemmArgs {
 };
 
 enum GemmCfg : int {
-  CFG_BIG = 0,    // 256 (fp8: 128) x 256 tiles, 8 wavefronts: prefill-sized groups
+  CFG_BIG = 0,    // 320 (fp8: 256) x 256 tiles, 8 wavefronts: prefill-sized groups
   CFG_SMALL = 1,  // 32 x 256 tiles, 4 wavefronts: decode-sized groups
   CFG_GATE = 2,   // 64 x 256 tiles, 4 wavefronts: gate projection
 };
@@ -70,6 +70,10 @@ int gemm_block_m(GemmCfg cfg, bool fp8);
 int gemm_block_n(GemmCfg cfg);
 hipError_t launch_gemm(GemmCfg cfg, Epilogue epi, bool fp8, const GemmArgs& a, int max_units,
                        hipStream_t st);
+// W8A8 grouped GEMM: int8 A and B, per-row a_scale and per-channel b_scale, bf16 result
+// (EPI_SWIGLU_BF16 or EPI_STORE_BF16); the bf16 tiles (gemm_block_m(cfg, false)).
+hipError_t launch_gemm_i8(GemmCfg cfg, Epilogue epi, const GemmArgs& a, int max_units,
+                          hipStream_t st);
 
 // Builds the unit table of a grouped GEMM on the device.  `offsets` [G+1] or, when
 // NULL, one group of `rows_if_null` rows; extra_rows > 0 appends group G of that many
@@ -100,6 +104,12 @@ hipError_t launch_routing(const int32_t* ids, long long R, int e_base, int E, in
 
 hipError_t launch_expand(const void* x, int T, int H, int k, int act_bytes, bool quant_fp8,
                          const int32_t* eri, void* out, float* out_scale, hipStream_t st);
+
+// int8 per-row quantization of bf16 rows (W8A8 activations).  dst_rows [rows * k] or NULL
+// (in place); n_rows: device count of rows that hold data, or NULL (all).
+hipError_t launch_quant_rows_i8(const void* src, int rows, int cols, int k, const int32_t* dst_rows,
+                                const int32_t* n_rows, int8_t* out, float* out_scale,
+                                hipStream_t st);
 
 hipError_t launch_finalize(const void* y, const void* skip, const float* w, const int32_t* eri,
                            void* out, int T, int H, int k, int act_bytes, hipStream_t st);

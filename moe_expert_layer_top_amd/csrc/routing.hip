@@ -467,6 +467,72 @@ __global__ __launch_bounds__(256) void expand_quant_kernel(const uint16_t* __res
   }
 }
 
+// Per-row int8 quantization of bf16 rows (the A8 of W8A8, [V32 §quantization
+// strategy]): one block per row finds the row's amax, then writes codes
+// round-half-even(x * (127 / amax)) with scale amax / 127 (a zero row: scale 1, codes 0),
+// all in float32.  dst_rows [rows * k] sends row r to rows dst_rows[r*k + j] (the
+// token expansion; negative entries are skipped); NULL writes row r in place of itself.
+// n_rows (device, or NULL) bounds the rows that hold data.
+__global__ __launch_bounds__(256) void quant_rows_i8_kernel(const uint16_t* __restrict__ src,
+                                                            int cols, int k,
+                                                            const int32_t* __restrict__ dst_rows,
+                                                            const int32_t* __restrict__ n_rows,
+                                                            int8_t* __restrict__ out,
+                                                            float* __restrict__ out_scale) {
+  __shared__ float wmax[4];
+  const int r = blockIdx.x;
+  if (n_rows && r >= *n_rows) return;
+  const uint16_t* row = src + static_cast<long long>(r) * cols;
+  float amax = 0.f;
+  for (int c = threadIdx.x * 8; c < cols; c += 256 * 8) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(row + c);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[i] << 16)), fabsf(__uint_as_float(w[i] & 0xffff0000u))));
+  }
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const bool zero = amax == 0.f;
+  const float scale = zero ? 1.0f : amax / 127.0f;
+  const float inv = zero ? 0.0f : 127.0f / amax;
+  for (int c = threadIdx.x * 8; c < cols; c += 256 * 8) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(row + c);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t q[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float v = __uint_as_float(i & 1 ? (w[i / 2] & 0xffff0000u) : (w[i / 2] << 16));
+      const float code = fminf(fmaxf(rintf(v * inv), -127.0f), 127.0f);
+      q[i / 4] |= (static_cast<uint32_t>(static_cast<int>(code)) & 0xffu) << (8 * (i % 4));
+    }
+    const uint2 qq = make_uint2(q[0], q[1]);
+    for (int j = 0; j < k; ++j) {
+      const int32_t d = dst_rows ? dst_rows[static_cast<long long>(r) * k + j] : r;
+      if (d < 0) continue;
+      *reinterpret_cast<uint2*>(out + static_cast<long long>(d) * cols + c) = qq;
+    }
+  }
+  if (threadIdx.x == 0) {
+    for (int j = 0; j < k; ++j) {
+      const int32_t d = dst_rows ? dst_rows[static_cast<long long>(r) * k + j] : r;
+      if (d >= 0) out_scale[d] = scale;
+    }
+  }
+}
+
+hipError_t launch_quant_rows_i8(const void* src, int rows, int cols, int k, const int32_t* dst_rows,
+                                const int32_t* n_rows, int8_t* out, float* out_scale,
+                                hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  if (cols % 8) return hipErrorInvalidValue;
+  quant_rows_i8_kernel<<<rows, 256, 0, st>>>(static_cast<const uint16_t*>(src), cols, k, dst_rows,
+                                             n_rows, out, out_scale);
+  return hipGetLastError();
+}
+
 hipError_t launch_expand(const void* x, int T, int H, int k, int act_bytes, bool quant_fp8,
                          const int32_t* eri, void* out, float* out_scale, hipStream_t st) {
   if (T == 0) return hipSuccess;

@@ -63,6 +63,11 @@ def test_workspace_query(L):
     assert M.moe_workspace_bytes(M.shape(8, 128, 4, 2, 128, 128, "f32", "bf16")) == 0
     assert M.moe_workspace_bytes(M.shape(8, 128, 4, 2, 128, 128, "bf16", "fp8")) > 0
     assert M.moe_grouped_ffn_workspace_bytes(c2, 256, 65536) > 65536 * 2048 * 2
+    # W8A8: int8 expanded rows (R x H) and row scales; h staged in bf16 and quantized per row
+    c6 = M.shape(8192, 7168, 256, 8, 2048, 2048, "bf16", "int8")
+    assert M.moe_workspace_bytes(c6) >= 65536 * 7168 * (2 + 1)
+    assert M.moe_grouped_ffn_workspace_bytes(c6, 256, 65536) >= 65536 * 2048 * (2 + 1)
+    assert M.moe_workspace_bytes(M.shape(8, 128, 4, 2, 128, 128, "f32", "int8")) == 0
 
 
 DUMMY = ctypes.c_void_p(4096)   # never dereferenced: validation fails first

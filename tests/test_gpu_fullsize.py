@@ -40,22 +40,23 @@ def sample_tokens(T, seed):
 def expert_dict(cfg, experts):
     w13, w2, s13, s2 = {}, {}, {}, {}
     for e, v in inputs.for_each_expert(cfg, inputs.expert_w13, experts):
-        if cfg.wt == "fp8":
+        if cfg.wt in ("fp8", "int8"):
             w13[e], s13[e] = v
         else:
             w13[e] = v
     for e, v in inputs.for_each_expert(cfg, inputs.expert_w2, experts):
-        if cfg.wt == "fp8":
+        if cfg.wt in ("fp8", "int8"):
             w2[e], s2[e] = v
         else:
             w2[e] = v
     d = {"w13": w13, "w2": w2}
-    if cfg.wt == "fp8":
+    if cfg.wt in ("fp8", "int8"):
         d.update(w13_scale=s13, w2_scale=s2)
     return d
 
 
-@pytest.mark.parametrize("name", ["c1_tiny_fp32", "c2_prefill_bf16", "c4_decode_bf16", "c5_skewed_fp8"])
+@pytest.mark.parametrize("name", ["c1_tiny_fp32", "c2_prefill_bf16", "c4_decode_bf16", "c5_skewed_fp8",
+                                  "c6_prefill_w8a8", "c7_decode_w8a8"])
 def test_full_layer_sampled(M, name):
     cfg = configs.get(name)
     say("full layer", name, "upload")
@@ -82,8 +83,10 @@ def test_full_layer_sampled(M, name):
     say("full layer", name, "routing")
     R = T * k
     fp8 = cfg.wt == "fp8"
-    ex = torch.empty((R, H), dtype=torch.uint8 if fp8 else g["x"].dtype, device="cuda")
-    exs = torch.empty((R, H // 128), dtype=torch.float32, device="cuda") if fp8 else None
+    i8 = cfg.wt == "int8"
+    ex = torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.int8 if i8 else g["x"].dtype, device="cuda")
+    exs = torch.empty((R, H // 128), dtype=torch.float32, device="cuda") if fp8 else \
+        torch.empty(R, dtype=torch.float32, device="cuda") if i8 else None
     eri = torch.empty(R, dtype=torch.int32, device="cuda")
     ssrc = torch.empty(R, dtype=torch.int32, device="cuda")
     tpe = torch.empty(E, dtype=torch.int32, device="cuda")
@@ -102,6 +105,10 @@ def test_full_layer_sampled(M, name):
     rows = rt["expanded_row_idx"].reshape(T, k)[S].reshape(-1)
     if fp8:
         q, sc = O.quant_1x128(O.to_f64(xs, cfg.act).astype(np.float32))
+        assert np.array_equal(host(ex)[rows], np.repeat(q, k, axis=0))
+        assert np.array_equal(host(exs)[rows], np.repeat(sc, k, axis=0))
+    elif i8:
+        q, sc = O.quant_per_token_int8(O.to_f64(xs, cfg.act).astype(np.float32))
         assert np.array_equal(host(ex)[rows], np.repeat(q, k, axis=0))
         assert np.array_equal(host(exs)[rows], np.repeat(sc, k, axis=0))
     else:

@@ -89,12 +89,15 @@ def run_init_routing(M, cfg, g, ids_dev, T, k, E, e_base, with_rows=True):
     s = M.shape(T, cfg.H, E, k, cfg.I, cfg.I_shared, cfg.act, cfg.wt)
     R = T * k
     fp8 = cfg.wt == "fp8"
+    i8 = cfg.wt == "int8"
     ex = None
     exs = None
     if with_rows:
-        ex = poison_(torch.empty((R, cfg.H), dtype=torch.uint8, device="cuda")) if fp8 else \
-            poison_(empty_act((R, cfg.H), cfg.act))
-        exs = poison_(torch.empty((R, cfg.H // 128), dtype=torch.float32, device="cuda")) if fp8 else None
+        if fp8 or i8:
+            ex = poison_(torch.empty((R, cfg.H), dtype=torch.uint8 if fp8 else torch.int8, device="cuda"))
+            exs = poison_(torch.empty((R, cfg.H // 128) if fp8 else (R,), dtype=torch.float32, device="cuda"))
+        else:
+            ex = poison_(empty_act((R, cfg.H), cfg.act))
     eri = poison_(torch.empty(R, dtype=torch.int32, device="cuda"))
     ssrc = poison_(torch.empty(R, dtype=torch.int32, device="cuda"))
     tpe = poison_(torch.empty(E, dtype=torch.int32, device="cuda"))
@@ -122,6 +125,11 @@ def test_init_routing(M, name):
         xq, xs = O.quant_1x128(O.to_f64(d["x"], cfg.act).astype(np.float32))
         assert np.array_equal(host(out["ex"]), O.expand_rows(xq, ref["sorted_src"], k))
         assert np.array_equal(host(out["exs"]), O.expand_rows(xs, ref["sorted_src"], k))
+    elif cfg.wt == "int8":
+        # per-token int8 codes and row scales, bit for bit
+        xq, xs = O.quant_per_token_int8(O.to_f64(d["x"], cfg.act).astype(np.float32))
+        assert np.array_equal(host(out["ex"]), O.expand_rows(xq, ref["sorted_src"], k))
+        assert np.array_equal(host(out["exs"]), xs[ref["sorted_src"] // k])
     else:
         want = O.expand_rows(d["x"], ref["sorted_src"], k)
         got = host(out["ex"])
@@ -142,6 +150,11 @@ def oracle_sorted_inputs(cfg, d):
         a_bytes = O.expand_rows(xq, rt["sorted_src"], k)
         a_scale = O.expand_rows(xs, rt["sorted_src"], k)
         a64 = O.dequant_1x128(a_bytes, a_scale)
+    elif cfg.wt == "int8":
+        xq, xs = O.quant_per_token_int8(O.to_f64(d["x"], cfg.act).astype(np.float32))
+        a_bytes = O.expand_rows(xq, rt["sorted_src"], k)
+        a_scale = np.ascontiguousarray(xs[rt["sorted_src"] // k])
+        a64 = O.dequant_rows(a_bytes, a_scale)
     else:
         a_bytes = O.expand_rows(d["x"], rt["sorted_src"], k)
         a_scale = None
@@ -161,7 +174,8 @@ def test_grouped_ffn(M, name):
     M.moe_grouped_ffn(s, cfg.E, R, to_dev(a_bytes), to_dev(a_scale), to_dev(rt["expert_offsets"]),
                       g["w13"], g.get("w13_scale"), g["w2"], g.get("w2_scale"), y, ws)
     torch.cuda.synchronize()
-    ref = O.grouped_ffn(a64, rt["expert_offsets"], O.expert_weights_f64(d), quant_h=cfg.wt == "fp8")
+    ref = O.grouped_ffn(a64, rt["expert_offsets"], O.expert_weights_f64(d),
+                        quant_h="int8" if cfg.wt == "int8" else cfg.wt == "fp8")
     got = act_to_f64(y, cfg.act)
     assert np.isfinite(got).all()
     err = max_row_rel_err(got, ref)
