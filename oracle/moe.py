@@ -160,6 +160,23 @@ def dequant_rows(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
     return np.asarray(q, dtype=np.float64) * np.asarray(scale, dtype=np.float64)[:, None]
 
 
+def int4_unpack(packed: np.ndarray, K: int) -> np.ndarray:
+    """Packed int4 weights [N, K/2] bytes -> int8 codes [N, K] in [-8, 7].
+
+    Layout (a storage convention of the W4A8 weights): K is cut into groups of 16;
+    byte i (0..7) of a group's 8 bytes holds element i in its low nibble and element
+    8 + i in its high nibble, each a 4-bit two's-complement code.
+    """
+    b = np.asarray(packed, dtype=np.uint8)
+    N = b.shape[0]
+    g = b.reshape(N, K // 16, 8)
+    lo = (g & 0x0F).astype(np.int16)
+    hi = (g >> 4).astype(np.int16)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    return np.concatenate([lo, hi], axis=2).reshape(N, K).astype(np.int8)
+
+
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return bf16_bits_to_f64(a)
@@ -393,6 +410,9 @@ def expert_weights_f64(inp: dict):
         if cfg.wt == "int8":
             return (dequant_rows(inp["w13"][e], inp["w13_scale"][e]),
                     dequant_rows(inp["w2"][e], inp["w2_scale"][e]))
+        if cfg.wt == "int4":
+            return (dequant_rows(int4_unpack(inp["w13"][e], cfg.H), inp["w13_scale"][e]),
+                    dequant_rows(int4_unpack(inp["w2"][e], cfg.I), inp["w2_scale"][e]))
         return to_f64(inp["w13"][e], cfg.wt), to_f64(inp["w2"][e], cfg.wt)
     return get
 
@@ -413,7 +433,7 @@ def moe_layer(inp: dict, logits32_override=None, router=None) -> dict:
     """
     cfg = inp["cfg"]
     fp8 = cfg.wt == "fp8"
-    int8 = cfg.wt == "int8"
+    int8 = cfg.wt in ("int8", "int4")       # W8A8 and W4A8 share the A8 activations
     x = to_f64(inp["x"], cfg.act)
     res = {}
     if cfg.pretagged:

@@ -35,7 +35,7 @@ class MoEConfig:
     I: int                   # routed SwiGLU intermediate size
     I_shared: int            # shared-expert intermediate size
     act: str                 # activation dtype: "f32" | "bf16"
-    wt: str                  # expert-weight dtype: "f32" | "bf16" | "fp8" | "int8"
+    wt: str                  # expert-weight dtype: "f32" | "bf16" | "fp8" | "int8" | "int4"
     x_std: float = 1.0
     wg_std: Optional[float] = None   # None -> 1/sqrt(H) (logits ~ N(0,1))
     w_std: float = 0.02
@@ -102,6 +102,11 @@ CONFIGS = {
         name="c7_decode_w8a8", cid=7, T=128, H=7168, E=256, k=8, I=2048, I_shared=2048,
         act="bf16", wt="int8", zipf_s=1.1, bias_alpha=0.5,
         description="the c4 decode batch with W8A8 experts"),
+    "c8_decode_w4a8": MoEConfig(
+        name="c8_decode_w4a8", cid=8, T=128, H=7168, E=256, k=8, I=2048, I_shared=2048,
+        act="bf16", wt="int4", zipf_s=1.1, bias_alpha=0.5,
+        description="the c4 decode batch with W4A8 experts (packed int4 weights per channel, "
+                    "int8 activations per token)"),
     # ---- reduced parity workloads -------------------------------------------------
     "p2_prefill_bf16": MoEConfig(
         name="p2_prefill_bf16", cid=12, T=1000, H=512, E=16, k=6, I=256, I_shared=256,
@@ -135,6 +140,14 @@ CONFIGS = {
         name="p7_decode_w8a8", cid=17, T=24, H=512, E=64, k=8, I=256, I_shared=256,
         act="bf16", wt="int8", zipf_s=1.1, bias_alpha=0.5,
         description="reduced W8A8 decode: many experts with 0-2 rows"),
+    "p8_prefill_w4a8": MoEConfig(
+        name="p8_prefill_w4a8", cid=18, T=700, H=512, E=16, k=4, I=256, I_shared=256,
+        act="bf16", wt="int4", zipf_s=1.2, bias_alpha=1.0,
+        description="reduced skewed W4A8 layer"),
+    "p9_decode_w4a8": MoEConfig(
+        name="p9_decode_w4a8", cid=19, T=24, H=512, E=64, k=8, I=256, I_shared=256,
+        act="bf16", wt="int4", zipf_s=1.1, bias_alpha=0.5,
+        description="reduced W4A8 decode"),
     "p1_small_fp32": MoEConfig(
         name="p1_small_fp32", cid=11, T=150, H=384, E=12, k=3, I=256, I_shared=128,
         act="f32", wt="f32", x_std=0.02, wg_std=0.02, w_std=0.02,
@@ -142,10 +155,11 @@ CONFIGS = {
 }
 
 FULL_CONFIGS = ["c1_tiny_fp32", "c2_prefill_bf16", "c3_ep_rank_bf16",
-                "c4_decode_bf16", "c5_skewed_fp8", "c6_prefill_w8a8", "c7_decode_w8a8"]
+                "c4_decode_bf16", "c5_skewed_fp8", "c6_prefill_w8a8", "c7_decode_w8a8",
+                "c8_decode_w4a8"]
 SMALL_CONFIGS = ["c1_tiny_fp32", "p1_small_fp32", "p2_prefill_bf16", "p2b_prefill_bf16",
                  "p2c_prefill_bf16", "p3_ep_rank_bf16", "p4_decode_bf16", "p5_skewed_fp8",
-                 "p6_prefill_w8a8", "p7_decode_w8a8"]
+                 "p6_prefill_w8a8", "p7_decode_w8a8", "p8_prefill_w4a8", "p9_decode_w4a8"]
 
 
 def get(name: str, **overrides) -> MoEConfig:

@@ -29,7 +29,8 @@ def upload_small(d: dict, device="cuda") -> dict:
 
 
 def _dtype_of(kind: str):
-    return {"f32": torch.float32, "bf16": torch.int16, "fp8": torch.uint8, "int8": torch.int8}[kind]
+    return {"f32": torch.float32, "bf16": torch.int16, "fp8": torch.uint8, "int8": torch.int8,
+            "int4": torch.uint8}[kind]
 
 
 def upload_experts(cfg: MoEConfig, device="cuda", workers=None) -> dict:
@@ -37,10 +38,11 @@ def upload_experts(cfg: MoEConfig, device="cuda", workers=None) -> dict:
     [E, 2I, H] / [E, H, I] device tensors (plus fp8 block scales or int8 channel scales)."""
     E, I, H = cfg.E, cfg.I, cfg.H
     dt = _dtype_of(cfg.wt)
-    out = {"w13": torch.empty((E, 2 * I, H), dtype=dt, device=device),
-           "w2": torch.empty((E, H, I), dtype=dt, device=device)}
+    pk = 2 if cfg.wt == "int4" else 1                # int4: two codes per byte
+    out = {"w13": torch.empty((E, 2 * I, H // pk), dtype=dt, device=device),
+           "w2": torch.empty((E, H, I // pk), dtype=dt, device=device)}
     fp8 = cfg.wt == "fp8"
-    scaled = cfg.wt in ("fp8", "int8")
+    scaled = cfg.wt in ("fp8", "int8", "int4")
     if fp8:
         out["w13_scale"] = torch.empty((E, 2 * I // 128, H // 128), dtype=torch.float32, device=device)
         out["w2_scale"] = torch.empty((E, H // 128, I // 128), dtype=torch.float32, device=device)

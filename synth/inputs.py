@@ -20,6 +20,10 @@ Recipe
 * int8 expert weights (static per-output-channel quantization, the W8 of W8A8):
   codes round(Phi^-1(u) * 127 / 4.2) of the same 16-bit quantile grid (|code| <= 127),
   times one fp32 scale per output channel drawn as ``std * 4.2 / 127 * 2**U(-0.5, 0.5)``.
+* int4 expert weights (the W4 of W4A8): codes round(Phi^-1(u) * 7 / 4.2) in [-7, 7] of
+  the same grid, packed two per byte (per 16 elements of K: byte i holds element i in
+  its low nibble and element 8 + i in its high nibble), with per-output-channel fp32
+  scales drawn as ``std * 4.2 / 7 * 2**U(-0.5, 0.5)``.
 * Expert-popularity bias (decode / skewed workloads): a seeded permutation ranks
   the experts, p_e is proportional to rank_e**-s, and b_e = alpha * ln p_e.
 * Pretagged rows (expert-parallel rank share): ids i.i.d. uniform over the
@@ -127,6 +131,24 @@ def normal_int8_channels(gen_codes: np.random.Generator, gen_scales: np.random.G
     return codes, scales.astype(np.float32).reshape(sshape)
 
 
+@lru_cache(maxsize=None)
+def _int4_table() -> np.ndarray:
+    return np.clip(np.rint(_quantiles16() * (7.0 / _FP8_RANGE_SIGMA)), -7, 7).astype(np.int8)
+
+
+def normal_int4_channels(gen_codes: np.random.Generator, gen_scales: np.random.Generator,
+                         shape, std: float):
+    """Packed int4 codes [..., N, K/2] (uint8) and fp32 scales [..., N]."""
+    *lead, N, K = shape
+    assert K % 16 == 0
+    n = int(np.prod(shape))
+    codes = _int4_table()[_u16(gen_codes, n)].reshape(-1, K // 16, 2, 8).astype(np.int16) & 0xF
+    packed = (codes[:, :, 0, :] | (codes[:, :, 1, :] << 4)).astype(np.uint8)
+    u = gen_scales.random(int(np.prod(tuple(lead) + (N,))))
+    scales = (std * _FP8_RANGE_SIGMA / 7.0) * np.exp2(u - 0.5)
+    return packed.reshape(tuple(lead) + (N, K // 2)), scales.astype(np.float32).reshape(tuple(lead) + (N,))
+
+
 def _normal(cfg: MoEConfig, dtype: str, gen, shape, std):
     if dtype == "f32":
         return normal_f32(gen, shape, std)
@@ -179,6 +201,8 @@ def expert_w13(cfg: MoEConfig, e: int):
         return normal_fp8_blocks(stream(cfg, W13, e), stream(cfg, W13S, e), shape, cfg.w_std)
     if cfg.wt == "int8":
         return normal_int8_channels(stream(cfg, W13, e), stream(cfg, W13S, e), shape, cfg.w_std)
+    if cfg.wt == "int4":
+        return normal_int4_channels(stream(cfg, W13, e), stream(cfg, W13S, e), shape, cfg.w_std)
     return _normal(cfg, cfg.wt, stream(cfg, W13, e), shape, cfg.w_std)
 
 
@@ -190,6 +214,8 @@ def expert_w2(cfg: MoEConfig, e: int):
         return normal_fp8_blocks(stream(cfg, W2, e), stream(cfg, W2S, e), shape, cfg.w_std)
     if cfg.wt == "int8":
         return normal_int8_channels(stream(cfg, W2, e), stream(cfg, W2S, e), shape, cfg.w_std)
+    if cfg.wt == "int4":
+        return normal_int4_channels(stream(cfg, W2, e), stream(cfg, W2S, e), shape, cfg.w_std)
     return _normal(cfg, cfg.wt, stream(cfg, W2, e), shape, cfg.w_std)
 
 
@@ -235,7 +261,7 @@ def layer_inputs(cfg: MoEConfig, with_experts: bool = True) -> dict:
             w13[e] = v
         for e, v in for_each_expert(cfg, expert_w2):
             w2[e] = v
-        if cfg.wt in ("fp8", "int8"):
+        if cfg.wt in ("fp8", "int8", "int4"):
             d["w13"] = np.stack([c for c, _ in w13])
             d["w13_scale"] = np.stack([s for _, s in w13])
             d["w2"] = np.stack([c for c, _ in w2])

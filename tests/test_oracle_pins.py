@@ -520,6 +520,45 @@ def test_w8a8_layer_expanded_rows_and_tolerance():
     assert rel < 6e-2, rel
 
 
+def test_int4_unpack_closed_form():
+    """Byte i of a group: element i in the low nibble, element 8 + i in the high nibble,
+    both 4-bit two's complement: 0x0F -> (-1, 0), 0x87 -> (7, -8), 0x78 -> (-8, 7)."""
+    packed = np.array([[0x0F, 0x87, 0x78, 0x00, 0x11, 0xF1, 0x1F, 0x88]], dtype=np.uint8)
+    codes = moe.int4_unpack(packed, 16)
+    assert codes[0, :8].tolist() == [-1, 7, -8, 0, 1, 1, -1, -8]
+    assert codes[0, 8:].tolist() == [0, -8, 7, 0, 1, -1, 1, -8]
+
+
+def test_int4_pack_unpack_round_trip():
+    """A packer written with explicit loops, then the oracle's unpack, is the identity."""
+    rng = np.random.default_rng(31)
+    N, K = 5, 64
+    codes = rng.integers(-8, 8, (N, K))
+    packed = np.zeros((N, K // 2), dtype=np.uint8)
+    for n in range(N):
+        for g in range(K // 16):
+            for i in range(8):
+                lo = codes[n, 16 * g + i] & 0xF
+                hi = codes[n, 16 * g + 8 + i] & 0xF
+                packed[n, 8 * g + i] = lo | (hi << 4)
+    assert np.array_equal(moe.int4_unpack(packed, K), codes.astype(np.int8))
+
+
+def test_w4a8_layer_weights_and_tolerance():
+    """The W4A8 workload's weights unpack to symmetric codes in [-7, 7]; its layer stays
+    within the quantized-layer tolerance of the same layer on unquantized activations."""
+    cfg = configs.get("p8_prefill_w4a8")
+    d = inputs.layer_inputs(cfg)
+    c = moe.int4_unpack(d["w13"][0], cfg.H)
+    assert c.shape == (2 * cfg.I, cfg.H) and np.abs(c.astype(np.int32)).max() <= 7
+    r = moe.moe_layer(d)
+    x = moe.to_f64(d["x"], cfg.act)
+    y = moe.grouped_ffn(x[r["sorted_src"] // cfg.k], r["expert_offsets"], moe.expert_weights_f64(d), quant_h=False)
+    out = moe.finalize(y, r["expanded_row_idx"], cfg.k, r["topk_w"], r["shared"])
+    rel = (np.abs(out - r["out"]).max(axis=1) / np.abs(out).max(axis=1)).max()
+    assert rel < 6e-2, rel
+
+
 def test_gate_logits_is_plain_product():
     rng = np.random.default_rng(10)
     x, wg = rng.standard_normal((3, 4)), rng.standard_normal((5, 4))
