@@ -59,7 +59,7 @@ def rows_per_expert(batch, qlen, topk, ep, experts):
 
 
 def _bytes(dt):
-    return {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}[dt]
+    return {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1, "int4": 0.5}[dt]
 
 
 def account(cfg, tpe) -> dict:
@@ -73,7 +73,7 @@ def account(cfg, tpe) -> dict:
     active = int(np.count_nonzero(tpe))
     ab = _bytes(cfg.act)
     fp8 = cfg.wt == "fp8"
-    i8 = cfg.wt == "int8"                         # W8A8: per-row and per-channel scales
+    i8 = cfg.wt in ("int8", "int4")               # W8A8 / W4A8: row and channel scales
     wb = _bytes(cfg.wt)
     eb = 1 if (fp8 or i8) else ab                 # expanded-row bytes
     hb = 1 if (fp8 or i8) else ab
@@ -268,17 +268,17 @@ def cpu_baseline(cfg, target_s=15.0, max_tokens=None):
         experts = sorted(set(idx.reshape(-1).tolist()))
         w13, w2, w13s, w2s = {}, {}, {}, {}
         for e, v in inputs.for_each_expert(cfg, inputs.expert_w13, experts):
-            if cfg.wt in ("fp8", "int8"):
+            if cfg.wt in ("fp8", "int8", "int4"):
                 w13[e], w13s[e] = v
             else:
                 w13[e] = v
         for e, v in inputs.for_each_expert(cfg, inputs.expert_w2, experts):
-            if cfg.wt in ("fp8", "int8"):
+            if cfg.wt in ("fp8", "int8", "int4"):
                 w2[e], w2s[e] = v
             else:
                 w2[e] = v
         d.update(w13=w13, w2=w2)
-        if cfg.wt in ("fp8", "int8"):
+        if cfg.wt in ("fp8", "int8", "int4"):
             d.update(w13_scale=w13s, w2_scale=w2s)
         return d
 
@@ -381,7 +381,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.wt if cfg.wt in ("fp8", "int8") else cfg.act,
+        "dtype": "int8" if cfg.wt == "int4" else cfg.wt if cfg.wt in ("fp8", "int8") else cfg.act,
         "data": "synthetic (seeded; see DESIGN.md input recipe)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
                    "I_shared": cfg.I_shared, "act": cfg.act, "wt": cfg.wt},

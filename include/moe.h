@@ -52,7 +52,7 @@ typedef enum {
   MOE_EDEVICE = -5        /* device-detected bad input (see moe_get_error) */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_INT8 = 3 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_INT8 = 3, MOE_INT4 = 4 } moe_dtype;
 
 /* Problem shape of one call.
  *   T        tokens (for re-routing: received rows)
@@ -68,7 +68,12 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_INT8 = 3 } moe_d
  *            MOE_INT8 (with act BF16: W8A8, [V32 §quantization strategy]; int8
  *            weights with one fp32 scale per output channel, the expert inputs
  *            and h quantized to int8 with one fp32 scale per row: scale =
- *            amax/127, code = round-half-even(x * 127/amax))               */
+ *            amax/127, code = round-half-even(x * 127/amax)) or MOE_INT4
+ *            (with act BF16: W4A8; 4-bit two's-complement weight codes with
+ *            one fp32 scale per output channel, packed two per byte: per 16
+ *            elements of K, byte i holds element i in its low nibble and
+ *            element 8 + i in its high nibble, so a weight row of K codes is
+ *            K/2 bytes; activations as MOE_INT8)                             */
 typedef struct {
   int32_t T, H, E, k, I, I_shared;
   int32_t act, wt;
@@ -134,9 +139,9 @@ moe_status moe_gate_topk_ex(const moe_shape* s, const moe_router* router, const 
  *   ids               [T, k] int32   global expert ids; local id = id - e_base
  *   expanded_x        [T*k, H]       OUT or NULL: row r = x[sorted_src[r] / k];
  *                                    act dtype, or fp8 / int8 codes when s->wt
- *                                    is fp8 / int8
+ *                                    is fp8 / int8 or int4
  *   expanded_scale    OUT fp32: [T*k, H/128] 1x128 scales (fp8), [T*k] row
- *                                    scales (int8), else NULL
+ *                                    scales (int8, int4), else NULL
  *   expanded_row_idx  [T*k] int32    OUT: slot s = t*k + j -> destination row, -1
  *                                    for an invalid id
  *   sorted_src        [T*k] int32    OUT or NULL: destination row -> slot s
@@ -159,13 +164,14 @@ moe_status moe_init_routing(const moe_shape* s, const void* x, const int32_t* id
  * counts instead of sizing work by the buffer bound).
  *   G              number of groups (experts)
  *   R_max          rows in a and y (>= group_offsets[G], which the kernels read)
- *   a              [R_max, H]  act, or fp8 / int8 codes when s->wt is fp8 / int8
+ *   a              [R_max, H]  act, or fp8 / int8 codes when s->wt is fp8 / int8 or int4
  *   a_scale        fp32 [R_max, H/128] (fp8), [R_max] (int8), else NULL
  *   group_offsets  [G+1] int32 device array, non-decreasing, offsets[0] = 0
- *   w13            [G, 2I, H]  wt: rows 0..I-1 = W1 (gate), I..2I-1 = W3 (up)
- *   w13_scale      fp32 [G, 2I/128, H/128] (fp8), [G, 2I] per channel (int8), else NULL
- *   w2             [G, H, I]   wt
- *   w2_scale       fp32 [G, H/128, I/128] (fp8), [G, H] per channel (int8), else NULL
+ *   w13            [G, 2I, H]  wt (int4: [G, 2I, H/2] packed bytes): rows 0..I-1 = W1
+ *                              (gate), I..2I-1 = W3 (up)
+ *   w13_scale      fp32 [G, 2I/128, H/128] (fp8), [G, 2I] per channel (int8, int4), else NULL
+ *   w2             [G, H, I]   wt (int4: [G, H, I/2] packed bytes)
+ *   w2_scale       fp32 [G, H/128, I/128] (fp8), [G, H] per channel (int8, int4), else NULL
  *   y              [R_max, H]  act  OUT (rows past offsets[G] are not written)
  *   ws             workspace of moe_grouped_ffn_workspace_bytes(s, G, R_max)  */
 moe_status moe_grouped_ffn(const moe_shape* s, int32_t G, int32_t R_max, const void* a,
@@ -192,12 +198,12 @@ moe_status moe_finalize_routing(const moe_shape* s, const void* y, const void* s
 /* Weights of one MoE layer. */
 typedef struct {
   const void* w_gate;      /* [E, H] act                                       */
-  const void* w13;         /* [E, 2I, H] wt                                    */
-  const void* w2;          /* [E, H, I] wt                                     */
+  const void* w13;         /* [E, 2I, H] wt (int4: [E, 2I, H/2] packed bytes)  */
+  const void* w2;          /* [E, H, I] wt (int4: [E, H, I/2] packed bytes)    */
   const void* sh_w13;      /* [2*I_shared, H] act (shared expert, never fp8)   */
   const void* sh_w2;       /* [H, I_shared] act                                */
-  const float* w13_scale;  /* fp8 [E, 2I/128, H/128]; int8 [E, 2I]; else NULL  */
-  const float* w2_scale;   /* fp8 [E, H/128, I/128]; int8 [E, H]; else NULL    */
+  const float* w13_scale;  /* fp8 [E, 2I/128, H/128]; int8/int4 [E, 2I]; else NULL */
+  const float* w2_scale;   /* fp8 [E, H/128, I/128]; int8/int4 [E, H]; else NULL   */
   const float* bias;       /* [E] gate-logit bias or NULL                      */
 } moe_weights;
 

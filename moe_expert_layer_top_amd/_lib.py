@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP, MOE_EDEVICE = 0, -1, -2, -3, -4, -5
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
-MOE_INT8 = 3
-DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "int8": MOE_INT8}
+MOE_INT8, MOE_INT4 = 3, 4
+DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "int8": MOE_INT8, "int4": MOE_INT4}
 
 EXPORTS = [
     "moe_workspace_bytes", "moe_grouped_ffn_workspace_bytes", "moe_gate_topk", "moe_gate_topk_ex",

@@ -27,11 +27,15 @@ constexpr int kGateMaxSplits = 64;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-int elem_bytes(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 2 : 1; }
+int elem_bytes(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 2 : 1; }  // int4: 1 (bound)
+
+// int8 activations with per-row scales: W8A8 and W4A8 experts
+bool q8_weights(const moe_shape* s) { return s->wt == MOE_INT8 || s->wt == MOE_INT4; }
 
 bool dtypes_ok(const moe_shape* s) {
   if (s->act == MOE_F32) return s->wt == MOE_F32;
-  if (s->act == MOE_BF16) return s->wt == MOE_BF16 || s->wt == MOE_FP8_E4M3 || s->wt == MOE_INT8;
+  if (s->act == MOE_BF16)
+    return s->wt == MOE_BF16 || s->wt == MOE_FP8_E4M3 || s->wt == MOE_INT8 || s->wt == MOE_INT4;
   return false;
 }
 
@@ -40,7 +44,8 @@ moe_status check_shape(const moe_shape* s) {
   if (!s) return MOE_EINVAL;
   if (s->T < 0 || s->H <= 0 || s->E < 1 || s->k < 1 || s->k > s->E) return MOE_EINVAL;
   if (s->act != MOE_F32 && s->act != MOE_BF16) return MOE_EUNSUPPORTED;
-  if (s->wt != MOE_F32 && s->wt != MOE_BF16 && s->wt != MOE_FP8_E4M3 && s->wt != MOE_INT8)
+  if (s->wt != MOE_F32 && s->wt != MOE_BF16 && s->wt != MOE_FP8_E4M3 && s->wt != MOE_INT8 &&
+      s->wt != MOE_INT4)
     return MOE_EUNSUPPORTED;
   if (!dtypes_ok(s)) return MOE_EUNSUPPORTED;
   if (s->E > kMaxE || s->k > kMaxK) return MOE_EUNSUPPORTED;
@@ -149,7 +154,7 @@ FfnLayout ffn_layout(const moe_shape* s, int G, int R_max, int I, int extra_rows
   o += kAlign;
   L.h = o;
   const bool fp8 = s->wt == MOE_FP8_E4M3;
-  const bool i8 = s->wt == MOE_INT8;
+  const bool i8 = q8_weights(s);
   o += align_up(static_cast<size_t>(R_max) * I * (fp8 ? 1 : 2));
   L.h_scale = o;
   if (fp8) o += align_up(static_cast<size_t>(R_max) * (I / 128) * 4);
@@ -187,7 +192,7 @@ Layout layer_layout(const moe_shape* s) {
   L.offsets = o;       o += align_up((E + 1) * 4);
   L.eri = o;           o += align_up(R * 4);
   L.sorted_src = o;    o += align_up(R * 4);
-  const bool i8 = s->wt == MOE_INT8;
+  const bool i8 = q8_weights(s);
   L.ex = o;            if (!gather_rows(s)) o += align_up(R * H * (fp8 || i8 ? 1 : ab));
   L.ex_scale = o;      if (fp8) o += align_up(R * (H / 128) * 4);
                        if (i8) o += align_up(R * 4);
@@ -286,7 +291,8 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
         static_cast<const float*>(io.w2), at<float>(ws, L.h), static_cast<float*>(io.y), H, I, st));
   }
   const bool fp8 = s->wt == MOE_FP8_E4M3;
-  const bool i8 = s->wt == MOE_INT8;
+  const bool i8 = q8_weights(s);
+  const bool w4 = s->wt == MOE_INT4;
   const int eb = (fp8 || i8) ? 1 : 2;
   const moe::GemmCfg cfg = ffn_cfg(G, R_max);
   const int bm = moe::gemm_block_m(cfg, fp8);
@@ -344,8 +350,12 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
     g1.b_scale_group = 2LL * I;
     g1.b_scale_ld = 1;
     g1.c_scale = nullptr;
+    if (w4) {   // two codes per byte
+      g1.ldb = H / 2;
+      g1.b_group = static_cast<long long>(I) * H;
+    }
   }
-  hipError_t e = i8 ? moe::launch_gemm_i8(cfg, moe::EPI_SWIGLU_BF16, g1, mu, st)
+  hipError_t e = i8 ? moe::launch_gemm_i8(cfg, moe::EPI_SWIGLU_BF16, w4, g1, mu, st)
                     : moe::launch_gemm(cfg, fp8 ? moe::EPI_SWIGLU_FP8 : moe::EPI_SWIGLU_BF16, fp8,
                                        g1, mu, st);
   if (e != hipSuccess) return MOE_EHIP;
@@ -390,8 +400,12 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
     g2.a_scale_ld = 1;
     g2.b_scale_group = H;
     g2.b_scale_ld = 1;
+    if (w4) {
+      g2.ldb = I / 2;
+      g2.b_group = static_cast<long long>(H) * I / 2;
+    }
   }
-  e = i8 ? moe::launch_gemm_i8(cfg, moe::EPI_STORE_BF16, g2, mu, st)
+  e = i8 ? moe::launch_gemm_i8(cfg, moe::EPI_STORE_BF16, w4, g2, mu, st)
          : moe::launch_gemm(cfg, moe::EPI_STORE_BF16, fp8, g2, mu, st);
   if (e != hipSuccess || prof.mark(ev_ffn2, st) != hipSuccess) return MOE_EHIP;
   return MOE_OK;
@@ -464,7 +478,7 @@ static moe_status init_routing_impl(const moe_shape* s, const void* x, const int
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   const bool fp8 = s->wt == MOE_FP8_E4M3;
-  const bool i8 = s->wt == MOE_INT8;
+  const bool i8 = q8_weights(s);
   if (!tokens_per_expert || !expert_offsets || !ws) return MOE_EINVAL;
   if (s->T > 0 && (!ids || !expanded_row_idx)) return MOE_EINVAL;
   if (expanded_x && s->T > 0 && !x) return MOE_EINVAL;
@@ -499,7 +513,7 @@ moe_status moe_grouped_ffn(const moe_shape* s, int32_t G, int32_t R_max, const v
   if (st != MOE_OK) return st;
   if ((st = check_inter(s, s->I)) != MOE_OK) return st;
   if (G < 1 || R_max < 0) return MOE_EINVAL;
-  const bool scaled = s->wt == MOE_FP8_E4M3 || s->wt == MOE_INT8;
+  const bool scaled = s->wt == MOE_FP8_E4M3 || q8_weights(s);
   if (!group_offsets || !ws) return MOE_EINVAL;
   if (R_max > 0 && (!a || !w13 || !w2 || !y)) return MOE_EINVAL;
   if (scaled && R_max > 0 && (!a_scale || !w13_scale || !w2_scale)) return MOE_EINVAL;
@@ -580,7 +594,7 @@ static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const voi
   const bool fp8 = s->wt == MOE_FP8_E4M3;
   if (s->T > 0 && (!x || !out || !w->w_gate || !w->w13 || !w->w2 || !w->sh_w13 || !w->sh_w2))
     return MOE_EINVAL;
-  if ((fp8 || s->wt == MOE_INT8) && (!w->w13_scale || !w->w2_scale)) return MOE_EINVAL;
+  if ((fp8 || q8_weights(s)) && (!w->w13_scale || !w->w2_scale)) return MOE_EINVAL;
   const size_t need = moe_workspace_bytes(s);
   if (need == 0) return MOE_EINVAL;
   if (ws_bytes < need) return MOE_EWORKSPACE;
@@ -622,14 +636,14 @@ static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const voi
   int32_t* ssrc = at<int32_t>(ws, L.sorted_src);
   const bool gathered = gather_rows(s);
   st = init_routing_impl(s, x, idx, 0, gathered ? nullptr : at<void>(ws, L.ex),
-                         (fp8 || s->wt == MOE_INT8) ? at<float>(ws, L.ex_scale) : nullptr, eri, ssrc,
+                         (fp8 || q8_weights(s)) ? at<float>(ws, L.ex_scale) : nullptr, eri, ssrc,
                          at<int32_t>(ws, L.tpe), offs, ws, ws_bytes, stream, prof);
   if (st != MOE_OK) return st;
   // routed experts as one grouped GEMM over the expert-sorted rows
   // The shared expert runs on every token ([MND §Expert Parallelism]: its output is
   // added); with the routed experts' shape it is one more group of the same launches.
   const int R = s->T * s->k;
-  FfnIo io{at<void>(ws, L.ex), (fp8 || s->wt == MOE_INT8) ? at<float>(ws, L.ex_scale) : nullptr, offs, w->w13,
+  FfnIo io{at<void>(ws, L.ex), (fp8 || q8_weights(s)) ? at<float>(ws, L.ex_scale) : nullptr, offs, w->w13,
            w->w13_scale, w->w2, w->w2_scale, at<void>(ws, L.y)};
   if (gathered) {
     io.a = x;

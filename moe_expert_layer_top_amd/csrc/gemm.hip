@@ -451,6 +451,18 @@ __device__ __forceinline__ void dma4(const void* g, uint8_t* lds_chunk) {
                : "memory", "m0");
 }
 
+// 16 packed int4 codes (8 bytes: per byte, element i low nibble, element 8 + i high
+// nibble) -> 16 int8 codes in element order.  Sign extension of each nibble n, per byte
+// without carries between bytes: ((n ^ 8) + 0x78) ^ 0x80.
+__device__ __forceinline__ i32x4 unpack_int4x16(uint2 pk) {
+  constexpr uint32_t kLo = 0x0F0F0F0Fu;
+  const uint32_t v[4] = {pk.x & kLo, pk.y & kLo, (pk.x >> 4) & kLo, (pk.y >> 4) & kLo};
+  i32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = static_cast<int>(((v[i] ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u);
+  return r;
+}
+
 template <int ROWB>
 __device__ __forceinline__ int swz(int row) {
   if constexpr (ROWB == 128) return row & 7;
@@ -458,21 +470,27 @@ __device__ __forceinline__ int swz(int row) {
 }
 
 template <int WM, int WN, int TM, int TN, int EPI, bool UNIFORM, int ROWB, int NST, bool FP8,
-          bool I8 = false>
+          bool I8 = false, bool W4 = false>
 __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   constexpr int NT = WM * WN * 64;
   constexpr int NW = NT / 64;
   constexpr int BM = WM * TM * 16;
   constexpr int BN = WN * TN * 16;
-  constexpr int EB = (FP8 || I8) ? 1 : 2;   // operand element bytes
+  // Q8: int8 activations and exact int32 accumulation (W8A8, and W4A8 whose packed int4
+  // weights are unpacked to int8 codes after LDS)
+  constexpr bool Q8 = I8 || W4;
+  constexpr int EB = (FP8 || Q8) ? 1 : 2;   // activation element bytes
   constexpr int KSTEP = ROWB / EB;       // elements per stage
-  constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
+  constexpr int CPR = ROWB / 16;         // 16-byte chunks per activation row
   constexpr int RPC = 64 / CPR;          // rows per 1 KB DMA (one wave instruction)
-  constexpr int A_LD = BM / RPC, B_LD = BN / RPC;
+  constexpr int ROWB_B = W4 ? ROWB / 2 : ROWB;   // weight bytes per row and stage
+  constexpr int CPR_B = ROWB_B / 16;
+  constexpr int RPC_B = 64 / CPR_B;
+  constexpr int A_LD = BM / RPC, B_LD = BN / RPC_B;
   constexpr int LD_ALL = A_LD + B_LD;
   constexpr int LMAX = (LD_ALL + NW - 1) / NW;   // DMA instructions per wave per stage
   constexpr int LREM = LD_ALL % NW;              // waves < LREM issue LMAX, others LMAX-1
-  constexpr int STAGE = (BM + BN) * ROWB;
+  constexpr int STAGE = BM * ROWB + BN * ROWB_B;
   constexpr bool SWIGLU = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_FP8);
   // fp8: one stage = one 128-wide K block of e4m3 codes; its 1x128 activation scales and
   // the two 128x128 weight-block scales of the tile come into LDS with the stage.
@@ -482,9 +500,10 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   static_assert(FP8 == (EPI == EPI_SWIGLU_FP8) || EPI == EPI_STORE_BF16, "epilogue matches operands");
   // I8 (W8A8): int8 codes, exact int32 accumulation, one dequantization in the epilogue
   // with the activation row's scale and the weight column's scale
-  static_assert(!I8 || (!FP8 && !UNIFORM && (EPI == EPI_SWIGLU_BF16 || EPI == EPI_STORE_BF16)),
+  static_assert(!Q8 || (!FP8 && !UNIFORM && (EPI == EPI_SWIGLU_BF16 || EPI == EPI_STORE_BF16)),
                 "int8 operands: grouped launches with a bf16 result");
-  static_assert(BM % RPC == 0 && BN % RPC == 0, "tiles are whole DMA chunks");
+  static_assert(!W4 || ROWB == 128, "int4 weights: 64-byte weight rows per stage");
+  static_assert(BM % RPC == 0 && BN % RPC_B == 0, "tiles are whole DMA chunks");
   static_assert(NST >= 2 && NST <= 4, "ring depth");
   static_assert(!SWIGLU || TN % 2 == 0, "swiglu needs gate/up tile pairs");
 
@@ -542,7 +561,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
                           (gather ? 0LL : static_cast<long long>(un.row0) * lda) +
                           static_cast<long long>(k0) * EB;
   const uint8_t* b_base = (alt ? p.B2 : p.B + static_cast<long long>(un.group) * p.b_group) +
-                          static_cast<long long>(k0) * EB;
+                          static_cast<long long>(k0) * EB / (W4 ? 2 : 1);
   void* const cptr = alt ? p.C2 : p.C;
   const long long ldc = alt ? p.ldc2 : p.ldc;
 
@@ -565,9 +584,11 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
     const long long src = gather ? gather[un.row0 + rc] / p.gather_div : rc;
     goff[i] = static_cast<uint32_t>(src * lda + ((lphys ^ swz<ROWB>(r)) << 4));
   }
+  const int lrow_b = lane / CPR_B;
+  const int lphys_b = lane % CPR_B;
 #pragma unroll
   for (int i = 0; i < B_PER; ++i) {
-    const int j = (wave + i * NW) * RPC + lrow;
+    const int j = (wave + i * NW) * RPC_B + lrow_b;
     int col, grow;
     if constexpr (SWIGLU) {
       constexpr int WCOLS = TN * 16, HALF = TN * 8;
@@ -579,7 +600,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
       grow = col;
     }
     if (col >= p.N) grow -= col - (p.N - 1);
-    goff[A_PER + i] = static_cast<uint32_t>(static_cast<long long>(grow) * p.ldb + ((lphys ^ swz<ROWB>(j)) << 4));
+    goff[A_PER + i] = static_cast<uint32_t>(static_cast<long long>(grow) * p.ldb + ((lphys_b ^ swz<ROWB_B>(j)) << 4));
   }
 
   // fp8 scale sources of this lane: wavefronts 0 .. BM/64-1 fetch the activation
@@ -622,7 +643,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   auto issue = [&](int step, uint8_t* buf, int b) __attribute__((always_inline)) {
     const long long kb = static_cast<long long>(step) * ROWB;
     const uint8_t* ak = a_base + kb;   // wave-uniform bases of this K step
-    const uint8_t* bk = b_base + kb;
+    const uint8_t* bk = b_base + static_cast<long long>(step) * ROWB_B;
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) dma16s(ak, lane_off_of(i), buf + (wave + i * NW) * 1024);
 #pragma unroll
@@ -707,9 +728,20 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
       const int o = lane_off(kk * 4 + kgrp);
       bf16x8 bfr[TN];
       bf16x8 afr[J > 0 ? J : 1];
+      if constexpr (W4) {
+        // this lane's 16 elements of K are the 8 bytes at byte kk*32 + kgrp*8 of the
+        // 64-byte weight row (16-byte chunk kk*2 + kgrp/2, swizzled like the DMA wrote it)
+        const int ob = frag_row * ROWB_B + (((kk * 2 + (kgrp >> 1)) ^ swz<ROWB_B>(frag_row)) << 4) +
+                       (kgrp & 1) * 8;
 #pragma unroll
-      for (int i = 0; i < TN; ++i)
-        bfr[i] = *reinterpret_cast<const bf16x8*>(lb + (wn * TN + i) * 16 * ROWB + o);
+        for (int i = 0; i < TN; ++i)
+          bfr[i] = __builtin_bit_cast(
+              bf16x8, unpack_int4x16(*reinterpret_cast<const uint2*>(lb + (wn * TN + i) * 16 * ROWB_B + ob)));
+      } else {
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+          bfr[i] = *reinterpret_cast<const bf16x8*>(lb + (wn * TN + i) * 16 * ROWB + o);
+      }
 #pragma unroll
       for (int j = 0; j < J; ++j)
         afr[j] = *reinterpret_cast<const bf16x8*>(buf + (j * WM + wm) * 16 * ROWB + o);
@@ -720,7 +752,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
           // weights as the MFMA's A operand and tokens as its B operand: the result tile is
           // [output column][token], so each lane ends up with 4 consecutive output
           // columns of one token row (stored as one 8- or 16-byte vector)
-          if constexpr (I8) {
+          if constexpr (Q8) {
             // the same 16 bytes per lane hold 16 int8 codes of K: one 16x16x64 MFMA
             // covers the 64-byte K slice that two bf16 steps would
             acc[j][i] = __builtin_bit_cast(
@@ -798,8 +830,8 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   asm volatile("" : "+s"(row0_e), "+s"(ldc_e), "+s"(cptr_e));
   const int crow = lane & 15;
   const int ccol4 = 4 * kgrp;
-  if constexpr (I8) {
-    // W8A8 dequantization: value = acc (exact int32) * s_a[row] * s_w[channel], with the
+  if constexpr (Q8) {
+    // W8A8 / W4A8 dequantization: value = acc (exact int32) * s_a[row] * s_w[channel], with the
     // activation scale of the unit's row and the per-output-channel weight scale
     constexpr int HT = TN / 2;
     const float* sw_base = p.b_scale + static_cast<long long>(un.group) * p.b_scale_group;
@@ -954,9 +986,10 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   }
 }
 
-template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST, bool FP8, bool I8 = false>
+template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST, bool FP8, bool I8 = false,
+          bool W4 = false>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma_kernel(GemmArgs p) {
-  gemm_dma_body<WM, WN, TM, TN, EPI, false, ROWB, NST, FP8, I8>(p);
+  gemm_dma_body<WM, WN, TM, TN, EPI, false, ROWB, NST, FP8, I8, W4>(p);
 }
 
 template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST>
@@ -1088,7 +1121,8 @@ hipError_t go(const GemmArgs& a, int max_units, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST, bool FP8 = false, bool I8 = false>
+template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST, bool FP8 = false, bool I8 = false,
+          bool W4 = false>
 hipError_t go_dma(const GemmArgs& a, int max_units, hipStream_t st) {
   const long long per_unit = static_cast<long long>(a.n_tiles) * a.splits;
   const long long slots = (static_cast<long long>(max_units) + kXcds - 1) / kXcds;
@@ -1096,14 +1130,14 @@ hipError_t go_dma(const GemmArgs& a, int max_units, hipStream_t st) {
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (a.uniform_rows > 0) {
-    if constexpr (FP8 || I8) {
+    if constexpr (FP8 || I8 || W4) {
       return hipErrorInvalidValue;  // quantized operands come only from the grouped (routed) path
     } else {
       dense_gemm_dma_kernel<WM, WN, TM, TN, EPI, ROWB, NST>
           <<<static_cast<unsigned>(blocks), WM * WN * 64, 0, st>>>(a);
     }
   } else {
-    grouped_gemm_dma_kernel<WM, WN, TM, TN, EPI, ROWB, NST, FP8, I8>
+    grouped_gemm_dma_kernel<WM, WN, TM, TN, EPI, ROWB, NST, FP8, I8, W4>
         <<<static_cast<unsigned>(blocks), WM * WN * 64, 0, st>>>(a);
   }
   return hipGetLastError();
@@ -1164,18 +1198,26 @@ hipError_t launch_gemm(GemmCfg cfg, Epilogue epi, bool fp8, const GemmArgs& a, i
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm_i8(GemmCfg cfg, Epilogue epi, const GemmArgs& a, int max_units,
+hipError_t launch_gemm_i8(GemmCfg cfg, Epilogue epi, bool w4, const GemmArgs& a, int max_units,
                           hipStream_t st) {
   if (a.uniform_rows > 0 || !a.a_scale || !a.b_scale) return hipErrorInvalidValue;
+  if (epi != EPI_SWIGLU_BF16 && epi != EPI_STORE_BF16) return hipErrorInvalidValue;
+  const bool sw = epi == EPI_SWIGLU_BF16;
   switch (cfg) {
     case CFG_BIG:
-      if (epi == EPI_SWIGLU_BF16) return go_dma<4, 2, 5, 8, EPI_SWIGLU_BF16, 128, 2, false, true>(a, max_units, st);
-      if (epi == EPI_STORE_BF16) return go_dma<4, 2, 5, 8, EPI_STORE_BF16, 128, 2, false, true>(a, max_units, st);
-      return hipErrorInvalidValue;
+      if (w4) {
+        return sw ? go_dma<4, 2, 5, 8, EPI_SWIGLU_BF16, 128, 2, false, false, true>(a, max_units, st)
+                  : go_dma<4, 2, 5, 8, EPI_STORE_BF16, 128, 2, false, false, true>(a, max_units, st);
+      }
+      return sw ? go_dma<4, 2, 5, 8, EPI_SWIGLU_BF16, 128, 2, false, true>(a, max_units, st)
+                : go_dma<4, 2, 5, 8, EPI_STORE_BF16, 128, 2, false, true>(a, max_units, st);
     case CFG_SMALL:
-      if (epi == EPI_SWIGLU_BF16) return go_dma<1, 4, 2, 4, EPI_SWIGLU_BF16, 128, 4, false, true>(a, max_units, st);
-      if (epi == EPI_STORE_BF16) return go_dma<1, 4, 2, 4, EPI_STORE_BF16, 128, 4, false, true>(a, max_units, st);
-      return hipErrorInvalidValue;
+      if (w4) {
+        return sw ? go_dma<1, 4, 2, 4, EPI_SWIGLU_BF16, 128, 4, false, false, true>(a, max_units, st)
+                  : go_dma<1, 4, 2, 4, EPI_STORE_BF16, 128, 4, false, false, true>(a, max_units, st);
+      }
+      return sw ? go_dma<1, 4, 2, 4, EPI_SWIGLU_BF16, 128, 4, false, true>(a, max_units, st)
+                : go_dma<1, 4, 2, 4, EPI_STORE_BF16, 128, 4, false, true>(a, max_units, st);
     default:
       return hipErrorInvalidValue;
   }

@@ -70,9 +70,10 @@ int gemm_block_m(GemmCfg cfg, bool fp8);
 int gemm_block_n(GemmCfg cfg);
 hipError_t launch_gemm(GemmCfg cfg, Epilogue epi, bool fp8, const GemmArgs& a, int max_units,
                        hipStream_t st);
-// W8A8 grouped GEMM: int8 A and B, per-row a_scale and per-channel b_scale, bf16 result
-// (EPI_SWIGLU_BF16 or EPI_STORE_BF16); the bf16 tiles (gemm_block_m(cfg, false)).
-hipError_t launch_gemm_i8(GemmCfg cfg, Epilogue epi, const GemmArgs& a, int max_units,
+// W8A8 / W4A8 grouped GEMM: int8 A, int8 B (w4: packed int4 B, ldb and b_group in bytes of
+// the packed rows), per-row a_scale and per-channel b_scale, bf16 result (EPI_SWIGLU_BF16
+// or EPI_STORE_BF16); the bf16 tiles (gemm_block_m(cfg, false)).
+hipError_t launch_gemm_i8(GemmCfg cfg, Epilogue epi, bool w4, const GemmArgs& a, int max_units,
                           hipStream_t st);
 
 // Builds the unit table of a grouped GEMM on the device.  `offsets` [G+1] or, when

@@ -9,7 +9,7 @@ import torch
 
 # max relative error bounds: bf16 2e-2, fp8 6e-2, fp32 1e-5 (the workload statement);
 # W8A8 6e-2 (its own quantization error against unquantized activations is <= 2.5%)
-TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "int8": 6e-2}
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "int8": 6e-2, "int4": 6e-2}
 
 
 def say(*a):
@@ -18,7 +18,7 @@ def say(*a):
 
 
 def tol_of(cfg) -> float:
-    return TOL[cfg.wt] if cfg.wt in ("fp8", "int8") else TOL[cfg.act]
+    return TOL[cfg.wt] if cfg.wt in ("fp8", "int8", "int4") else TOL[cfg.act]
 
 
 def host(t: torch.Tensor) -> np.ndarray:

@@ -68,6 +68,8 @@ def test_workspace_query(L):
     assert M.moe_workspace_bytes(c6) >= 65536 * 7168 * (2 + 1)
     assert M.moe_grouped_ffn_workspace_bytes(c6, 256, 65536) >= 65536 * 2048 * (2 + 1)
     assert M.moe_workspace_bytes(M.shape(8, 128, 4, 2, 128, 128, "f32", "int8")) == 0
+    c8 = M.shape(128, 7168, 256, 8, 2048, 2048, "bf16", "int4")
+    assert M.moe_workspace_bytes(c8) > 1024 * 7168
 
 
 DUMMY = ctypes.c_void_p(4096)   # never dereferenced: validation fails first

@@ -40,23 +40,23 @@ def sample_tokens(T, seed):
 def expert_dict(cfg, experts):
     w13, w2, s13, s2 = {}, {}, {}, {}
     for e, v in inputs.for_each_expert(cfg, inputs.expert_w13, experts):
-        if cfg.wt in ("fp8", "int8"):
+        if cfg.wt in ("fp8", "int8", "int4"):
             w13[e], s13[e] = v
         else:
             w13[e] = v
     for e, v in inputs.for_each_expert(cfg, inputs.expert_w2, experts):
-        if cfg.wt in ("fp8", "int8"):
+        if cfg.wt in ("fp8", "int8", "int4"):
             w2[e], s2[e] = v
         else:
             w2[e] = v
     d = {"w13": w13, "w2": w2}
-    if cfg.wt in ("fp8", "int8"):
+    if cfg.wt in ("fp8", "int8", "int4"):
         d.update(w13_scale=s13, w2_scale=s2)
     return d
 
 
 @pytest.mark.parametrize("name", ["c1_tiny_fp32", "c2_prefill_bf16", "c4_decode_bf16", "c5_skewed_fp8",
-                                  "c6_prefill_w8a8", "c7_decode_w8a8"])
+                                  "c6_prefill_w8a8", "c7_decode_w8a8", "c8_decode_w4a8"])
 def test_full_layer_sampled(M, name):
     cfg = configs.get(name)
     say("full layer", name, "upload")
@@ -83,7 +83,7 @@ def test_full_layer_sampled(M, name):
     say("full layer", name, "routing")
     R = T * k
     fp8 = cfg.wt == "fp8"
-    i8 = cfg.wt == "int8"
+    i8 = cfg.wt in ("int8", "int4")
     ex = torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.int8 if i8 else g["x"].dtype, device="cuda")
     exs = torch.empty((R, H // 128), dtype=torch.float32, device="cuda") if fp8 else \
         torch.empty(R, dtype=torch.float32, device="cuda") if i8 else None

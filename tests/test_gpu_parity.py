@@ -89,7 +89,7 @@ def run_init_routing(M, cfg, g, ids_dev, T, k, E, e_base, with_rows=True):
     s = M.shape(T, cfg.H, E, k, cfg.I, cfg.I_shared, cfg.act, cfg.wt)
     R = T * k
     fp8 = cfg.wt == "fp8"
-    i8 = cfg.wt == "int8"
+    i8 = cfg.wt in ("int8", "int4")
     ex = None
     exs = None
     if with_rows:
@@ -125,7 +125,7 @@ def test_init_routing(M, name):
         xq, xs = O.quant_1x128(O.to_f64(d["x"], cfg.act).astype(np.float32))
         assert np.array_equal(host(out["ex"]), O.expand_rows(xq, ref["sorted_src"], k))
         assert np.array_equal(host(out["exs"]), O.expand_rows(xs, ref["sorted_src"], k))
-    elif cfg.wt == "int8":
+    elif cfg.wt in ("int8", "int4"):
         # per-token int8 codes and row scales, bit for bit
         xq, xs = O.quant_per_token_int8(O.to_f64(d["x"], cfg.act).astype(np.float32))
         assert np.array_equal(host(out["ex"]), O.expand_rows(xq, ref["sorted_src"], k))
@@ -150,7 +150,7 @@ def oracle_sorted_inputs(cfg, d):
         a_bytes = O.expand_rows(xq, rt["sorted_src"], k)
         a_scale = O.expand_rows(xs, rt["sorted_src"], k)
         a64 = O.dequant_1x128(a_bytes, a_scale)
-    elif cfg.wt == "int8":
+    elif cfg.wt in ("int8", "int4"):
         xq, xs = O.quant_per_token_int8(O.to_f64(d["x"], cfg.act).astype(np.float32))
         a_bytes = O.expand_rows(xq, rt["sorted_src"], k)
         a_scale = np.ascontiguousarray(xs[rt["sorted_src"] // k])
@@ -175,7 +175,7 @@ def test_grouped_ffn(M, name):
                       g["w13"], g.get("w13_scale"), g["w2"], g.get("w2_scale"), y, ws)
     torch.cuda.synchronize()
     ref = O.grouped_ffn(a64, rt["expert_offsets"], O.expert_weights_f64(d),
-                        quant_h="int8" if cfg.wt == "int8" else cfg.wt == "fp8")
+                        quant_h="int8" if cfg.wt in ("int8", "int4") else cfg.wt == "fp8")
     got = act_to_f64(y, cfg.act)
     assert np.isfinite(got).all()
     err = max_row_rel_err(got, ref)
