@@ -180,7 +180,7 @@ def roofline_entry(acc_k: dict, ms: float) -> dict:
 
 # ----------------------------------------------------------------------------- GPU run
 
-def run_gpu(cfg, steps, warmup, two_streams=True):
+def run_gpu(cfg, steps, warmup, two_streams=True, flush=False):
     import torch
 
     import moe_expert_layer_top_amd as M
@@ -228,7 +228,21 @@ def run_gpu(cfg, steps, warmup, two_streams=True):
         stage_ms[M.EV_NAMES[j]] = float(np.mean([events[i][j - 1].elapsed_time(events[i][j])
                                                  for i in range(steps)]))
     tpe = np.bincount(idx.cpu().numpy().reshape(-1), minlength=cfg.E)
-    return dict(total_ms=total_ms, wall_s=wall, stage_ms=stage_ms, tpe=tpe, setup_s=setup_s,
+    cold_ms = None
+    if flush:
+        # cold layers: before each one, a 512 MB write evicts the L2s and the 256 MB
+        # last-level cache, so nothing of the previous layer is re-read from cache; each
+        # layer is timed alone by its own start/finalize events
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        lay = []
+        for i in range(steps):
+            scratch.zero_()
+            M.moe_layer_profiled(s, W, g["x"], out, idx, w, logits, ws, events[i], side=side)
+            torch.cuda.synchronize()
+            lay.append(events[i][0].elapsed_time(events[i][nev - 1]))
+        cold_ms = float(np.median(lay))
+        del scratch
+    return dict(total_ms=total_ms, wall_s=wall, stage_ms=stage_ms, tpe=tpe, setup_s=setup_s, cold_ms=cold_ms,
                 logits=logits.cpu().numpy(), idx=idx.cpu().numpy())
 
 
@@ -320,6 +334,8 @@ def main():
     ap.add_argument("--config", default="c2_prefill_bf16")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--flush", action="store_true",
+                    help="also time layers one by one after a 512 MB cache-evicting write (cold_ms_per_step)")
     ap.add_argument("--one-stream", action="store_true",
                     help="run the shared expert's own launches on the layer's stream")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -335,7 +351,7 @@ def main():
 
     from synth import configs
     cfg = configs.get(args.config)
-    r = run_gpu(cfg, args.steps, args.warmup, two_streams=not args.one_stream)
+    r = run_gpu(cfg, args.steps, args.warmup, two_streams=not args.one_stream, flush=args.flush)
     ms = r["total_ms"] / args.steps
     tokens = cfg.shared_rows
     acc = launch_accounting(cfg, account(cfg, r["tpe"]))
@@ -393,6 +409,7 @@ def main():
         "active_experts": int(np.count_nonzero(r["tpe"])),
         "max_rows_per_expert": int(r["tpe"].max()),
         "wall_ms_per_step": r["wall_s"] * 1e3 / args.steps,
+        "cold_ms_per_step": r["cold_ms"],
         "setup_s": r["setup_s"],
     }
     if not args.no_cpu:
