@@ -246,6 +246,100 @@ def run_gpu(cfg, steps, warmup, two_streams=True, flush=False):
                 logits=logits.cpu().numpy(), idx=idx.cpu().numpy())
 
 
+EP_STAGES = ["route", "ffn", "unsort", "shared"]
+
+
+def run_gpu_ep(cfg, steps, warmup):
+    """One expert-parallel rank's share (pretagged rows): the re-routing sort with the row
+    copy (moe_init_routing, k = 1), the grouped experts over the rank's experts
+    (moe_grouped_ffn), the un-sort back to arrival order (moe_finalize_routing, k = 1) and
+    the shared expert on the rank's local tokens (moe_grouped_ffn, G = 1).  The shared
+    expert needs none of the routed work, so it runs on a second stream beside it
+    ([MND §Computation and communication overlap], Dispatch Overlap); the stages are
+    marked by HIP events on the main stream ("shared" is the wait for the side stream)."""
+    import torch
+
+    import moe_expert_layer_top_amd as M
+    from synth.device import upload_layer
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    g = upload_layer(cfg, dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    s = M.shape_of(cfg)
+    R, H, E = cfg.T, cfg.H, cfg.E
+    act_dt = torch.float32 if cfg.act == "f32" else torch.int16
+    ws = torch.empty(M.moe_workspace_bytes(s), dtype=torch.uint8, device=dev)
+    ex = torch.empty((R, H), dtype=act_dt, device=dev)
+    eri = torch.empty(R, dtype=torch.int32, device=dev)
+    ssrc = torch.empty(R, dtype=torch.int32, device=dev)
+    tpe = torch.empty(E, dtype=torch.int32, device=dev)
+    offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    y = torch.empty((R, H), dtype=act_dt, device=dev)
+    y_arr = torch.empty((R, H), dtype=act_dt, device=dev)
+    wsf = torch.empty(M.moe_grouped_ffn_workspace_bytes(s, E, R), dtype=torch.uint8, device=dev)
+    s_sh = M.shape(cfg.T_local, H, 1, 1, cfg.I_shared, cfg.I_shared, cfg.act, cfg.act)
+    sh = torch.empty((cfg.T_local, H), dtype=act_dt, device=dev)
+    ws2 = torch.empty(M.moe_grouped_ffn_workspace_bytes(s_sh, 1, cfg.T_local), dtype=torch.uint8, device=dev)
+    offs1 = torch.tensor([0, cfg.T_local], dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+
+    def step(ev=None):
+        mark = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
+        mark(0)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            M.moe_grouped_ffn(s_sh, 1, cfg.T_local, g["x_local"], None, offs1, g["sh_w13"], None,
+                              g["sh_w2"], None, sh, ws2)
+        M.moe_init_routing(s, g["x"], g["ids"], cfg.e_base, ex, None, eri, ssrc, tpe, offs, ws)
+        mark(1)
+        M.moe_grouped_ffn(s, E, R, ex, None, offs, g["w13"], None, g["w2"], None, y, wsf)
+        mark(2)
+        M.moe_finalize_routing(s, y, None, None, eri, y_arr)
+        mark(3)
+        stream.wait_stream(side)
+        mark(4)
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        step(events[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    stage_ms = {name: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(steps)]))
+                for j, name in enumerate(EP_STAGES)}
+    return dict(total_ms=start.elapsed_time(end), wall_s=wall, stage_ms=stage_ms,
+                tpe=tpe.cpu().numpy(), setup_s=setup_s)
+
+
+def account_ep(cfg, tpe) -> dict:
+    """Algorithmic FLOPs and bytes of the rank-share stages (as account())."""
+    T, H, E, I, Is, TL = cfg.T, cfg.H, cfg.E, cfg.I, cfg.I_shared, cfg.T_local
+    ab = _bytes(cfg.act)
+    active = int(np.count_nonzero(tpe))
+    R = int(np.sum(tpe))
+    return {
+        "route": dict(flops=0, bytes=T * 4 + T * H * ab + R * H * ab + 2 * R * 4 + E * 8, dt=None),
+        "ffn": dict(flops=2 * R * H * 2 * I + 2 * R * I * H,
+                    bytes=active * 3 * I * H * ab + R * H * ab + 2 * R * I * ab + R * H * ab, dt=cfg.act),
+        "unsort": dict(flops=0, bytes=2 * R * H * ab + R * 4, dt=None),
+        "shared": dict(flops=2 * TL * H * 2 * Is + 2 * TL * Is * H,
+                       bytes=3 * Is * H * ab + 2 * TL * H * ab + 2 * TL * Is * ab, dt=cfg.act),
+    }
+
+
+EP_SIDE = ("shared",)   # stages whose time is a wait for the side stream (no rates)
+
+
 # ----------------------------------------------------------------------------- CPU oracle baseline
 
 def blas_threads() -> int:
@@ -270,6 +364,8 @@ def cpu_baseline(cfg, target_s=15.0, max_tokens=None):
     from synth import inputs
 
     x_all = inputs.tokens(cfg)
+    if cfg.pretagged:
+        return cpu_baseline_ep(cfg, x_all, target_s)
     wg = inputs.gate_weight(cfg)
     bias = inputs.expert_bias(cfg)
 
@@ -309,6 +405,38 @@ def cpu_baseline(cfg, target_s=15.0, max_tokens=None):
             "sample": f"first {ts} of the {cfg.T} tokens of {cfg.name} through the float64 oracle "
                       f"(gate, top-k, routing, grouped SwiGLU experts, shared expert, combine); "
                       f"{dt:.1f} s"}
+
+
+def cpu_baseline_ep(cfg, x_all, target_s):
+    """The oracle on the first rows of a rank share: rows[:ts] with their ids, and the
+    same fraction of the local tokens for the shared expert; local tokens per second."""
+    import dataclasses
+
+    from oracle import moe as O
+    from synth import inputs
+
+    ids_all = inputs.pretagged_ids(cfg)
+    xl_all = inputs.local_tokens(cfg)
+    ts = 8
+    while True:
+        tl = max(1, ts * cfg.T_local // cfg.T)
+        ids = ids_all[:ts]
+        experts = sorted(set((ids[:, 0] - cfg.e_base).tolist()))
+        d = {"cfg": dataclasses.replace(cfg, T=ts, T_local=tl), "x": x_all[:ts], "ids": ids,
+             "x_local": xl_all[:tl], "bias": None,
+             "sh_w13": inputs.shared_w13(cfg), "sh_w2": inputs.shared_w2(cfg),
+             "w13": dict(inputs.for_each_expert(cfg, inputs.expert_w13, experts)),
+             "w2": dict(inputs.for_each_expert(cfg, inputs.expert_w2, experts))}
+        t0 = time.perf_counter()
+        O.moe_layer(d)
+        dt = time.perf_counter() - t0
+        if dt >= target_s * 0.5 or ts >= cfg.T:
+            break
+        ts = min(cfg.T, max(ts + 8, int(ts * min(8.0, target_s / max(dt, 1e-3)))))
+    return {"value": tl / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"first {ts} of the {cfg.T} received rows of {cfg.name} with {tl} of its "
+                      f"{cfg.T_local} local tokens through the float64 oracle (re-routing, grouped "
+                      f"experts, un-sort, shared expert); {dt:.1f} s"}
 
 
 def copy_calibration(nbytes=1 << 30, reps=3):
@@ -351,6 +479,9 @@ def main():
 
     from synth import configs
     cfg = configs.get(args.config)
+    if cfg.pretagged:
+        main_ep(cfg, args)
+        return
     r = run_gpu(cfg, args.steps, args.warmup, two_streams=not args.one_stream, flush=args.flush)
     ms = r["total_ms"] / args.steps
     tokens = cfg.shared_rows
@@ -416,6 +547,57 @@ def main():
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     else:
         line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+def main_ep(cfg, args):
+    """Bench line of an expert-parallel rank share: value = local tokens/s; the received
+    rows/s beside it."""
+    r = run_gpu_ep(cfg, args.steps, args.warmup)
+    ms = r["total_ms"] / args.steps
+    acc = account_ep(cfg, r["tpe"])
+    kern = {name: roofline_entry(acc[name], r["stage_ms"][name]) for name in acc if name not in EP_SIDE}
+    kern["shared"] = {"ms": r["stage_ms"]["shared"], "side_stream": True,
+                      "note": "ms = time the main stream waited for the shared expert"}
+    dk = kern["ffn"]
+    if dk["bound"] == "mfma":
+        roof = {"kernel": "ffn (plan + GEMM1 + GEMM2 of moe_grouped_ffn)", "bound": "mfma",
+                "achieved": acc["ffn"]["flops"] / (r["stage_ms"]["ffn"] / 1e3) / 1e12,
+                "peak": PEAK_TFLOPS[acc["ffn"]["dt"]], "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": "ffn (plan + GEMM1 + GEMM2 of moe_grouped_ffn)", "bound": "hbm",
+                "achieved": acc["ffn"]["bytes"] / (r["stage_ms"]["ffn"] / 1e3) / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["algorithmic_bytes"] = acc["ffn"]["bytes"]
+    roof["mfma_frac"] = dk.get("mfma_frac")
+    perm_ms = r["stage_ms"]["route"] + r["stage_ms"]["unsort"]
+    perm_bytes = acc["route"]["bytes"] + acc["unsort"]["bytes"]
+    line = {
+        "metric": METRIC,
+        "value": cfg.T_local * 1e3 / ms,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.act,
+        "data": "synthetic (seeded; see DESIGN.md input recipe)",
+        "config": {"workload": cfg.name, "rows": cfg.T, "T_local": cfg.T_local, "H": cfg.H, "E": cfg.E,
+                   "e_base": cfg.e_base, "I": cfg.I, "I_shared": cfg.I_shared, "act": cfg.act, "wt": cfg.wt},
+        "rows_per_s": cfg.T * 1e3 / ms,
+        "roofline": roof,
+        "ffn_mfma_frac": dk.get("mfma_frac"),
+        "permute_combine_hbm_frac": perm_bytes / (perm_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+        "kernels": kern,
+        "wall_ms_per_step": r["wall_s"] * 1e3 / args.steps,
+        "setup_s": r["setup_s"],
+        "cpu_baseline": None if args.no_cpu else cpu_baseline(cfg, args.cpu_seconds),
+    }
     print(json.dumps(line), flush=True)
 
 
