@@ -286,9 +286,14 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
   const FfnLayout L = ffn_layout(s, G, R_max, I, alt_rows);
   const int H = s->H;
   if (s->act == MOE_F32) {
-    return hip_status(moe::launch_grouped_ffn_f32(
+    // one fused launch: its boundaries are marked as the plan (empty) and both GEMMs
+    if (prof.mark(ev_plan, st) != hipSuccess) return MOE_EHIP;
+    const moe_status fst = hip_status(moe::launch_grouped_ffn_f32(
         static_cast<const float*>(io.a), io.offsets, G, R_max, static_cast<const float*>(io.w13),
         static_cast<const float*>(io.w2), at<float>(ws, L.h), static_cast<float*>(io.y), H, I, st));
+    if (fst != MOE_OK) return fst;
+    if (prof.mark(ev_ffn1, st) != hipSuccess || prof.mark(ev_ffn2, st) != hipSuccess) return MOE_EHIP;
+    return MOE_OK;
   }
   const bool fp8 = s->wt == MOE_FP8_E4M3;
   const bool i8 = q8_weights(s);
