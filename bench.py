@@ -93,23 +93,29 @@ def account(cfg, tpe) -> dict:
                      dt=mfma_dt),
         "ffn2": dict(flops=2 * R * I * H,
                      bytes=active * H * I * wb + sc_w2 + R * I * hb + sc_h + R * H * ab, dt=mfma_dt),
-        "shared": dict(flops=2 * T * H * 2 * Is + 2 * T * Is * H,
-                       bytes=3 * Is * H * ab + T * H * ab + 2 * T * Is * ab + T * H * ab,
-                       dt=cfg.act),
-        # the shared expert's two GEMMs separately (x -> h_s, h_s -> s)
-        "shared1": dict(flops=2 * T * H * 2 * Is, bytes=2 * Is * H * ab + T * H * ab + T * Is * ab,
-                        dt=cfg.act),
-        "shared2": dict(flops=2 * T * Is * H, bytes=Is * H * ab + T * Is * ab + T * H * ab,
-                        dt=cfg.act),
         "finalize": dict(flops=0, bytes=R * H * ab + 2 * T * H * ab + T * k * 8, dt=None),
     }
+    # the shared expert's two GEMMs (x -> h_s, h_s -> s); W8A8 beside int8 / int4 experts:
+    # int8 tokens and weights with their row and channel scales, h_s counted once as int8
+    swb = _bytes(cfg.sh_wt)
+    sq = cfg.sh_wt == "int8"
+    xb, shb = (1, 1) if sq else (ab, ab)
+    sdt = "int8" if sq else cfg.act
+    acc["shared1"] = dict(flops=2 * T * H * 2 * Is,
+                          bytes=2 * Is * H * swb + T * H * xb + T * Is * shb
+                          + ((2 * Is + 2 * T) * 4 if sq else 0), dt=sdt)
+    acc["shared2"] = dict(flops=2 * T * Is * H,
+                          bytes=Is * H * swb + T * Is * shb + T * H * ab + ((H + T) * 4 if sq else 0),
+                          dt=sdt)
+    acc["shared"] = dict(flops=acc["shared1"]["flops"] + acc["shared2"]["flops"],
+                         bytes=acc["shared1"]["bytes"] + acc["shared2"]["bytes"], dt=sdt)
     return acc
 
 
 def shared_is_merged(cfg) -> bool:
     """moe_layer runs the shared expert as one more group of the routed grouped-GEMM
-    launches when it has the routed experts' shape and dtype (bf16, I_shared == I)."""
-    return cfg.act == "bf16" and cfg.wt == "bf16" and cfg.I_shared == cfg.I
+    launches when it has the routed experts' shape and dtype (bf16 or int8, I_shared == I)."""
+    return cfg.act == "bf16" and cfg.wt in ("bf16", "int8") and cfg.I_shared == cfg.I
 
 
 def gathers_rows(cfg) -> bool:
@@ -128,6 +134,9 @@ def launch_accounting(cfg, acc: dict) -> dict:
         ab = _bytes(cfg.act)
         out["expand"] = dict(flops=0, bytes=0, dt=None)
         out["ffn1"]["bytes"] += cfg.T * cfg.H * ab - cfg.R * cfg.H * ab
+    if shared_is_merged(cfg) and cfg.sh_wt == "int8":
+        # the expansion also writes the tokens' int8 codes in token order for the shared expert
+        out["expand"]["bytes"] += cfg.T * cfg.H + cfg.T * 4
     if shared_is_merged(cfg):
         for k, sk in (("ffn1", "shared1"), ("ffn2", "shared2")):
             out[k] = dict(flops=out[k]["flops"] + acc[sk]["flops"],
@@ -198,8 +207,7 @@ def run_gpu(cfg, steps, warmup, two_streams=True, flush=False):
     w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
     logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
     ws = torch.empty(M.moe_workspace_bytes(s), dtype=torch.uint8, device=dev)
-    W = M.weights(g["w_gate"], g["w13"], g["w2"], g["sh_w13"], g["sh_w2"], g.get("w13_scale"),
-                  g.get("w2_scale"), g.get("bias"))
+    W = M.weights_of(g)
     nev = len(M.EV_NAMES)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
     stream = torch.cuda.current_stream()
@@ -371,8 +379,7 @@ def cpu_baseline(cfg, target_s=15.0, max_tokens=None):
 
     def prepare(ts):
         sub = dataclasses.replace(cfg, T=ts)
-        d = {"cfg": sub, "x": x_all[:ts], "w_gate": wg, "bias": bias,
-             "sh_w13": inputs.shared_w13(cfg), "sh_w2": inputs.shared_w2(cfg)}
+        d = {"cfg": sub, "x": x_all[:ts], "w_gate": wg, "bias": bias, **inputs.shared_weights(cfg)}
         xl = O.to_f64(d["x"], cfg.act)
         idx, _ = O.route_topk(O.gate_logits(xl, O.to_f64(wg, cfg.act)).astype(np.float32), bias, cfg.k)
         experts = sorted(set(idx.reshape(-1).tolist()))
@@ -424,7 +431,7 @@ def cpu_baseline_ep(cfg, x_all, target_s):
         experts = sorted(set((ids[:, 0] - cfg.e_base).tolist()))
         d = {"cfg": dataclasses.replace(cfg, T=ts, T_local=tl), "x": x_all[:ts], "ids": ids,
              "x_local": xl_all[:tl], "bias": None,
-             "sh_w13": inputs.shared_w13(cfg), "sh_w2": inputs.shared_w2(cfg),
+             **inputs.shared_weights(cfg),
              "w13": dict(inputs.for_each_expert(cfg, inputs.expert_w13, experts)),
              "w2": dict(inputs.for_each_expert(cfg, inputs.expert_w2, experts))}
         t0 = time.perf_counter()

@@ -200,11 +200,15 @@ typedef struct {
   const void* w_gate;      /* [E, H] act                                       */
   const void* w13;         /* [E, 2I, H] wt (int4: [E, 2I, H/2] packed bytes)  */
   const void* w2;          /* [E, H, I] wt (int4: [E, H, I/2] packed bytes)    */
-  const void* sh_w13;      /* [2*I_shared, H] act (shared expert, never fp8)   */
-  const void* sh_w2;       /* [H, I_shared] act                                */
+  const void* sh_w13;      /* [2*I_shared, H] shared expert: act, or int8 codes when wt
+                              is int8 or int4 (then it is W8A8, [V32 §quantization
+                              strategy]); never fp8                             */
+  const void* sh_w2;       /* [H, I_shared] act, or int8 codes as sh_w13       */
   const float* w13_scale;  /* fp8 [E, 2I/128, H/128]; int8/int4 [E, 2I]; else NULL */
   const float* w2_scale;   /* fp8 [E, H/128, I/128]; int8/int4 [E, H]; else NULL   */
   const float* bias;       /* [E] gate-logit bias or NULL                      */
+  const float* sh_w13_scale; /* int8 shared expert: [2*I_shared] per channel; else NULL */
+  const float* sh_w2_scale;  /* int8 shared expert: [H] per channel; else NULL          */
 } moe_weights;
 
 /* The whole layer: gate + top-k, init-routing, grouped experts, shared expert
@@ -221,9 +225,10 @@ moe_status moe_layer(const moe_shape* s, const moe_weights* w, const void* x, vo
 /* moe_layer with the shared expert on a second stream.  [V32 §multi-stream parallel
  * optimization] and [MND §Computation and communication overlap] (Dispatch Overlap):
  * the shared expert needs neither the gate nor the routing, so it can run beside them.
- * When the shared expert runs in launches of its own (fp8 or fp32 experts, or
+ * When the shared expert runs in launches of its own (fp8, int4 or fp32 experts, or
  * I_shared != I; otherwise it is already a group of the routed launches and `side` is
- * not used), its two GEMMs are enqueued on `side` behind an event recorded on `stream`
+ * not used), its launches (for the int8 shared expert of int4 layers: the per-token
+ * quantization of x, then its two GEMMs) are enqueued on `side` behind an event recorded on `stream`
  * at entry, and `stream` waits for them before finalize.  On return, all of the call's
  * work is ordered before anything enqueued later on `stream`, as with moe_layer; the
  * results are bit-identical to moe_layer's.  side == NULL or side == stream: same as

@@ -45,7 +45,8 @@ class moe_weights(ctypes.Structure):
     _fields_ = [("w_gate", ctypes.c_void_p), ("w13", ctypes.c_void_p), ("w2", ctypes.c_void_p),
                 ("sh_w13", ctypes.c_void_p), ("sh_w2", ctypes.c_void_p),
                 ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
-                ("bias", ctypes.c_void_p)]
+                ("bias", ctypes.c_void_p), ("sh_w13_scale", ctypes.c_void_p),
+                ("sh_w2_scale", ctypes.c_void_p)]
 
 
 class moe_router(ctypes.Structure):
@@ -176,9 +177,20 @@ def moe_finalize_routing(s, y, skip, topk_w, expanded_row_idx, out, stream=None)
            "moe_finalize_routing")
 
 
-def weights(w_gate, w13, w2, sh_w13, sh_w2, w13_scale=None, w2_scale=None, bias=None) -> moe_weights:
+def weights(w_gate, w13, w2, sh_w13, sh_w2, w13_scale=None, w2_scale=None, bias=None,
+            sh_w13_scale=None, sh_w2_scale=None) -> moe_weights:
     return moe_weights(_ptr(w_gate), _ptr(w13), _ptr(w2), _ptr(sh_w13), _ptr(sh_w2),
-                       _ptr(w13_scale), _ptr(w2_scale), _ptr(bias))
+                       _ptr(w13_scale), _ptr(w2_scale), _ptr(bias), _ptr(sh_w13_scale),
+                       _ptr(sh_w2_scale))
+
+
+def weights_of(g: dict) -> moe_weights:
+    """moe_weights from a dict of device tensors named as the layer's inputs (w_gate, w13,
+    w2, sh_w13, sh_w2 and, where present, w13_scale, w2_scale, bias, sh_w13_scale,
+    sh_w2_scale)."""
+    return weights(g.get("w_gate"), g["w13"], g["w2"], g["sh_w13"], g["sh_w2"],
+                   g.get("w13_scale"), g.get("w2_scale"), g.get("bias"), g.get("sh_w13_scale"),
+                   g.get("sh_w2_scale"))
 
 
 def moe_layer(s, w: moe_weights, x, out, topk_idx, topk_w, logits, ws, stream=None):

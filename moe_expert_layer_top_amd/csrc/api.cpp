@@ -23,7 +23,8 @@ using moe::Unit;
 constexpr size_t kAlign = 256;
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;
-constexpr int kGateMaxSplits = 64;
+constexpr int kGateMaxSplits = 16;
+constexpr int kSmallTileRows = 512;  // at most this many rows in all: the short tile
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -107,8 +108,11 @@ GatePlan gate_plan(const moe_shape* s) {
 
 // ------------------------------------------------------------------ grouped FFN plan
 moe::GemmCfg ffn_cfg(int G, int R_max) {
-  // decode-sized groups (a few rows each) take the short tile, prefill the tall one
-  return (G > 0 && R_max <= 64LL * G) ? moe::CFG_SMALL : moe::CFG_BIG;
+  // decode-sized groups (a few rows each) take the short tile, prefill the tall one; so
+  // do small batches in few groups (the dense shared expert at decode), which the tall
+  // tile would give a handful of workgroups on a 256-CU machine
+  return (G > 0 && (R_max <= 64LL * G || R_max <= kSmallTileRows)) ? moe::CFG_SMALL
+                                                                    : moe::CFG_BIG;
 }
 
 // Upper bound on the units the planner writes: every group of n > 0 rows makes
@@ -118,11 +122,19 @@ int max_units(moe::GemmCfg cfg, bool fp8, int G, int R_max, int extra_rows = 0) 
   return R_max / bm + std::min(G, R_max) + (extra_rows > 0 ? extra_rows / bm + 1 : 0);
 }
 
+// The shared expert's dtypes: W8A8 beside W8A8 or W4A8 routed experts ([V32 §quantization
+// strategy] quantizes it W8A8 in both), else its weights are in the activation dtype.
+moe_shape shared_shape(const moe_shape* s) {
+  moe_shape sh = *s;
+  sh.wt = q8_weights(s) ? MOE_INT8 : s->act;
+  return sh;
+}
+
 // The shared expert runs inside the routed grouped-GEMM launches (as one extra group
 // whose units read x and the shared weights) when it has the routed experts' shape
-// and dtype: bf16 activations and weights, I_shared == I.
+// and dtype: bf16 activations, bf16 or int8 weights, I_shared == I.
 bool merge_shared(const moe_shape* s) {
-  return s->act == MOE_BF16 && s->wt == MOE_BF16 && s->I_shared == s->I;
+  return s->act == MOE_BF16 && (s->wt == MOE_BF16 || s->wt == MOE_INT8) && s->I_shared == s->I;
 }
 
 // bf16 layers gather the routed rows from x inside the first expert GEMM (32-bit
@@ -132,10 +144,11 @@ bool gather_rows(const moe_shape* s) {
 }
 
 struct FfnLayout {
-  size_t units, n_units, h, h_scale, hq, h2, total;
+  size_t units, n_units, h, h_scale, hq, h2, h2_scale, h2q, total;
 };
 
-// extra_rows > 0: room for the extra group's units and its intermediate h2 [extra_rows, I].
+// extra_rows > 0: room for the extra group's units and its intermediate h2 [extra_rows, I]
+// (int8: with its row scales and codes).
 FfnLayout ffn_layout(const moe_shape* s, int G, int R_max, int I, int extra_rows = 0) {
   FfnLayout L{};
   size_t o = 0;
@@ -163,6 +176,10 @@ FfnLayout ffn_layout(const moe_shape* s, int G, int R_max, int I, int extra_rows
   if (i8) o += align_up(static_cast<size_t>(R_max) * I);   // h quantized per row
   L.h2 = o;
   if (extra_rows > 0) o += align_up(static_cast<size_t>(extra_rows) * I * 2);
+  L.h2_scale = o;
+  if (extra_rows > 0 && i8) o += align_up(static_cast<size_t>(extra_rows) * 4);
+  L.h2q = o;
+  if (extra_rows > 0 && i8) o += align_up(static_cast<size_t>(extra_rows) * I);
   L.total = o;
   return L;
 }
@@ -170,7 +187,7 @@ FfnLayout ffn_layout(const moe_shape* s, int G, int R_max, int I, int extra_rows
 // ------------------------------------------------------------------ layer layout
 struct Layout {
   size_t err, seg_err, part, logits, idx, w, counts, tpe, offsets, eri, sorted_src, ex, ex_scale,
-      y, ffn, sh_out, sh_ffn, total;
+      y, ffn, sh_out, sh_xq, sh_xs, sh_ffn, total;
 };
 
 Layout layer_layout(const moe_shape* s) {
@@ -200,8 +217,10 @@ Layout layer_layout(const moe_shape* s) {
   const bool merged = merge_shared(s);
   L.ffn = o;           o += ffn_layout(s, s->E, static_cast<int>(R), s->I, merged ? s->T : 0).total;
   L.sh_out = o;        o += align_up(T * H * ab);
-  moe_shape sh = *s;
-  sh.wt = s->act;  // the shared expert is never fp8
+  // W8A8 shared expert: the tokens' int8 codes and scales in token order
+  L.sh_xq = o;         if (i8) o += align_up(T * H);
+  L.sh_xs = o;         if (i8) o += align_up(T * 4);
+  const moe_shape sh = shared_shape(s);
   L.sh_ffn = o;        if (!merged) o += ffn_layout(&sh, 1, s->T, s->I_shared).total;
   L.total = o;
   return L;
@@ -298,16 +317,20 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
   const bool fp8 = s->wt == MOE_FP8_E4M3;
   const bool i8 = q8_weights(s);
   const bool w4 = s->wt == MOE_INT4;
+  if (alt_rows > 0 && (fp8 || w4)) return MOE_EUNSUPPORTED;  // bf16 / int8 panels only
   const int eb = (fp8 || i8) ? 1 : 2;
   const moe::GemmCfg cfg = ffn_cfg(G, R_max);
   const int bm = moe::gemm_block_m(cfg, fp8);
   Unit* units = at<Unit>(ws, L.units);
   int32_t* n_units = at<int32_t>(ws, L.n_units);
+  // grouped rows, and the int8 kernels (which have no uniform-row form), run from a unit
+  // table; a dense bf16 / fp8 FFN cuts its rows into uniform slices
+  const bool planned = io.offsets || i8;
   int mu;
-  if (io.offsets) {
+  if (planned) {
     mu = max_units(cfg, fp8, G, R_max, alt_rows);
-    hipError_t e = moe::launch_plan(io.offsets, G, 0, alt_rows, bm, std::max(1, mu), units,
-                                    n_units, st);
+    hipError_t e = moe::launch_plan(io.offsets, G, io.offsets ? 0 : R_max, alt_rows, bm,
+                                    std::max(1, mu), units, n_units, st);
     if (e != hipSuccess) return MOE_EHIP;
   } else {
     mu = (R_max + bm - 1) / bm;
@@ -330,7 +353,7 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
   g1.c_scale_ld = I / 128;
   g1.units = units;
   g1.n_units = n_units;
-  g1.uniform_rows = io.offsets ? 0 : R_max;
+  g1.uniform_rows = planned ? 0 : R_max;
   g1.N = I;
   g1.K = H;
   g1.up_off = I;
@@ -359,6 +382,11 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
       g1.ldb = H / 2;
       g1.b_group = static_cast<long long>(I) * H;
     }
+    if (alt_rows > 0) {   // the int8 shared expert: its token codes and its own scales
+      g1.lda2 = H;
+      g1.a_scale2 = alt->a_scale;
+      g1.b_scale2 = alt->w13_scale;
+    }
   }
   hipError_t e = i8 ? moe::launch_gemm_i8(cfg, moe::EPI_SWIGLU_BF16, w4, g1, mu, st)
                     : moe::launch_gemm(cfg, fp8 ? moe::EPI_SWIGLU_FP8 : moe::EPI_SWIGLU_BF16, fp8,
@@ -368,6 +396,9 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
     e = moe::launch_quant_rows_i8(at<uint8_t>(ws, L.h), R_max, I, 1, nullptr,
                                   io.offsets ? io.offsets + G : nullptr, at<int8_t>(ws, L.hq),
                                   at<float>(ws, L.h_scale), st);
+    if (e == hipSuccess && alt_rows > 0)
+      e = moe::launch_quant_rows_i8(at<uint8_t>(ws, L.h2), alt_rows, I, 1, nullptr, nullptr,
+                                    at<int8_t>(ws, L.h2q), at<float>(ws, L.h2_scale), st);
     if (e != hipSuccess) return MOE_EHIP;
   }
   if (prof.mark(ev_ffn1, st) != hipSuccess) return MOE_EHIP;
@@ -409,6 +440,12 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
       g2.ldb = I / 2;
       g2.b_group = static_cast<long long>(H) * I / 2;
     }
+    if (alt_rows > 0) {
+      g2.A2 = at<uint8_t>(ws, L.h2q);
+      g2.lda2 = I;
+      g2.a_scale2 = at<float>(ws, L.h2_scale);
+      g2.b_scale2 = alt->w2_scale;
+    }
   }
   e = i8 ? moe::launch_gemm_i8(cfg, moe::EPI_STORE_BF16, w4, g2, mu, st)
          : moe::launch_gemm(cfg, moe::EPI_STORE_BF16, fp8, g2, mu, st);
@@ -422,8 +459,7 @@ extern "C" {
 
 size_t moe_workspace_bytes(const moe_shape* s) {
   if (check_shape(s) != MOE_OK || check_inter(s, s->I) != MOE_OK) return 0;
-  moe_shape sh = *s;
-  sh.wt = s->act;
+  const moe_shape sh = shared_shape(s);
   if (check_inter(&sh, s->I_shared) != MOE_OK) return 0;
   return layer_layout(s).total;
 }
@@ -463,7 +499,8 @@ static moe_status init_routing_impl(const moe_shape* s, const void* x, const int
                                     int32_t e_base, void* expanded_x, float* expanded_scale,
                                     int32_t* expanded_row_idx, int32_t* sorted_src,
                                     int32_t* tokens_per_expert, int32_t* expert_offsets, void* ws,
-                                    size_t ws_bytes, hipStream_t stream, const Prof& prof);
+                                    size_t ws_bytes, hipStream_t stream, const Prof& prof,
+                                    int8_t* tok_q = nullptr, float* tok_s = nullptr);
 
 moe_status moe_init_routing(const moe_shape* s, const void* x, const int32_t* ids, int32_t e_base,
                             void* expanded_x, float* expanded_scale, int32_t* expanded_row_idx,
@@ -479,7 +516,8 @@ static moe_status init_routing_impl(const moe_shape* s, const void* x, const int
                                     int32_t e_base, void* expanded_x, float* expanded_scale,
                                     int32_t* expanded_row_idx, int32_t* sorted_src,
                                     int32_t* tokens_per_expert, int32_t* expert_offsets, void* ws,
-                                    size_t ws_bytes, hipStream_t stream, const Prof& prof) {
+                                    size_t ws_bytes, hipStream_t stream, const Prof& prof,
+                                    int8_t* tok_q, float* tok_s) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   const bool fp8 = s->wt == MOE_FP8_E4M3;
@@ -500,8 +538,10 @@ static moe_status init_routing_impl(const moe_shape* s, const void* x, const int
   if (e != hipSuccess || prof.mark(MOE_EV_ROUTE, stream) != hipSuccess) return MOE_EHIP;
   if (expanded_x && s->T > 0) {
     // int8 (W8A8): each token quantized once per row, its codes copied to its k rows
+    // (and, for the layer's shared expert, once more in token order: tok_q / tok_s)
     e = i8 ? moe::launch_quant_rows_i8(x, s->T, s->H, s->k, expanded_row_idx, nullptr,
-                                       static_cast<int8_t*>(expanded_x), expanded_scale, stream)
+                                       static_cast<int8_t*>(expanded_x), expanded_scale, stream,
+                                       tok_q, tok_s)
            : moe::launch_expand(x, s->T, s->H, s->k, elem_bytes(s->act), fp8, expanded_row_idx,
                                 expanded_x, expanded_scale, stream);
     if (e != hipSuccess) return MOE_EHIP;
@@ -599,7 +639,9 @@ static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const voi
   const bool fp8 = s->wt == MOE_FP8_E4M3;
   if (s->T > 0 && (!x || !out || !w->w_gate || !w->w13 || !w->w2 || !w->sh_w13 || !w->sh_w2))
     return MOE_EINVAL;
-  if ((fp8 || q8_weights(s)) && (!w->w13_scale || !w->w2_scale)) return MOE_EINVAL;
+  const bool q8 = q8_weights(s);
+  if ((fp8 || q8) && (!w->w13_scale || !w->w2_scale)) return MOE_EINVAL;
+  if (q8 && s->T > 0 && (!w->sh_w13_scale || !w->sh_w2_scale)) return MOE_EINVAL;
   const size_t need = moe_workspace_bytes(s);
   if (need == 0) return MOE_EINVAL;
   if (ws_bytes < need) return MOE_EWORKSPACE;
@@ -614,10 +656,19 @@ static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const voi
   // communication overlap], Dispatch Overlap).  When it runs in launches of its own and
   // the caller gives a second stream, it starts there at once and overlaps the routing
   // kernels, which leave most of the machine idle; finalize waits for it.
+  // The W8A8 shared expert reads x as per-token int8 codes in token order: on the second
+  // stream it quantizes x itself, otherwise the expansion writes that copy as well.
   const bool merged = merge_shared(s);
+  int8_t* sh_xq = q8 ? at<int8_t>(ws, L.sh_xq) : nullptr;
+  float* sh_xs = q8 ? at<float>(ws, L.sh_xs) : nullptr;
   FfnIo sio{x, nullptr, nullptr, w->sh_w13, nullptr, w->sh_w2, nullptr, at<void>(ws, L.sh_out)};
-  moe_shape sh = *s;
-  sh.wt = s->act;
+  if (q8) {
+    sio.a = sh_xq;
+    sio.a_scale = sh_xs;
+    sio.w13_scale = w->sh_w13_scale;
+    sio.w2_scale = w->sh_w2_scale;
+  }
+  const moe_shape sh = shared_shape(s);
   SideFork sf;
   const bool forked = side && !merged;
   if (forked) {
@@ -625,6 +676,9 @@ static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const voi
         hipEventCreateWithFlags(&sf.join, hipEventDisableTiming) != hipSuccess ||
         hipEventRecord(sf.fork, stream) != hipSuccess ||
         hipStreamWaitEvent(side, sf.fork, 0) != hipSuccess)
+      return MOE_EHIP;
+    if (q8 && moe::launch_quant_rows_i8(x, s->T, s->H, 1, nullptr, nullptr, sh_xq, sh_xs,
+                                        side) != hipSuccess)
       return MOE_EHIP;
     st = run_ffn(&sh, 1, s->T, s->I_shared, sio, at<void>(ws, L.sh_ffn), side);
     if (st != MOE_OK) return st;
@@ -641,14 +695,15 @@ static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const voi
   int32_t* ssrc = at<int32_t>(ws, L.sorted_src);
   const bool gathered = gather_rows(s);
   st = init_routing_impl(s, x, idx, 0, gathered ? nullptr : at<void>(ws, L.ex),
-                         (fp8 || q8_weights(s)) ? at<float>(ws, L.ex_scale) : nullptr, eri, ssrc,
-                         at<int32_t>(ws, L.tpe), offs, ws, ws_bytes, stream, prof);
+                         (fp8 || q8) ? at<float>(ws, L.ex_scale) : nullptr, eri, ssrc,
+                         at<int32_t>(ws, L.tpe), offs, ws, ws_bytes, stream, prof,
+                         forked ? nullptr : sh_xq, forked ? nullptr : sh_xs);
   if (st != MOE_OK) return st;
   // routed experts as one grouped GEMM over the expert-sorted rows
   // The shared expert runs on every token ([MND §Expert Parallelism]: its output is
   // added); with the routed experts' shape it is one more group of the same launches.
   const int R = s->T * s->k;
-  FfnIo io{at<void>(ws, L.ex), (fp8 || q8_weights(s)) ? at<float>(ws, L.ex_scale) : nullptr, offs, w->w13,
+  FfnIo io{at<void>(ws, L.ex), (fp8 || q8) ? at<float>(ws, L.ex_scale) : nullptr, offs, w->w13,
            w->w13_scale, w->w2, w->w2_scale, at<void>(ws, L.y)};
   if (gathered) {
     io.a = x;

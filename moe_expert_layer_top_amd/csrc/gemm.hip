@@ -833,13 +833,16 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   if constexpr (Q8) {
     // W8A8 / W4A8 dequantization: value = acc (exact int32) * s_a[row] * s_w[channel], with the
     // activation scale of the unit's row and the per-output-channel weight scale
+    // (units of the alternate group take its own activation and weight scales)
     constexpr int HT = TN / 2;
-    const float* sw_base = p.b_scale + static_cast<long long>(un.group) * p.b_scale_group;
+    const float* sw_base =
+        alt ? p.b_scale2 : p.b_scale + static_cast<long long>(un.group) * p.b_scale_group;
+    const float* sa_base = alt ? p.a_scale2 : p.a_scale;
     float sa[TM];
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       const int row = 16 * (j * WM + wm) + crow;
-      sa[j] = (j < jcount && row < rows) ? p.a_scale[row0_e + row] : 0.f;
+      sa[j] = (j < jcount && row < rows) ? sa_base[row0_e + row] : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < TN; ++i) {

@@ -45,8 +45,10 @@ struct GemmArgs {
   int n_tiles;              // output tiles along N
   int splits;               // split-k factor
   int k_chunk;              // elements of K per split (multiple of the stage depth)
-  // Alternate group (bf16 DMA kernels only): units whose group equals alt_group read
-  // A2 (pitch lda2) and the single weight panel B2, and write C2 (pitch ldc2).  -1: none.
+  // Alternate group (bf16 and int8 DMA kernels): units whose group equals alt_group read
+  // A2 (pitch lda2) and the single weight panel B2 (pitch ldb, like the primary groups),
+  // and write C2 (pitch ldc2); int8 units take their scales from a_scale2 [rows] and
+  // b_scale2 [Brows].  -1: none.
   // Gathered activations (bf16 DMA kernels only): when set, row r of a unit of the
   // primary groups is row gather[row0 + r] / gather_div of A (x indexed by token,
   // through the slot order of the expert sort) instead of row row0 + r.
@@ -58,6 +60,8 @@ struct GemmArgs {
   const uint8_t* B2 = nullptr;
   void* C2 = nullptr;
   long long ldc2 = 0;
+  const float* a_scale2 = nullptr;
+  const float* b_scale2 = nullptr;
 };
 
 enum GemmCfg : int {
@@ -107,10 +111,12 @@ hipError_t launch_expand(const void* x, int T, int H, int k, int act_bytes, bool
                          const int32_t* eri, void* out, float* out_scale, hipStream_t st);
 
 // int8 per-row quantization of bf16 rows (W8A8 activations).  dst_rows [rows * k] or NULL
-// (in place); n_rows: device count of rows that hold data, or NULL (all).
+// (in place); n_rows: device count of rows that hold data, or NULL (all); tok_out /
+// tok_scale (or NULL): a second copy of every row's codes and scale, in place.
 hipError_t launch_quant_rows_i8(const void* src, int rows, int cols, int k, const int32_t* dst_rows,
                                 const int32_t* n_rows, int8_t* out, float* out_scale,
-                                hipStream_t st);
+                                hipStream_t st, int8_t* tok_out = nullptr,
+                                float* tok_scale = nullptr);
 
 hipError_t launch_finalize(const void* y, const void* skip, const float* w, const int32_t* eri,
                            void* out, int T, int H, int k, int act_bytes, hipStream_t st);

@@ -12,6 +12,8 @@
 //   route_place   each wavefront replays its segment in slot order and places every
 //                 slot at offsets[e] + (earlier slots of e), writing the src->dst
 //                 map (expanded_row_idx) and its inverse (sorted_src)
+// or, for up to 16 segments (decode batches), in one launch doing the same three passes
+// in one block (route_small),
 // and the copy kernel `expand_rows` reads each token row once and writes its k
 // copies (optionally quantized to fp8 with one scale per 1x128 vector).
 
@@ -19,6 +21,8 @@
 #include "kernels.h"
 
 namespace moe {
+
+constexpr size_t kSmallRouteLds = 60 * 1024;  // LDS bound of the single-launch routing
 
 // ------------------------------------------------------------------ top-k router
 // [MND §Expert Parallelism]: every token goes to k different routed experts whose
@@ -40,28 +44,35 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
   if (t >= T) return;
+  // Partial logits: every lane's VPL experts advance through the splits together, with
+  // kBatch splits of each in flight at once (about 32 loads per lane), and each expert's
+  // partials are added strictly in split order, so the sum does not depend on the batching.
+  constexpr int kBatch = VPL >= 16 ? 2 : VPL >= 8 ? 4 : 8;
+  const float* p = part + static_cast<long long>(t) * E + lane;
   float z[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) z[v] = v * 64 + lane < E ? p[v * 64] : -INFINITY;
+  for (int s0 = 1; s0 < splits; s0 += kBatch) {
+    float q[VPL][kBatch];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        q[v][i] = (v * 64 + lane < E && s0 + i < splits)
+                      ? p[(s0 + i) * split_stride + v * 64] : 0.f;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        if (s0 + i < splits) z[v] += q[v][i];
+  }
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     const int e = v * 64 + lane;
-    float l = -INFINITY;
     if (e < E) {
-      const float* p = part + static_cast<long long>(t) * E + e;
-      // partials are loaded 8 at a time (all in flight together) and added strictly in
-      // split order, so the sum does not depend on the batching
-      l = p[0];
-      for (int s0 = 1; s0 < splits; s0 += 8) {
-        float q[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = s0 + i < splits ? p[(s0 + i) * split_stride] : 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (s0 + i < splits) l += q[i];
-      }
-      if (logits_out) logits_out[static_cast<long long>(t) * E + e] = l;
-      if (bias) l += bias[e];
+      if (logits_out) logits_out[static_cast<long long>(t) * E + e] = z[v];
+      if (bias) z[v] += bias[e];
     }
-    z[v] = l;
   }
   // softmax statistics over all E experts, before any candidate is masked
   float zmax = 0.f, zsum = 1.f;
@@ -270,6 +281,32 @@ __global__ __launch_bounds__(256) void route_count_kernel(const int32_t* __restr
   if (lane == 0) seg_err[seg] = any_err ? 1 : 0;
 }
 
+// Exclusive prefix of one value per thread over a block of 1024 threads (16 waves),
+// in thread order; wsum: 16 ints of LDS.
+__device__ __forceinline__ int32_t block_excl_scan1024(int32_t run, int32_t* wsum) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int32_t incl = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  if (w == 0) {
+    int32_t v = lane < 16 ? wsum[lane] : 0;
+    int32_t inc = v;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int32_t u = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += u;
+    }
+    if (lane < 16) wsum[lane] = inc - v;  // exclusive wave base
+  }
+  __syncthreads();
+  return wsum[w] + incl - run;
+}
+
 // One block: base[seg*E+e] = offsets[e] + sum_{seg'<seg} counts[seg'*E+e] (in place),
 // tokens_per_expert[e] and expert_offsets[0..E].
 __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ counts, int nseg,
@@ -298,28 +335,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
       }
     }
   }
-  // exclusive scan of `run` over experts (block of 1024 threads, 16 waves)
-  const int lane = e & 63, w = e >> 6;
-  int32_t incl = run;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int32_t v = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += v;
-  }
-  if (lane == 63) wsum[w] = incl;
-  __syncthreads();
-  if (w == 0) {
-    int32_t v = lane < 16 ? wsum[lane] : 0;
-    int32_t inc = v;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const int32_t u = __shfl_up(inc, o, 64);
-      if (lane >= o) inc += u;
-    }
-    if (lane < 16) wsum[lane] = inc - v;  // exclusive wave base
-  }
-  __syncthreads();
-  const int32_t excl = wsum[w] + incl - run;
+  const int32_t excl = block_excl_scan1024(run, wsum);
   if (e == 0) *err_word = any_err;
   if (e < E) {
     tpe[e] = run;
@@ -379,12 +395,107 @@ __global__ __launch_bounds__(256) void route_place_kernel(const int32_t* __restr
   }
 }
 
+// Single-launch routing for a few segments (decode batches, one rank's share): wave w of
+// one 1024-thread block owns segment w.  Its keys stay in registers from the count to
+// the placement and the per-segment counts and their prefix stay in LDS, so the three
+// launches above become one; the order of the result is the same stable slot order.
+__global__ __launch_bounds__(1024) void route_small_kernel(const int32_t* __restrict__ ids,
+                                                           long long R, int e_base, int E, int bits,
+                                                           int nseg, int32_t* __restrict__ tpe,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ err_word,
+                                                           int32_t* __restrict__ eri,
+                                                           int32_t* __restrict__ sorted_src) {
+  extern __shared__ int32_t cnt_lds[];  // [nseg][E]
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t werr[16];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool owner = wave < nseg;
+  int32_t* cnt = cnt_lds + wave * E;
+  int err = 0;
+  const long long s0 = static_cast<long long>(wave) * kSegSlots;
+  uint32_t keys[kSegSlots / 64];
+  if (owner) {
+    for (int e = lane; e < E; e += 64) cnt[e] = 0;
+#pragma unroll
+    for (int it = 0; it < kSegSlots / 64; ++it)
+      keys[it] = local_key(ids, s0 + it * 64 + lane, R, e_base, E, &err);
+#pragma unroll
+    for (int it = 0; it < kSegSlots / 64; ++it) {
+      const long long s = s0 + it * 64 + lane;
+      const uint32_t key = keys[it];
+      const uint64_t active = __ballot(s < R);
+      if (active == 0) break;
+      const uint64_t peers = peer_mask(key, bits, active);
+      const bool leader = (s < R) && key < static_cast<uint32_t>(E) &&
+                          (__builtin_ctzll(peers) == lane);
+      if (leader) cnt[key] += __builtin_popcountll(peers);
+    }
+  }
+  const bool any_err = __ballot(err) != 0;
+  if (lane == 0) werr[wave] = any_err ? 1 : 0;
+  __syncthreads();
+  // per expert: exclusive prefix over segments, then over experts
+  const int e = threadIdx.x;
+  int32_t run = 0;
+  if (e < E) {
+    for (int w = 0; w < nseg; ++w) {
+      const int32_t c = cnt_lds[w * E + e];
+      cnt_lds[w * E + e] = run;
+      run += c;
+    }
+  }
+  const int32_t excl = block_excl_scan1024(run, wsum);
+  if (e < E) {
+    tpe[e] = run;
+    offsets[e] = excl;
+    if (e == E - 1) offsets[E] = excl + run;
+    for (int w = 0; w < nseg; ++w) cnt_lds[w * E + e] += excl;
+  }
+  if (e == 0) {
+    int32_t any = 0;
+    for (int w = 0; w < 16; ++w) any |= werr[w];
+    *err_word = any;
+  }
+  __syncthreads();
+  if (!owner) return;
+#pragma unroll
+  for (int it = 0; it < kSegSlots / 64; ++it) {
+    const long long s = s0 + it * 64 + lane;
+    const uint64_t active = __ballot(s < R);
+    if (active == 0) break;
+    const uint32_t key = keys[it];
+    const uint64_t peers = peer_mask(key, bits, active);
+    const bool valid = (s < R) && key < static_cast<uint32_t>(E);
+    int32_t pos = -1;
+    if (valid) {
+      const uint64_t lower = peers & ((1ull << lane) - 1ull);
+      pos = cnt[key] + __builtin_popcountll(lower);
+    }
+    // every lane has read cnt[] before the leaders advance it (in-order LDS within a wave)
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    if (valid && __builtin_ctzll(peers) == lane) cnt[key] += __builtin_popcountll(peers);
+    if (s < R) {
+      eri[s] = pos;
+      if (valid && sorted_src) sorted_src[pos] = static_cast<int32_t>(s);
+    }
+  }
+}
+
 hipError_t launch_routing(const int32_t* ids, long long R, int e_base, int E, int32_t* counts_ws,
                           int32_t* seg_err, int32_t* err_word, int32_t* eri, int32_t* sorted_src,
                           int32_t* tpe, int32_t* offsets, hipStream_t st) {
   const int nseg = static_cast<int>((R + kSegSlots - 1) / kSegSlots);
   int bits = 0;
   while ((1 << bits) <= E) ++bits;  // keys 0..E (E = invalid sentinel)
+  // up to 16 segments whose counts fit in 60 KB of LDS: one launch
+  const size_t small_lds = static_cast<size_t>(nseg) * E * sizeof(int32_t);
+  if (nseg <= 16 && small_lds <= kSmallRouteLds) {
+    route_small_kernel<<<1, 1024, small_lds, st>>>(ids, R, e_base, E, bits, nseg, tpe, offsets,
+                                                    err_word, eri, sorted_src);
+    return hipGetLastError();
+  }
   const size_t lds = 4 * static_cast<size_t>(E) * sizeof(int32_t);
   if (nseg > 0) {
     route_count_kernel<<<(nseg + 3) / 4, 256, lds, st>>>(ids, R, e_base, E, bits, counts_ws, nseg,
@@ -472,25 +583,55 @@ __global__ __launch_bounds__(256) void expand_quant_kernel(const uint16_t* __res
 // round-half-even(x * (127 / amax)) with scale amax / 127 (a zero row: scale 1, codes 0),
 // all in float32.  dst_rows [rows * k] sends row r to rows dst_rows[r*k + j] (the
 // token expansion; negative entries are skipped); NULL writes row r in place of itself.
-// n_rows (device, or NULL) bounds the rows that hold data.
+// tok_out / tok_scale (or NULL) receive one more copy of row r in place (the tokens in
+// their own order, for the shared expert).  n_rows (device, or NULL) bounds the rows
+// that hold data.  Rows of up to 8192 columns are read from memory once: each thread
+// keeps its 8-column vectors in registers between the amax and the coding pass.
+constexpr int kQuantKeep = 4;  // 8-column vectors a thread keeps (256 threads: 8192 columns)
+
+__device__ __forceinline__ float amax8_bf16(const uint4& raw, float amax) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[i] << 16)),
+                             fabsf(__uint_as_float(w[i] & 0xffff0000u))));
+  return amax;
+}
+
+__device__ __forceinline__ uint2 codes8_i8(const uint4& raw, float inv) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t q[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float v = __uint_as_float(i & 1 ? (w[i / 2] & 0xffff0000u) : (w[i / 2] << 16));
+    const float code = fminf(fmaxf(rintf(v * inv), -127.0f), 127.0f);
+    q[i / 4] |= (static_cast<uint32_t>(static_cast<int>(code)) & 0xffu) << (8 * (i % 4));
+  }
+  return make_uint2(q[0], q[1]);
+}
+
 __global__ __launch_bounds__(256) void quant_rows_i8_kernel(const uint16_t* __restrict__ src,
                                                             int cols, int k,
                                                             const int32_t* __restrict__ dst_rows,
                                                             const int32_t* __restrict__ n_rows,
                                                             int8_t* __restrict__ out,
-                                                            float* __restrict__ out_scale) {
+                                                            float* __restrict__ out_scale,
+                                                            int8_t* __restrict__ tok_out,
+                                                            float* __restrict__ tok_scale) {
   __shared__ float wmax[4];
   const int r = blockIdx.x;
   if (n_rows && r >= *n_rows) return;
   const uint16_t* row = src + static_cast<long long>(r) * cols;
   float amax = 0.f;
-  for (int c = threadIdx.x * 8; c < cols; c += 256 * 8) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(row + c);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint4 keep[kQuantKeep];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[i] << 16)), fabsf(__uint_as_float(w[i] & 0xffff0000u))));
+  for (int it = 0; it < kQuantKeep; ++it) {
+    const int c = (threadIdx.x + it * 256) * 8;
+    keep[it] = c < cols ? *reinterpret_cast<const uint4*>(row + c) : make_uint4(0, 0, 0, 0);
+    amax = amax8_bf16(keep[it], amax);
   }
+  for (int c = (threadIdx.x + kQuantKeep * 256) * 8; c < cols; c += 256 * 8)
+    amax = amax8_bf16(*reinterpret_cast<const uint4*>(row + c), amax);
   amax = wave_max(amax);
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
   __syncthreads();
@@ -498,38 +639,37 @@ __global__ __launch_bounds__(256) void quant_rows_i8_kernel(const uint16_t* __re
   const bool zero = amax == 0.f;
   const float scale = zero ? 1.0f : amax / 127.0f;
   const float inv = zero ? 0.0f : 127.0f / amax;
-  for (int c = threadIdx.x * 8; c < cols; c += 256 * 8) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(row + c);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-    uint32_t q[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float v = __uint_as_float(i & 1 ? (w[i / 2] & 0xffff0000u) : (w[i / 2] << 16));
-      const float code = fminf(fmaxf(rintf(v * inv), -127.0f), 127.0f);
-      q[i / 4] |= (static_cast<uint32_t>(static_cast<int>(code)) & 0xffu) << (8 * (i % 4));
-    }
-    const uint2 qq = make_uint2(q[0], q[1]);
+  auto emit = [&](int c, const uint2 qq) {
     for (int j = 0; j < k; ++j) {
       const int32_t d = dst_rows ? dst_rows[static_cast<long long>(r) * k + j] : r;
       if (d < 0) continue;
       *reinterpret_cast<uint2*>(out + static_cast<long long>(d) * cols + c) = qq;
     }
+    if (tok_out) *reinterpret_cast<uint2*>(tok_out + static_cast<long long>(r) * cols + c) = qq;
+  };
+#pragma unroll
+  for (int it = 0; it < kQuantKeep; ++it) {
+    const int c = (threadIdx.x + it * 256) * 8;
+    if (c < cols) emit(c, codes8_i8(keep[it], inv));
   }
+  for (int c = (threadIdx.x + kQuantKeep * 256) * 8; c < cols; c += 256 * 8)
+    emit(c, codes8_i8(*reinterpret_cast<const uint4*>(row + c), inv));
   if (threadIdx.x == 0) {
     for (int j = 0; j < k; ++j) {
       const int32_t d = dst_rows ? dst_rows[static_cast<long long>(r) * k + j] : r;
       if (d >= 0) out_scale[d] = scale;
     }
+    if (tok_scale) tok_scale[r] = scale;
   }
 }
 
 hipError_t launch_quant_rows_i8(const void* src, int rows, int cols, int k, const int32_t* dst_rows,
                                 const int32_t* n_rows, int8_t* out, float* out_scale,
-                                hipStream_t st) {
+                                hipStream_t st, int8_t* tok_out, float* tok_scale) {
   if (rows == 0) return hipSuccess;
-  if (cols % 8) return hipErrorInvalidValue;
+  if (cols % 8 || (tok_out == nullptr) != (tok_scale == nullptr)) return hipErrorInvalidValue;
   quant_rows_i8_kernel<<<rows, 256, 0, st>>>(static_cast<const uint16_t*>(src), cols, k, dst_rows,
-                                             n_rows, out, out_scale);
+                                             n_rows, out, out_scale, tok_out, tok_scale);
   return hipGetLastError();
 }
 

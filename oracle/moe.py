@@ -417,6 +417,19 @@ def expert_weights_f64(inp: dict):
     return get
 
 
+def shared_expert(x: np.ndarray, inp: dict) -> np.ndarray:
+    """The shared expert on float64 tokens x: the same SwiGLU FFN with the shared
+    weights ([MND §Expert Parallelism]).  Beside W8A8 or W4A8 routed experts it is
+    W8A8 ([V32 §quantization strategy] quantizes the shared expert W8A8 in both): per-
+    token int8 tokens, int8 weights with per-channel scales, h requantized per row."""
+    cfg = inp["cfg"]
+    if cfg.sh_wt == "int8":
+        xq, xs = quant_per_token_int8(x.astype(np.float32))
+        return swiglu_ffn(dequant_rows(xq, xs), dequant_rows(inp["sh_w13"], inp["sh_w13_scale"]),
+                          dequant_rows(inp["sh_w2"], inp["sh_w2_scale"]), quant_h="int8")
+    return swiglu_ffn(x, to_f64(inp["sh_w13"], cfg.sh_wt), to_f64(inp["sh_w2"], cfg.sh_wt))
+
+
 def moe_layer(inp: dict, logits32_override=None, router=None) -> dict:
     """The whole layer on one GPU's share, step by step.
 
@@ -472,7 +485,7 @@ def moe_layer(inp: dict, logits32_override=None, router=None) -> dict:
                     quant_h="int8" if int8 else fp8)
     res["y_sorted"] = y
     sx = to_f64(inp["x_local"], cfg.act) if cfg.pretagged else x
-    s = swiglu_ffn(sx, to_f64(inp["sh_w13"], cfg.act), to_f64(inp["sh_w2"], cfg.act))
+    s = shared_expert(sx, inp)
     res["shared"] = s
     if cfg.pretagged:
         res["y_arrival"] = finalize(y, rt["expanded_row_idx"], 1)

@@ -64,6 +64,12 @@ class MoEConfig:
     def shared_rows(self) -> int:
         return self.T_local if self.pretagged else self.T
 
+    @property
+    def sh_wt(self) -> str:
+        """Shared-expert weight dtype: int8 (W8A8) beside W8A8 or W4A8 routed experts,
+        else the activation dtype (bf16 also beside fp8 routed experts)."""
+        return "int8" if self.wt in ("int8", "int4") else self.act
+
 
 # Calibrated by oracle/calibrate_bias.py so that the most-loaded expert receives
 # about 8x the mean rows (max/mean in [7.5, 8.5]) at the full T=16384 workload.

@@ -73,7 +73,7 @@ def upload_layer(cfg: MoEConfig, device="cuda") -> dict:
         d["x_local"] = to_dev(inputs.local_tokens(cfg), device)
     else:
         d["w_gate"] = to_dev(inputs.gate_weight(cfg), device)
-    d["sh_w13"] = to_dev(inputs.shared_w13(cfg), device)
-    d["sh_w2"] = to_dev(inputs.shared_w2(cfg), device)
+    for name, v in inputs.shared_weights(cfg).items():
+        d[name] = to_dev(v, device)
     d.update(upload_experts(cfg, device))
     return d

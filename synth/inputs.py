@@ -26,6 +26,8 @@ Recipe
   scales drawn as ``std * 4.2 / 7 * 2**U(-0.5, 0.5)``.
 * Expert-popularity bias (decode / skewed workloads): a seeded permutation ranks
   the experts, p_e is proportional to rank_e**-s, and b_e = alpha * ln p_e.
+* The shared expert beside int8 or int4 experts is int8 (W8A8), drawn like the int8
+  expert weights from its own streams; otherwise it is in the activation dtype.
 * Pretagged rows (expert-parallel rank share): ids i.i.d. uniform over the
   rank's experts [e_base, e_base + E).
 
@@ -44,7 +46,7 @@ from scipy.special import ndtri
 from .configs import MoEConfig
 
 # tensor ids folded into the seed
-X, WG, W13, W2, SW13, SW2, BIAS, IDS, XLOCAL, W13S, W2S, PERM = range(1, 13)
+X, WG, W13, W2, SW13, SW2, BIAS, IDS, XLOCAL, W13S, W2S, PERM, SW13S, SW2S = range(1, 15)
 SHARED = 0xFFFF  # "expert" slot used for non-expert tensors
 
 _FP8_RANGE_SIGMA = 4.2
@@ -219,13 +221,33 @@ def expert_w2(cfg: MoEConfig, e: int):
     return _normal(cfg, cfg.wt, stream(cfg, W2, e), shape, cfg.w_std)
 
 
-def shared_w13(cfg: MoEConfig) -> np.ndarray:
-    """Shared expert [2*I_shared, H], always in the activation dtype."""
-    return _normal(cfg, cfg.act, stream(cfg, SW13), (2 * cfg.I_shared, cfg.H), cfg.w_std)
+def shared_w13(cfg: MoEConfig):
+    """Shared expert [2*I_shared, H] in cfg.sh_wt: the activation dtype, or for int8
+    (codes, scales [2*I_shared]) drawn like the int8 expert weights."""
+    shape = (2 * cfg.I_shared, cfg.H)
+    if cfg.sh_wt == "int8":
+        return normal_int8_channels(stream(cfg, SW13), stream(cfg, SW13S), shape, cfg.w_std)
+    return _normal(cfg, cfg.sh_wt, stream(cfg, SW13), shape, cfg.w_std)
 
 
-def shared_w2(cfg: MoEConfig) -> np.ndarray:
-    return _normal(cfg, cfg.act, stream(cfg, SW2), (cfg.H, cfg.I_shared), cfg.w_std)
+def shared_w2(cfg: MoEConfig):
+    """Shared expert down projection [H, I_shared]; int8: (codes, scales [H])."""
+    shape = (cfg.H, cfg.I_shared)
+    if cfg.sh_wt == "int8":
+        return normal_int8_channels(stream(cfg, SW2), stream(cfg, SW2S), shape, cfg.w_std)
+    return _normal(cfg, cfg.sh_wt, stream(cfg, SW2), shape, cfg.w_std)
+
+
+def shared_weights(cfg: MoEConfig) -> dict:
+    """sh_w13, sh_w2 and, for int8, sh_w13_scale and sh_w2_scale."""
+    d = {}
+    for name, fn in (("sh_w13", shared_w13), ("sh_w2", shared_w2)):
+        v = fn(cfg)
+        if cfg.sh_wt == "int8":
+            d[name], d[name + "_scale"] = v
+        else:
+            d[name] = v
+    return d
 
 
 def _workers() -> int:
@@ -252,8 +274,7 @@ def layer_inputs(cfg: MoEConfig, with_experts: bool = True) -> dict:
         d["x_local"] = local_tokens(cfg)
     else:
         d["w_gate"] = gate_weight(cfg)
-    d["sh_w13"] = shared_w13(cfg)
-    d["sh_w2"] = shared_w2(cfg)
+    d.update(shared_weights(cfg))
     if with_experts:
         w13 = [None] * cfg.E
         w2 = [None] * cfg.E

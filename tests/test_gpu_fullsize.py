@@ -68,8 +68,7 @@ def test_full_layer_sampled(M, name):
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
     logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
     ws = torch.empty(M.moe_workspace_bytes(s), dtype=torch.uint8, device="cuda")
-    W = M.weights(g["w_gate"], g["w13"], g["w2"], g["sh_w13"], g["sh_w2"], g.get("w13_scale"),
-                  g.get("w2_scale"), g.get("bias"))
+    W = M.weights_of(g)
     say("full layer", name, "run")
     M.moe_layer(s, W, g["x"], out, idx, w, logits, ws)
     torch.cuda.synchronize()
@@ -119,7 +118,7 @@ def test_full_layer_sampled(M, name):
     experts = sorted(set(i_gpu[S].reshape(-1).tolist()))
     say("full layer", name, f"oracle on tokens {S.tolist()} ({len(experts)} experts)")
     d = {"cfg": dataclasses.replace(cfg, T=len(S)), "x": xs, "w_gate": inputs.gate_weight(cfg),
-         "bias": bias, "sh_w13": inputs.shared_w13(cfg), "sh_w2": inputs.shared_w2(cfg)}
+         "bias": bias, **inputs.shared_weights(cfg)}
     d.update(expert_dict(cfg, experts))
     ref = O.moe_layer(d, logits32_override=l_gpu[S])
     err = max_row_rel_err(act_to_f64(out, cfg.act)[S], ref["out"])

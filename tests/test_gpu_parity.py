@@ -239,8 +239,7 @@ def run_layer(M, cfg, g, T=None):
     idx = poison_(torch.empty((T, cfg.k), dtype=torch.int32, device="cuda"))
     w = poison_(torch.empty((T, cfg.k), dtype=torch.float32, device="cuda"))
     logits = poison_(torch.empty((T, cfg.E), dtype=torch.float32, device="cuda"))
-    W = M.weights(g["w_gate"], g["w13"], g["w2"], g["sh_w13"], g["sh_w2"], g.get("w13_scale"),
-                  g.get("w2_scale"), g.get("bias"))
+    W = M.weights_of(g)
     M.moe_layer(s, W, g["x"], out, idx, w, logits, ws_for(M, s))
     torch.cuda.synchronize()
     return out, idx, w, logits
@@ -327,6 +326,32 @@ def test_all_tokens_to_one_expert(M):
     torch.cuda.synchronize()
     ref = O.swiglu_ffn(O.to_f64(d["x"], cfg.act), O.to_f64(d["w13"][3], cfg.wt), O.to_f64(d["w2"][3], cfg.wt))
     assert max_row_rel_err(act_to_f64(y, cfg.act), ref) <= tol_of(cfg)
+
+
+# Routing runs in one launch for up to 16 segments of 1024 slots whose per-segment counts
+# fit in 60 KB of LDS, and in three launches otherwise: both sides of each boundary, with a
+# skewed expert popularity (one expert takes a quarter of the slots) and two invalid ids.
+@pytest.mark.parametrize("T,k,E", [(2048, 8, 256), (2049, 8, 256), (900, 16, 1024),
+                                   (1000, 16, 1024), (3, 5, 7), (5000, 1, 1), (40000, 1, 1)])
+def test_routing_single_and_three_launch(M, T, k, E):
+    cfg, _, g = case("p4_decode_bf16")
+    say("routing paths", T, k, E)
+    rng = np.random.default_rng(1000 + T * 31 + k * 7 + E)
+    ids = rng.integers(0, E, (T, k))
+    ids[rng.random(T) < 0.25, 0] = 0                 # a quarter of the tokens pick expert 0
+    ids[T // 2, k - 1] = E                            # two slots outside the local experts
+    ids[T - 1, 0] = -1
+    ids = np.ascontiguousarray(ids + cfg.e_base, dtype=np.int32)
+    out = run_init_routing(M, cfg, g, to_dev(ids), T, k, E, cfg.e_base, with_rows=False)
+    ref = O.init_routing(ids, E, cfg.e_base)
+    assert ref["n_invalid"] == (1 if (T // 2, k - 1) == (T - 1, 0) else 2)
+    assert np.array_equal(host(out["tpe"]), ref["tokens_per_expert"])
+    assert np.array_equal(host(out["offs"]), ref["expert_offsets"])
+    assert np.array_equal(host(out["eri"]), ref["expanded_row_idx"])
+    n = int(ref["expert_offsets"][-1])
+    assert np.array_equal(host(out["ssrc"])[:n], ref["sorted_src"])
+    assert M.moe_get_error(out["ws"]) == M.MOE_EDEVICE
+    assert M.moe_get_error(out["ws"]) == M.MOE_OK
 
 
 def test_invalid_ids_are_flagged_and_dropped(M):

@@ -95,8 +95,7 @@ def test_layer_router(M, name, rname):
     idx = poison_(torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda"))
     w = poison_(torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda"))
     logits = poison_(torch.empty((cfg.T, cfg.E), dtype=torch.float32, device="cuda"))
-    W = M.weights(g["w_gate"], g["w13"], g["w2"], g["sh_w13"], g["sh_w2"], g.get("w13_scale"),
-                  g.get("w2_scale"), g.get("bias"))
+    W = M.weights_of(g)
     M.moe_layer_ex(s, M.router(**r), W, g["x"], out, idx, w, logits, ws_for(M, s), side=torch.cuda.Stream())
     torch.cuda.synchronize()
     ref = O.moe_layer(d, logits32_override=host(logits), router=r)

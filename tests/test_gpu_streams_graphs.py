@@ -17,7 +17,10 @@ pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
 
 # fp32 and fp8 layers and I_shared != I run the shared expert in launches of its own (the
 # side stream is used); p2 has it inside the routed launches (the side stream is not).
-OVERLAP = ["p1_small_fp32", "p2_prefill_bf16", "p2c_prefill_bf16", "p5_skewed_fp8"]
+# p6: the int8 shared expert is a group of the routed launches (side unused); p9: the int8
+# shared expert of a W4A8 layer quantizes x itself on the side stream
+OVERLAP = ["p1_small_fp32", "p2_prefill_bf16", "p2c_prefill_bf16", "p5_skewed_fp8",
+           "p6_prefill_w8a8", "p9_decode_w4a8"]
 
 
 @pytest.fixture(scope="module")
@@ -45,8 +48,7 @@ def layer_bufs(M, cfg, T=None):
 
 
 def weights_of(M, g):
-    return M.weights(g["w_gate"], g["w13"], g["w2"], g["sh_w13"], g["sh_w2"], g.get("w13_scale"),
-                     g.get("w2_scale"), g.get("bias"))
+    return M.weights_of(g)
 
 
 def outputs(b):
@@ -93,7 +95,8 @@ def new_x(cfg, g, seed):
 
 
 @pytest.mark.parametrize("name,overlap", [("p2_prefill_bf16", False), ("p5_skewed_fp8", False),
-                                          ("p5_skewed_fp8", True), ("p4_decode_bf16", False)])
+                                          ("p5_skewed_fp8", True), ("p4_decode_bf16", False),
+                                          ("p6_prefill_w8a8", False), ("p9_decode_w4a8", True)])
 def test_layer_graph_replay(M, name, overlap):
     """Capture the layer once, then replay it on new inputs written into the captured
     input buffer, with eager calls and synchronizations between replays; every replay

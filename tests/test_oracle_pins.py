@@ -501,6 +501,42 @@ def test_int8_gemm_is_integer_product_times_scales():
                        rtol=1e-13, atol=0)
 
 
+def _shared_unquantized(d, x):
+    """The int8 shared expert on exact activations: dequantized weights, no token or h
+    quantization (a plain SwiGLU FFN)."""
+    w13 = d["sh_w13"].astype(np.float64) * d["sh_w13_scale"].astype(np.float64)[:, None]
+    w2 = d["sh_w2"].astype(np.float64) * d["sh_w2_scale"].astype(np.float64)[:, None]
+    I = w13.shape[0] // 2
+    g, u = x @ w13[:I].T, x @ w13[I:].T
+    return (g / (1.0 + np.exp(-g)) * u) @ w2.T
+
+
+@pytest.mark.parametrize("name", ["p6_prefill_w8a8", "p9_decode_w4a8"])
+def test_shared_expert_is_w8a8_beside_int8_and_int4_experts(name):
+    """[V32 §quantization strategy]: the shared expert is W8A8 whether the routed experts
+    are W8A8 or W4A8.  Its weights are int8 codes with one scale per output channel, and
+    its output stays within the int8 tolerance of the same FFN on exact activations; the
+    quantization does change it (the error is not zero)."""
+    cfg = configs.get(name)
+    d = inputs.layer_inputs(cfg)
+    assert cfg.sh_wt == "int8"
+    assert d["sh_w13"].dtype == np.int8 and d["sh_w13"].shape == (2 * cfg.I_shared, cfg.H)
+    assert d["sh_w2"].dtype == np.int8 and d["sh_w2"].shape == (cfg.H, cfg.I_shared)
+    assert d["sh_w13_scale"].shape == (2 * cfg.I_shared,) and d["sh_w2_scale"].shape == (cfg.H,)
+    x = moe.to_f64(d["x"], cfg.act)
+    got = moe.shared_expert(x, d)
+    ref = _shared_unquantized(d, x)
+    rel = (np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1))
+    assert rel.max() < 6e-2 and rel.max() > 1e-4, rel.max()
+
+
+def test_shared_expert_stays_in_activation_dtype_elsewhere():
+    for name in ("p2_prefill_bf16", "p5_skewed_fp8", "p1_small_fp32"):
+        cfg = configs.get(name)
+        assert cfg.sh_wt == cfg.act
+        assert "sh_w13_scale" not in inputs.shared_weights(cfg)
+
+
 def test_w8a8_layer_expanded_rows_and_tolerance():
     """The W8A8 layer's expanded rows are each token's per-token codes, and the layer's
     output stays within the int8 tolerance of the same layer on unquantized
@@ -515,7 +551,7 @@ def test_w8a8_layer_expanded_rows_and_tolerance():
     x = moe.to_f64(d["x"], cfg.act)
     a = x[tok]
     y = moe.grouped_ffn(a, r["expert_offsets"], moe.expert_weights_f64(d), quant_h=False)
-    out = moe.finalize(y, r["expanded_row_idx"], cfg.k, r["topk_w"], r["shared"])
+    out = moe.finalize(y, r["expanded_row_idx"], cfg.k, r["topk_w"], _shared_unquantized(d, x))
     rel = (np.abs(out - r["out"]).max(axis=1) / np.abs(out).max(axis=1)).max()
     assert rel < 6e-2, rel
 
@@ -554,7 +590,7 @@ def test_w4a8_layer_weights_and_tolerance():
     r = moe.moe_layer(d)
     x = moe.to_f64(d["x"], cfg.act)
     y = moe.grouped_ffn(x[r["sorted_src"] // cfg.k], r["expert_offsets"], moe.expert_weights_f64(d), quant_h=False)
-    out = moe.finalize(y, r["expanded_row_idx"], cfg.k, r["topk_w"], r["shared"])
+    out = moe.finalize(y, r["expanded_row_idx"], cfg.k, r["topk_w"], _shared_unquantized(d, x))
     rel = (np.abs(out - r["out"]).max(axis=1) / np.abs(out).max(axis=1)).max()
     assert rel < 6e-2, rel
 
