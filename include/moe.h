@@ -255,7 +255,8 @@ enum {
   MOE_EV_EXPAND = 4,     /* after the row expansion (+ fp8 quantization)        */
   MOE_EV_PLAN = 5,       /* after the grouped-GEMM unit table                   */
   MOE_EV_FFN1 = 6,       /* after the routed gate/up GEMM with SwiGLU           */
-  MOE_EV_FFN2 = 7,       /* after the routed down GEMM                          */
+  MOE_EV_FFN2 = 7,       /* after the routed down GEMM (int8 / int4 experts: and the
+                            per-row quantization of h before it)                */
   MOE_EV_SHARED = 8,     /* after both shared-expert GEMMs                      */
   MOE_EV_FINALIZE = 9,   /* after the un-permute + combine                      */
   MOE_EV_COUNT = 10

@@ -391,7 +391,9 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
   hipError_t e = i8 ? moe::launch_gemm_i8(cfg, moe::EPI_SWIGLU_BF16, w4, g1, mu, st)
                     : moe::launch_gemm(cfg, fp8 ? moe::EPI_SWIGLU_FP8 : moe::EPI_SWIGLU_BF16, fp8,
                                        g1, mu, st);
-  if (e != hipSuccess) return MOE_EHIP;
+  // the ffn1 mark closes the first GEMM alone; h's int8 quantization (W8A8) is timed
+  // with the down projection that consumes it
+  if (e != hipSuccess || prof.mark(ev_ffn1, st) != hipSuccess) return MOE_EHIP;
   if (i8) {
     e = moe::launch_quant_rows_i8(at<uint8_t>(ws, L.h), R_max, I, 1, nullptr,
                                   io.offsets ? io.offsets + G : nullptr, at<int8_t>(ws, L.hq),
@@ -401,7 +403,6 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
                                     at<int8_t>(ws, L.h2q), at<float>(ws, L.h2_scale), st);
     if (e != hipSuccess) return MOE_EHIP;
   }
-  if (prof.mark(ev_ffn1, st) != hipSuccess) return MOE_EHIP;
   GemmArgs g2 = g1;
   g2.gather = nullptr;
   g2.gather_div = 1;

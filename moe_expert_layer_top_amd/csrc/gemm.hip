@@ -418,14 +418,23 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* lds_chunk) {
 // Same as dma16 with the address split into a wave-uniform 64-bit base (scalar
 // registers) and a 32-bit per-lane byte offset: the per-lane address needs one VGPR
 // instead of two and no 64-bit add.
+// NT: non-temporal (streaming) cache policy, for data read once.
+template <bool NT = false>
 __device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint8_t* lds_chunk) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
           (__attribute__((address_space(3))) uint8_t*)lds_chunk)));
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(off), "s"(base), "s"(m0)
-               : "memory", "m0");
+  if constexpr (NT) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(off), "s"(base), "s"(m0)
+                 : "memory", "m0");
+  } else {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(m0)
+                 : "memory", "m0");
+  }
 }
 
 // 4 bytes per lane (global_load_lds_dword) into lds_chunk + 4 * lane; base/offset form.
@@ -491,6 +500,11 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   constexpr int LMAX = (LD_ALL + NW - 1) / NW;   // DMA instructions per wave per stage
   constexpr int LREM = LD_ALL % NW;              // waves < LREM issue LMAX, others LMAX-1
   constexpr int STAGE = BM * ROWB + BN * ROWB_B;
+  // Weights read by this unit alone stream through the caches non-temporally (they are
+  // not read again); weights that other units of the group also read stay cacheable.
+  // Packed int4 rows are 64-byte half lines per stage: never non-temporal, so that the
+  // line's other half, read one stage later, still hits.
+  constexpr bool NTW_OK = !W4 && !UNIFORM;
   constexpr bool SWIGLU = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_FP8);
   // fp8: one stage = one 128-wide K block of e4m3 codes; its 1x128 activation scales and
   // the two 128x128 weight-block scales of the tile come into LDS with the stage.
@@ -564,6 +578,8 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
                           static_cast<long long>(k0) * EB / (W4 ? 2 : 1);
   void* const cptr = alt ? p.C2 : p.C;
   const long long ldc = alt ? p.ldc2 : p.ldc;
+  bool ntb = false;   // wave-uniform: stream this unit's weights non-temporally
+  if constexpr (!UNIFORM) ntb = (un.flags & kUnitSoleReader) != 0;
 
   // DMA plan.  Every wavefront issues A_PER activation chunks (q = wave + i * NW) and
   // B_PER weight chunks (q = wave + i * NW) per stage; both counts are compile-time, so
@@ -646,8 +662,13 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
     const uint8_t* bk = b_base + static_cast<long long>(step) * ROWB_B;
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) dma16s(ak, lane_off_of(i), buf + (wave + i * NW) * 1024);
+    if (NTW_OK && ntb) {
 #pragma unroll
-    for (int i = 0; i < B_PER; ++i) dma16s(bk, lane_off_of(A_PER + i), buf + BM * ROWB + (wave + i * NW) * 1024);
+      for (int i = 0; i < B_PER; ++i) dma16s<true>(bk, lane_off_of(A_PER + i), buf + BM * ROWB + (wave + i * NW) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < B_PER; ++i) dma16s<false>(bk, lane_off_of(A_PER + i), buf + BM * ROWB + (wave + i * NW) * 1024);
+    }
     if constexpr (FP8) {
       if (wave < BM / 64) dma4s(sc_base + step, lane_off_of(LMAX), reinterpret_cast<uint8_t*>(&sa_st[b & 1][64 * wave]));
       else if (wave == BM / 64) dma4s(sc_base + step, lane_off_of(LMAX), reinterpret_cast<uint8_t*>(&sb_st[b & 1][0]));
@@ -1076,7 +1097,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
         un.group = G;
         un.row0 = i * per_x;
         un.rows = min(per_x, extra_rows - i * per_x);
-        un.pad = 0;
+        un.flags = nx == 1 ? kUnitSoleReader : 0;
         if (base + i < cap) units[base + i] = un;
       }
       if (nu > 0) {
@@ -1086,7 +1107,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
           un.group = g;
           un.row0 = start + i * per;
           un.rows = min(per, n - i * per);
-          un.pad = 0;
+          un.flags = nu == 1 ? kUnitSoleReader : 0;
           if (base + x1 + i < cap) units[base + x1 + i] = un;
         }
       }

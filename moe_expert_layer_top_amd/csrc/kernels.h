@@ -10,8 +10,11 @@ constexpr int kSegSlots = 1024;  // routing slots per counting-sort segment (one
 
 // Unit of grouped-GEMM work: rows [row0, row0 + rows) of group `group`.
 struct Unit {
-  int32_t group, row0, rows, pad;
+  int32_t group, row0, rows, flags;
 };
+// Unit::flags bit: no other unit reads this group's weights (the weight panel is streamed
+// once, with a non-temporal cache policy)
+constexpr int32_t kUnitSoleReader = 1;
 
 enum Epilogue : int {
   EPI_SWIGLU_BF16 = 0,  // h = silu(gate) * up, stored bf16
