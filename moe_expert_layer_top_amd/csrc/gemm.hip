@@ -474,8 +474,8 @@ __device__ __forceinline__ i32x4 unpack_int4x16(uint2 pk) {
 
 template <int ROWB>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (ROWB == 128) return row & 7;
-  else return (row >> 1) & 3;
+  if constexpr (ROWB >= 128) return row & 7;   // 128- and 256-byte rows: 8 rows, 8 slots
+  else return (row >> 1) & 3;                  // 64-byte rows: 2 rows per 128-byte window
 }
 
 template <int WM, int WN, int TM, int TN, int EPI, bool UNIFORM, int ROWB, int NST, bool FP8,
@@ -502,9 +502,9 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   constexpr int STAGE = BM * ROWB + BN * ROWB_B;
   // Weights read by this unit alone stream through the caches non-temporally (they are
   // not read again); weights that other units of the group also read stay cacheable.
-  // Packed int4 rows are 64-byte half lines per stage: never non-temporal, so that the
-  // line's other half, read one stage later, still hits.
-  constexpr bool NTW_OK = !W4 && !UNIFORM;
+  // Packed int4 rows of a 128-element stage are 64-byte half lines: not non-temporal, so
+  // that the line's other half, read one stage later, still hits.
+  constexpr bool NTW_OK = !UNIFORM && ROWB_B >= 128;
   constexpr bool SWIGLU = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_FP8);
   // fp8: one stage = one 128-wide K block of e4m3 codes; its 1x128 activation scales and
   // the two 128x128 weight-block scales of the tile come into LDS with the stage.
@@ -516,7 +516,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   // with the activation row's scale and the weight column's scale
   static_assert(!Q8 || (!FP8 && !UNIFORM && (EPI == EPI_SWIGLU_BF16 || EPI == EPI_STORE_BF16)),
                 "int8 operands: grouped launches with a bf16 result");
-  static_assert(!W4 || ROWB == 128, "int4 weights: 64-byte weight rows per stage");
+  static_assert(!W4 || ROWB == 128 || ROWB == 256, "int4 weights: 64- or 128-byte weight rows per stage");
   static_assert(BM % RPC == 0 && BN % RPC_B == 0, "tiles are whole DMA chunks");
   static_assert(NST >= 2 && NST <= 4, "ring depth");
   static_assert(!SWIGLU || TN % 2 == 0, "swiglu needs gate/up tile pairs");
@@ -1225,6 +1225,7 @@ hipError_t launch_gemm(GemmCfg cfg, Epilogue epi, bool fp8, const GemmArgs& a, i
 hipError_t launch_gemm_i8(GemmCfg cfg, Epilogue epi, bool w4, const GemmArgs& a, int max_units,
                           hipStream_t st) {
   if (a.uniform_rows > 0 || !a.a_scale || !a.b_scale) return hipErrorInvalidValue;
+  if (a.splits != 1 || a.k_chunk != a.K || a.K % 128) return hipErrorInvalidValue;
   if (epi != EPI_SWIGLU_BF16 && epi != EPI_STORE_BF16) return hipErrorInvalidValue;
   const bool sw = epi == EPI_SWIGLU_BF16;
   switch (cfg) {
@@ -1236,6 +1237,11 @@ hipError_t launch_gemm_i8(GemmCfg cfg, Epilogue epi, bool w4, const GemmArgs& a,
       return sw ? go_dma<4, 2, 5, 8, EPI_SWIGLU_BF16, 128, 2, false, true>(a, max_units, st)
                 : go_dma<4, 2, 5, 8, EPI_STORE_BF16, 128, 2, false, true>(a, max_units, st);
     case CFG_SMALL:
+      if (w4 && a.k_chunk % 256 == 0) {
+        // 256-element stages: whole 128-byte lines of packed weights, 3-deep ring (40 KB stages)
+        return sw ? go_dma<1, 4, 2, 4, EPI_SWIGLU_BF16, 256, 3, false, false, true>(a, max_units, st)
+                  : go_dma<1, 4, 2, 4, EPI_STORE_BF16, 256, 3, false, false, true>(a, max_units, st);
+      }
       if (w4) {
         return sw ? go_dma<1, 4, 2, 4, EPI_SWIGLU_BF16, 128, 4, false, false, true>(a, max_units, st)
                   : go_dma<1, 4, 2, 4, EPI_STORE_BF16, 128, 4, false, false, true>(a, max_units, st);

@@ -154,6 +154,11 @@ CONFIGS = {
         name="p9_decode_w4a8", cid=19, T=24, H=512, E=64, k=8, I=256, I_shared=256,
         act="bf16", wt="int4", zipf_s=1.1, bias_alpha=0.5,
         description="reduced W4A8 decode"),
+    "p9b_decode_w4a8": MoEConfig(
+        name="p9b_decode_w4a8", cid=29, T=24, H=384, E=64, k=8, I=384, I_shared=384,
+        act="bf16", wt="int4", zipf_s=1.1, bias_alpha=0.5,
+        description="reduced W4A8 decode with H and I multiples of 128 but not of 256 "
+                    "(the 128-element weight stages)"),
     "p1_small_fp32": MoEConfig(
         name="p1_small_fp32", cid=11, T=150, H=384, E=12, k=3, I=256, I_shared=128,
         act="f32", wt="f32", x_std=0.02, wg_std=0.02, w_std=0.02,
@@ -165,7 +170,8 @@ FULL_CONFIGS = ["c1_tiny_fp32", "c2_prefill_bf16", "c3_ep_rank_bf16",
                 "c8_decode_w4a8"]
 SMALL_CONFIGS = ["c1_tiny_fp32", "p1_small_fp32", "p2_prefill_bf16", "p2b_prefill_bf16",
                  "p2c_prefill_bf16", "p3_ep_rank_bf16", "p4_decode_bf16", "p5_skewed_fp8",
-                 "p6_prefill_w8a8", "p7_decode_w8a8", "p8_prefill_w4a8", "p9_decode_w4a8"]
+                 "p6_prefill_w8a8", "p7_decode_w8a8", "p8_prefill_w4a8", "p9_decode_w4a8",
+                 "p9b_decode_w4a8"]
 
 
 def get(name: str, **overrides) -> MoEConfig:
