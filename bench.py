@@ -112,16 +112,22 @@ def account(cfg, tpe) -> dict:
     return acc
 
 
+def layer_plan(cfg) -> dict:
+    """The library's own launch plan for the workload's shape (moe_layer_plan_of)."""
+    import moe_expert_layer_top_amd as M
+    return M.moe_layer_plan_of(M.shape_of(cfg))
+
+
 def shared_is_merged(cfg) -> bool:
     """moe_layer runs the shared expert as one more group of the routed grouped-GEMM
-    launches when it has the routed experts' shape and dtype (bf16 or int8, I_shared == I)."""
-    return cfg.act == "bf16" and cfg.wt in ("bf16", "int8") and cfg.I_shared == cfg.I
+    launches (same shape and dtype, routed GEMMs not split along K)."""
+    return bool(layer_plan(cfg)["shared_merged"])
 
 
 def gathers_rows(cfg) -> bool:
     """bf16 layers never write the expanded rows: the first expert GEMM reads each routed
-    row from x through the sort's slot order (32-bit offsets: T*H*2 < 4 GiB)."""
-    return cfg.act == "bf16" and cfg.wt == "bf16" and 2 * cfg.T * cfg.H < (1 << 32)
+    row from x through the sort's slot order."""
+    return bool(layer_plan(cfg)["rows_gathered"])
 
 
 def launch_accounting(cfg, acc: dict) -> dict:

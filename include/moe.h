@@ -86,6 +86,20 @@ size_t moe_workspace_bytes(const moe_shape* s);
 /* Workspace bytes needed by moe_grouped_ffn for G groups and at most R_max rows. */
 size_t moe_grouped_ffn_workspace_bytes(const moe_shape* s, int32_t G, int32_t R_max);
 
+/* How moe_layer runs shape `s`: a host-side description of its launch plan, for callers
+ * that account work per launch (no device work, no allocation).  The routed experts'
+ * GEMMs split their reduction into ffn1_splits / ffn2_splits slices (fp32 partials added
+ * by a reduction launch; 1 = no split) only when their grid would leave half the CUs
+ * idle ([MND §Quantization]: split-K for small batches).
+ *   shared_merged  1: the shared expert is one more group of the routed expert launches
+ *   rows_gathered  1: the first expert GEMM reads x through the sort (no expanded copy)
+ *   block_m        rows per unit of the routed expert GEMMs
+ * Returns MOE_EINVAL / MOE_EUNSUPPORTED for the shapes moe_layer rejects.           */
+typedef struct {
+  int32_t shared_merged, rows_gathered, ffn1_splits, ffn2_splits, block_m;
+} moe_layer_plan;
+moe_status moe_layer_plan_of(const moe_shape* s, moe_layer_plan* out);
+
 /* Gate and top-k router.  [MND §Expert Parallelism]: each token is sent to k
  * different routed experts whose outputs are weighted-summed; [MND §MoE Router]:
  * a sort that tracks indices yields the top-k expert ids and scores per token.

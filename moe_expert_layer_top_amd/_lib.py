@@ -24,6 +24,7 @@ EXPORTS = [
     "moe_workspace_bytes", "moe_grouped_ffn_workspace_bytes", "moe_gate_topk", "moe_gate_topk_ex",
     "moe_init_routing", "moe_grouped_ffn", "moe_finalize_routing", "moe_layer", "moe_layer_ex",
     "moe_layer_overlap", "moe_layer_profiled", "moe_get_error", "moe_status_str",
+    "moe_layer_plan_of",
 ]
 SCORING = {"sigmoid": 0, "softmax": 1}
 EV_NAMES = ["start", "gate", "topk", "route", "expand", "plan", "ffn1", "ffn2", "shared", "finalize"]
@@ -47,6 +48,19 @@ class moe_weights(ctypes.Structure):
                 ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
                 ("bias", ctypes.c_void_p), ("sh_w13_scale", ctypes.c_void_p),
                 ("sh_w2_scale", ctypes.c_void_p)]
+
+
+class moe_layer_plan(ctypes.Structure):
+    _fields_ = [("shared_merged", ctypes.c_int32), ("rows_gathered", ctypes.c_int32),
+                ("ffn1_splits", ctypes.c_int32), ("ffn2_splits", ctypes.c_int32),
+                ("block_m", ctypes.c_int32)]
+
+
+def moe_layer_plan_of(s) -> dict:
+    """The layer's launch plan for shape s (host-side; see include/moe.h)."""
+    p = moe_layer_plan()
+    _check(lib().moe_layer_plan_of(ctypes.byref(s), ctypes.byref(p)), "moe_layer_plan_of")
+    return {f: int(getattr(p, f)) for f, _ in moe_layer_plan._fields_}
 
 
 class moe_router(ctypes.Structure):
@@ -86,6 +100,7 @@ def lib() -> ctypes.CDLL:
                                          ctypes.POINTER(ctypes.c_void_p), I32]),
             "moe_get_error": (I32, [P, P]),
             "moe_status_str": (ctypes.c_char_p, [I32]),
+            "moe_layer_plan_of": (I32, [S, ctypes.POINTER(moe_layer_plan)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)

@@ -25,6 +25,10 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;
 constexpr int kGateMaxSplits = 16;
 constexpr int kSmallTileRows = 512;  // at most this many rows in all: the short tile
+constexpr int kMaxFfnSplits = 8;     // split-K slices of a decode-sized expert GEMM
+constexpr long long kSplitBelowWgs = 128;  // split-K only grids smaller than this
+constexpr long long kCus = 256;             // MI355X compute units
+constexpr int kMinSliceStages = 8;        // K stages per split-K slice, at least
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -122,6 +126,59 @@ int max_units(moe::GemmCfg cfg, bool fp8, int G, int R_max, int extra_rows = 0) 
   return R_max / bm + std::min(G, R_max) + (extra_rows > 0 ? extra_rows / bm + 1 : 0);
 }
 
+// Split-K of a decode-sized grouped FFN ([MND §Quantization]: for some shapes and small
+// batches split-K lowers the latency).  When the short-tile grid would leave half the
+// CUs idle (units x N tiles < 128: a token or two of a model with few, narrow experts;
+// DeepSeek-shaped decode keeps at least 128 workgroups per GEMM, which already stream
+// the weights at HBM speed), each GEMM splits its reduction into up to
+// kMaxFfnSplits slices of at least kMinSliceStages stages (so the ring's prologue and the
+// partial traffic stay small against the weights a slice streams) and stores fp32
+// partials, which a reduction
+// kernel adds in slice order before the SwiGLU (first GEMM) or the bf16 rounding (second).
+// Everything here is known on the host, so workspace sizes follow from the shape.
+struct FfnSplit {
+  int s1, kc1, s2, kc2;  // slices and K elements per slice of the two GEMMs
+  bool on() const { return s1 > 1 || s2 > 1; }
+};
+
+int split_of(long long wgs, long long capacity, int K, int kstep, int* kc) {
+  const int steps = K / kstep;
+  int sp = 1;
+  // as many slices as one round of resident workgroups holds: more would queue a second round
+  if (wgs < kSplitBelowWgs)
+    sp = static_cast<int>(std::min<long long>(kMaxFfnSplits, capacity / std::max(1LL, wgs)));
+  sp = std::max(1, std::min(sp, steps / kMinSliceStages));
+  const int per = (steps + sp - 1) / sp;
+  sp = (steps + per - 1) / per;
+  *kc = per * kstep;
+  return sp;
+}
+
+FfnSplit ffn_split(const moe_shape* s, int G, int R_max, int I, int extra_rows = 0) {
+  FfnSplit f{1, s->H, 1, I};
+  if (s->act == MOE_F32 || G < 1 || R_max <= 0) return f;
+  const moe::GemmCfg cfg = ffn_cfg(G, R_max);
+  if (cfg != moe::CFG_SMALL) return f;
+  const bool fp8 = s->wt == MOE_FP8_E4M3, i8 = q8_weights(s), w4 = s->wt == MOE_INT4;
+  const int bm = moe::gemm_block_m(cfg, fp8), bn = moe::gemm_block_n(cfg);
+  // units: every non-empty group makes one at least (one group: its row slices), plus the
+  // extra group's row slices
+  const long long units = (G == 1 ? (R_max + bm - 1) / bm : std::min(G, R_max)) +
+                          (extra_rows + bm - 1) / bm;
+  const long long cap = static_cast<long long>(kCus) * moe::gemm_wgs_per_cu(cfg, fp8);
+  const int s1 = split_of(units * (2LL * I / bn), cap, s->H, moe::gemm_k_step(cfg, fp8, i8, w4, s->H),
+                          &f.kc1);
+  const int s2 = split_of(units * ((s->H + bn - 1) / bn), cap, I,
+                          moe::gemm_k_step(cfg, fp8, i8, w4, I), &f.kc2);
+  // each GEMM splits on its own (one unit table serves both; a GEMM that does not split
+  // keeps its fused epilogue)
+  f.s1 = s1;
+  f.s2 = s2;
+  if (s1 == 1) f.kc1 = s->H;
+  if (s2 == 1) f.kc2 = I;
+  return f;
+}
+
 // The shared expert's dtypes: W8A8 beside W8A8 or W4A8 routed experts ([V32 §quantization
 // strategy] quantizes it W8A8 in both), else its weights are in the activation dtype.
 moe_shape shared_shape(const moe_shape* s) {
@@ -144,7 +201,7 @@ bool gather_rows(const moe_shape* s) {
 }
 
 struct FfnLayout {
-  size_t units, n_units, h, h_scale, hq, h2, h2_scale, h2q, total;
+  size_t units, n_units, h, h_scale, hq, h2, h2_scale, h2q, part, part2, total;
 };
 
 // extra_rows > 0: room for the extra group's units and its intermediate h2 [extra_rows, I]
@@ -180,6 +237,15 @@ FfnLayout ffn_layout(const moe_shape* s, int G, int R_max, int I, int extra_rows
   if (extra_rows > 0 && i8) o += align_up(static_cast<size_t>(extra_rows) * 4);
   L.h2q = o;
   if (extra_rows > 0 && i8) o += align_up(static_cast<size_t>(extra_rows) * I);
+  // split-K partials of either GEMM (the first is reduced before the second runs), and
+  // of the extra group's rows
+  const FfnSplit sp = ffn_split(s, G, R_max, I, extra_rows);
+  const size_t per_row = 4 * std::max(static_cast<size_t>(sp.s1 > 1 ? sp.s1 : 0) * 2 * I,
+                                      static_cast<size_t>(sp.s2 > 1 ? sp.s2 : 0) * s->H);
+  L.part = o;
+  o += align_up(static_cast<size_t>(R_max) * per_row);
+  L.part2 = o;
+  if (extra_rows > 0) o += align_up(static_cast<size_t>(extra_rows) * per_row);
   L.total = o;
   return L;
 }
@@ -321,6 +387,11 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
   const int eb = (fp8 || i8) ? 1 : 2;
   const moe::GemmCfg cfg = ffn_cfg(G, R_max);
   const int bm = moe::gemm_block_m(cfg, fp8);
+  const int bn = moe::gemm_block_n(cfg);
+  const FfnSplit sp = ffn_split(s, G, R_max, I, alt_rows);
+  float* part = at<float>(ws, L.part);
+  float* part2 = at<float>(ws, L.part2);   // the extra group's partials
+  const int32_t* n_rows = io.offsets ? io.offsets + G : nullptr;   // rows holding data
   Unit* units = at<Unit>(ws, L.units);
   int32_t* n_units = at<int32_t>(ws, L.n_units);
   // grouped rows, and the int8 kernels (which have no uniform-row form), run from a unit
@@ -388,16 +459,44 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
       g1.b_scale2 = alt->w13_scale;
     }
   }
-  hipError_t e = i8 ? moe::launch_gemm_i8(cfg, moe::EPI_SWIGLU_BF16, w4, g1, mu, st)
-                    : moe::launch_gemm(cfg, fp8 ? moe::EPI_SWIGLU_FP8 : moe::EPI_SWIGLU_BF16, fp8,
-                                       g1, mu, st);
+  hipError_t e;
+  if (sp.s1 > 1) {
+    // split-K: the stacked gate | up projection as a plain GEMM into fp32 partials, then
+    // SwiGLU (and the fp8 quantization of h) over their slice-ordered sum
+    GemmArgs p1 = g1;
+    p1.N = 2 * I;
+    p1.up_off = 0;
+    p1.n_tiles = (2 * I + bn - 1) / bn;
+    p1.splits = sp.s1;
+    p1.k_chunk = sp.kc1;
+    p1.C = part;
+    p1.ldc = 2 * I;
+    p1.c_split = static_cast<long long>(R_max) * 2 * I;
+    p1.c_scale = nullptr;
+    if (alt_rows > 0) {
+      p1.C2 = part2;
+      p1.ldc2 = 2 * I;
+      p1.c_split2 = static_cast<long long>(alt_rows) * 2 * I;
+    }
+    e = i8 ? moe::launch_gemm_i8(cfg, moe::EPI_STORE_F32, w4, p1, mu, st)
+           : moe::launch_gemm(cfg, moe::EPI_STORE_F32, fp8, p1, mu, st);
+    if (e == hipSuccess)
+      e = moe::launch_swiglu_reduce(part, sp.s1, p1.c_split, R_max, I, n_rows, at<uint8_t>(ws, L.h),
+                                    fp8, fp8 ? at<float>(ws, L.h_scale) : nullptr, st);
+    if (e == hipSuccess && alt_rows > 0)
+      e = moe::launch_swiglu_reduce(part2, sp.s1, p1.c_split2, alt_rows, I, nullptr,
+                                    at<uint8_t>(ws, L.h2), false, nullptr, st);
+  } else {
+    e = i8 ? moe::launch_gemm_i8(cfg, moe::EPI_SWIGLU_BF16, w4, g1, mu, st)
+           : moe::launch_gemm(cfg, fp8 ? moe::EPI_SWIGLU_FP8 : moe::EPI_SWIGLU_BF16, fp8, g1, mu,
+                              st);
+  }
   // the ffn1 mark closes the first GEMM alone; h's int8 quantization (W8A8) is timed
   // with the down projection that consumes it
   if (e != hipSuccess || prof.mark(ev_ffn1, st) != hipSuccess) return MOE_EHIP;
   if (i8) {
-    e = moe::launch_quant_rows_i8(at<uint8_t>(ws, L.h), R_max, I, 1, nullptr,
-                                  io.offsets ? io.offsets + G : nullptr, at<int8_t>(ws, L.hq),
-                                  at<float>(ws, L.h_scale), st);
+    e = moe::launch_quant_rows_i8(at<uint8_t>(ws, L.h), R_max, I, 1, nullptr, n_rows,
+                                  at<int8_t>(ws, L.hq), at<float>(ws, L.h_scale), st);
     if (e == hipSuccess && alt_rows > 0)
       e = moe::launch_quant_rows_i8(at<uint8_t>(ws, L.h2), alt_rows, I, 1, nullptr, nullptr,
                                     at<int8_t>(ws, L.h2q), at<float>(ws, L.h2_scale), st);
@@ -448,8 +547,27 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
       g2.b_scale2 = alt->w2_scale;
     }
   }
-  e = i8 ? moe::launch_gemm_i8(cfg, moe::EPI_STORE_BF16, w4, g2, mu, st)
-         : moe::launch_gemm(cfg, moe::EPI_STORE_BF16, fp8, g2, mu, st);
+  if (sp.s2 > 1) {
+    GemmArgs p2 = g2;
+    p2.splits = sp.s2;
+    p2.k_chunk = sp.kc2;
+    p2.C = part;
+    p2.ldc = H;
+    p2.c_split = static_cast<long long>(R_max) * H;
+    if (alt_rows > 0) {
+      p2.C2 = part2;
+      p2.ldc2 = H;
+      p2.c_split2 = static_cast<long long>(alt_rows) * H;
+    }
+    e = i8 ? moe::launch_gemm_i8(cfg, moe::EPI_STORE_F32, w4, p2, mu, st)
+           : moe::launch_gemm(cfg, moe::EPI_STORE_F32, fp8, p2, mu, st);
+    if (e == hipSuccess) e = moe::launch_sum_reduce(part, sp.s2, p2.c_split, R_max, H, n_rows, io.y, st);
+    if (e == hipSuccess && alt_rows > 0)
+      e = moe::launch_sum_reduce(part2, sp.s2, p2.c_split2, alt_rows, H, nullptr, alt->y, st);
+  } else {
+    e = i8 ? moe::launch_gemm_i8(cfg, moe::EPI_STORE_BF16, w4, g2, mu, st)
+           : moe::launch_gemm(cfg, moe::EPI_STORE_BF16, fp8, g2, mu, st);
+  }
   if (e != hipSuccess || prof.mark(ev_ffn2, st) != hipSuccess) return MOE_EHIP;
   return MOE_OK;
 }
@@ -463,6 +581,22 @@ size_t moe_workspace_bytes(const moe_shape* s) {
   const moe_shape sh = shared_shape(s);
   if (check_inter(&sh, s->I_shared) != MOE_OK) return 0;
   return layer_layout(s).total;
+}
+
+moe_status moe_layer_plan_of(const moe_shape* s, moe_layer_plan* out) {
+  if (!out) return MOE_EINVAL;
+  moe_status st = check_shape(s);
+  if (st != MOE_OK || (st = check_inter(s, s->I)) != MOE_OK) return st;
+  const moe_shape sh = shared_shape(s);
+  if ((st = check_inter(&sh, s->I_shared)) != MOE_OK) return st;
+  const int R = s->T * s->k;
+  const FfnSplit sp = ffn_split(s, s->E, R, s->I, merge_shared(s) ? s->T : 0);
+  out->shared_merged = merge_shared(s) ? 1 : 0;
+  out->rows_gathered = gather_rows(s) ? 1 : 0;
+  out->ffn1_splits = sp.s1;
+  out->ffn2_splits = sp.s2;
+  out->block_m = s->act == MOE_F32 ? 0 : moe::gemm_block_m(ffn_cfg(s->E, R), s->wt == MOE_FP8_E4M3);
+  return MOE_OK;
 }
 
 size_t moe_grouped_ffn_workspace_bytes(const moe_shape* s, int32_t G, int32_t R_max) {

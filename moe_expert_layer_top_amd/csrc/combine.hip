@@ -4,6 +4,7 @@
 // [R1P §MoE deployment strategy optimization]: finalize-routing restores the
 // original token order through expanded_row_idx and, in the same op, forms the
 // weighted sum of the routed-expert rows plus the shared-expert output.
+// [MND] = page "Lower latency and higher throughput with multi-node DeepSeek deployment".
 
 #include "common.h"
 #include "kernels.h"
@@ -119,6 +120,97 @@ hipError_t launch_finalize(const void* y, const void* skip, const float* w, cons
   if (static_cast<long long>(T) * H * act_bytes / 16 >= (1LL << 31) * 256LL) return hipErrorInvalidValue;
   return act_bytes == 2 ? finalize_go<true>(y, skip, w, eri, out, T, H, k, st)
                         : finalize_go<false>(y, skip, w, eri, out, T, H, k, st);
+}
+
+// ------------------------------------------------------------------ split-K reductions
+// A grouped GEMM whose grid would leave most CUs idle (decode batches of a few tokens)
+// splits its reduction into S slices and stores fp32 partials [S][rows][N]; these
+// kernels add the S partials of an element in slice order (fp32) and finish the step
+// the GEMM's own epilogue would have done.  One block per row; rows at or past *n_rows
+// (device count, or all rows when NULL) hold no data and are skipped.
+
+// SwiGLU of the first expert GEMM: partial columns 0..I-1 are the gate projection,
+// I..2I-1 the up projection; h = silu(g) * u, stored bf16, or (FP8) quantized per
+// 1x128 block with scale = amax / 448 and codes e4m3(h * 448 / amax) ([MND §Quantization],
+// the same arithmetic as the fused epilogue).  Thread t owns 4 consecutive h columns of
+// each 1024-column pass; a 128-column block is 32 consecutive threads (half a wave).
+template <bool FP8>
+__global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float* __restrict__ part, int S,
+                                                            long long split_stride, int I,
+                                                            const int32_t* __restrict__ n_rows,
+                                                            uint8_t* __restrict__ h,
+                                                            float* __restrict__ h_scale) {
+  const int r = blockIdx.x;
+  if (n_rows && r >= *n_rows) return;
+  const float* row = part + static_cast<long long>(r) * 2 * I;
+  for (int c = threadIdx.x * 4; c < I; c += 256 * 4) {
+    f32x4 g = *reinterpret_cast<const f32x4*>(row + c);
+    f32x4 u = *reinterpret_cast<const f32x4*>(row + I + c);
+    for (int sp = 1; sp < S; ++sp) {
+      const float* q = row + sp * split_stride;
+      g += *reinterpret_cast<const f32x4*>(q + c);
+      u += *reinterpret_cast<const f32x4*>(q + I + c);
+    }
+    float hv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hv[i] = g[i] / (1.0f + __expf(-g[i])) * u[i];
+    if constexpr (FP8) {
+      float m = fmaxf(fmaxf(fabsf(hv[0]), fabsf(hv[1])), fmaxf(fabsf(hv[2]), fabsf(hv[3])));
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
+      const bool zero = m == 0.f;
+      const float scale = zero ? 1.0f : m / 448.0f;
+      const float inv = zero ? 0.0f : 448.0f / m;
+      uint32_t q = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q |= f32_to_e4m3(hv[i] * inv) << (8 * i);
+      *reinterpret_cast<uint32_t*>(h + static_cast<long long>(r) * I + c) = zero ? 0u : q;
+      if ((threadIdx.x & 31) == 0) h_scale[static_cast<long long>(r) * (I / kQBlock) + c / kQBlock] = scale;
+    } else {
+      *reinterpret_cast<uint2*>(h + (static_cast<long long>(r) * I + c) * 2) =
+          make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+    }
+  }
+}
+
+// Plain sum of the partials, rounded once to bf16 (the second expert GEMM).
+__global__ __launch_bounds__(256) void sum_reduce_kernel(const float* __restrict__ part, int S,
+                                                         long long split_stride, int N,
+                                                         const int32_t* __restrict__ n_rows,
+                                                         uint16_t* __restrict__ y) {
+  const int r = blockIdx.x;
+  if (n_rows && r >= *n_rows) return;
+  const float* row = part + static_cast<long long>(r) * N;
+  for (int c = threadIdx.x * 4; c < N; c += 256 * 4) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(row + c);
+    for (int sp = 1; sp < S; ++sp) v += *reinterpret_cast<const f32x4*>(row + sp * split_stride + c);
+    *reinterpret_cast<uint2*>(y + static_cast<long long>(r) * N + c) =
+        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  }
+}
+
+hipError_t launch_swiglu_reduce(const float* part, int S, long long split_stride, int rows, int I,
+                                const int32_t* n_rows, void* h, bool fp8, float* h_scale,
+                                hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  if (S < 1 || I % kQBlock || (fp8 && !h_scale)) return hipErrorInvalidValue;
+  if (fp8) {
+    swiglu_reduce_kernel<true><<<rows, 256, 0, st>>>(part, S, split_stride, I, n_rows,
+                                                      static_cast<uint8_t*>(h), h_scale);
+  } else {
+    swiglu_reduce_kernel<false><<<rows, 256, 0, st>>>(part, S, split_stride, I, n_rows,
+                                                       static_cast<uint8_t*>(h), nullptr);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_reduce(const float* part, int S, long long split_stride, int rows, int N,
+                             const int32_t* n_rows, void* y, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  if (S < 1 || N % 4) return hipErrorInvalidValue;
+  sum_reduce_kernel<<<rows, 256, 0, st>>>(part, S, split_stride, N, n_rows,
+                                          static_cast<uint16_t*>(y));
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ fp32 path

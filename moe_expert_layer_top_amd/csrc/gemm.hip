@@ -514,7 +514,8 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   static_assert(FP8 == (EPI == EPI_SWIGLU_FP8) || EPI == EPI_STORE_BF16, "epilogue matches operands");
   // I8 (W8A8): int8 codes, exact int32 accumulation, one dequantization in the epilogue
   // with the activation row's scale and the weight column's scale
-  static_assert(!Q8 || (!FP8 && !UNIFORM && (EPI == EPI_SWIGLU_BF16 || EPI == EPI_STORE_BF16)),
+  static_assert(!Q8 || (!FP8 && !UNIFORM && (EPI == EPI_SWIGLU_BF16 || EPI == EPI_STORE_BF16 ||
+                                             EPI == EPI_STORE_F32)),
                 "int8 operands: grouped launches with a bf16 result");
   static_assert(!W4 || ROWB == 128 || ROWB == 256, "int4 weights: 64- or 128-byte weight rows per stage");
   static_assert(BM % RPC == 0 && BN % RPC_B == 0, "tiles are whole DMA chunks");
@@ -902,22 +903,23 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
         const long long o = static_cast<long long>(row0_e + row) * ldc_e + col;
         // bf16 rows are 8-byte aligned (ldc is a multiple of 128); fp32 partials only
         // take the 16-byte store when the address allows it
+        const long long cs = split * (alt ? p.c_split2 : p.c_split);   // split-K slice offset
         const bool vec = col + 3 < p.N &&
                          (EPI == EPI_STORE_BF16 ||
-                          (reinterpret_cast<uintptr_t>(static_cast<float*>(cptr_e) + o + split * p.c_split) & 15) == 0);
+                          (reinterpret_cast<uintptr_t>(static_cast<float*>(cptr_e) + o + cs) & 15) == 0);
         if (vec) {
           if constexpr (EPI == EPI_STORE_BF16) {
             *reinterpret_cast<uint2*>(static_cast<uint16_t*>(cptr_e) + o) =
                 make_uint2(pack_bf16x2(acc[j][i][0], acc[j][i][1]), pack_bf16x2(acc[j][i][2], acc[j][i][3]));
           } else {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(cptr_e) + o + split * p.c_split) = acc[j][i];
+            *reinterpret_cast<f32x4*>(static_cast<float*>(cptr_e) + o + cs) = acc[j][i];
           }
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             if (col + r >= p.N) continue;
             if constexpr (EPI == EPI_STORE_BF16) static_cast<uint16_t*>(cptr_e)[o + r] = f32_to_bf16(acc[j][i][r]);
-            else static_cast<float*>(cptr_e)[o + r + split * p.c_split] = acc[j][i][r];
+            else static_cast<float*>(cptr_e)[o + r + cs] = acc[j][i][r];
           }
         }
       }
@@ -1173,6 +1175,7 @@ hipError_t go_epi(Epilogue epi, bool fp8, const GemmArgs& a, int max_units, hipS
     switch (epi) {
       case EPI_SWIGLU_FP8: return go<WM, WN, TM, TN, EPI_SWIGLU_FP8, true>(a, max_units, st);
       case EPI_STORE_BF16: return go<WM, WN, TM, TN, EPI_STORE_BF16, true>(a, max_units, st);
+      case EPI_STORE_F32: return go<WM, WN, TM, TN, EPI_STORE_F32, true>(a, max_units, st);
       default: return hipErrorInvalidValue;
     }
   }
@@ -1194,6 +1197,18 @@ int gemm_block_m(GemmCfg cfg, bool fp8) {
 
 int gemm_block_n(GemmCfg) { return 256; }
 
+int gemm_wgs_per_cu(GemmCfg cfg, bool fp8) {
+  // LDS per workgroup against the 160 KB of a CU: the bf16 / int8 / int4 short tiles hold
+  // 120-144 KB of ring (one per CU), the fp8 short tile 72 KB (two)
+  return (cfg == CFG_SMALL && fp8) ? 2 : 1;
+}
+
+int gemm_k_step(GemmCfg cfg, bool fp8, bool i8, bool w4, int K) {
+  if (fp8) return 128;                                        // one scale block per stage
+  if (w4 && cfg == CFG_SMALL && K % 256 == 0) return 256;     // whole lines of packed weights
+  return (i8 || w4) ? 128 : 64;                               // 128-byte rows per stage
+}
+
 hipError_t launch_gemm(GemmCfg cfg, Epilogue epi, bool fp8, const GemmArgs& a, int max_units,
                        hipStream_t st) {
   switch (cfg) {
@@ -1214,6 +1229,7 @@ hipError_t launch_gemm(GemmCfg cfg, Epilogue epi, bool fp8, const GemmArgs& a, i
       if (fp8) return go_epi<1, 4, 2, 4>(epi, fp8, a, max_units, st);
       if (epi == EPI_SWIGLU_BF16) return go_dma<1, 4, 2, 4, EPI_SWIGLU_BF16, 128, 4>(a, max_units, st);
       if (epi == EPI_STORE_BF16) return go_dma<1, 4, 2, 4, EPI_STORE_BF16, 128, 4>(a, max_units, st);
+      if (epi == EPI_STORE_F32) return go_dma<1, 4, 2, 4, EPI_STORE_F32, 128, 4>(a, max_units, st);
       return hipErrorInvalidValue;
     case CFG_GATE:
       if (epi != EPI_STORE_F32 || fp8) return hipErrorInvalidValue;
@@ -1225,9 +1241,16 @@ hipError_t launch_gemm(GemmCfg cfg, Epilogue epi, bool fp8, const GemmArgs& a, i
 hipError_t launch_gemm_i8(GemmCfg cfg, Epilogue epi, bool w4, const GemmArgs& a, int max_units,
                           hipStream_t st) {
   if (a.uniform_rows > 0 || !a.a_scale || !a.b_scale) return hipErrorInvalidValue;
-  if (a.splits != 1 || a.k_chunk != a.K || a.K % 128) return hipErrorInvalidValue;
-  if (epi != EPI_SWIGLU_BF16 && epi != EPI_STORE_BF16) return hipErrorInvalidValue;
+  if (a.splits < 1 || a.K % 128 || a.k_chunk % 128) return hipErrorInvalidValue;
+  if (epi != EPI_SWIGLU_BF16 && epi != EPI_STORE_BF16 && epi != EPI_STORE_F32) return hipErrorInvalidValue;
+  if (epi == EPI_STORE_F32 && cfg != CFG_SMALL) return hipErrorInvalidValue;
   const bool sw = epi == EPI_SWIGLU_BF16;
+  if (epi == EPI_STORE_F32) {   // split-K partials of a decode-sized grouped GEMM
+    if (w4 && a.K % 256 == 0 && a.k_chunk % 256 == 0)
+      return go_dma<1, 4, 2, 4, EPI_STORE_F32, 256, 3, false, false, true>(a, max_units, st);
+    if (w4) return go_dma<1, 4, 2, 4, EPI_STORE_F32, 128, 4, false, false, true>(a, max_units, st);
+    return go_dma<1, 4, 2, 4, EPI_STORE_F32, 128, 4, false, true>(a, max_units, st);
+  }
   switch (cfg) {
     case CFG_BIG:
       if (w4) {
@@ -1237,7 +1260,7 @@ hipError_t launch_gemm_i8(GemmCfg cfg, Epilogue epi, bool w4, const GemmArgs& a,
       return sw ? go_dma<4, 2, 5, 8, EPI_SWIGLU_BF16, 128, 2, false, true>(a, max_units, st)
                 : go_dma<4, 2, 5, 8, EPI_STORE_BF16, 128, 2, false, true>(a, max_units, st);
     case CFG_SMALL:
-      if (w4 && a.k_chunk % 256 == 0) {
+      if (w4 && a.K % 256 == 0 && a.k_chunk % 256 == 0) {
         // 256-element stages: whole 128-byte lines of packed weights, 3-deep ring (40 KB stages)
         return sw ? go_dma<1, 4, 2, 4, EPI_SWIGLU_BF16, 256, 3, false, false, true>(a, max_units, st)
                   : go_dma<1, 4, 2, 4, EPI_STORE_BF16, 256, 3, false, false, true>(a, max_units, st);

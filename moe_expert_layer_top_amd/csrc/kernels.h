@@ -65,6 +65,7 @@ struct GemmArgs {
   long long ldc2 = 0;
   const float* a_scale2 = nullptr;
   const float* b_scale2 = nullptr;
+  long long c_split2 = 0;   // EPI_STORE_F32: elements between the alternate group's partials
 };
 
 enum GemmCfg : int {
@@ -123,6 +124,22 @@ hipError_t launch_quant_rows_i8(const void* src, int rows, int cols, int k, cons
 
 hipError_t launch_finalize(const void* y, const void* skip, const float* w, const int32_t* eri,
                            void* out, int T, int H, int k, int act_bytes, hipStream_t st);
+
+// Split-K reductions over fp32 partials [S][rows][N] (slice stride split_stride floats),
+// one block per row, rows >= *n_rows skipped (n_rows NULL: all rows).
+// swiglu: N = 2I (gate | up) -> h [rows, I] bf16, or fp8 codes + h_scale [rows, I/128].
+hipError_t launch_swiglu_reduce(const float* part, int S, long long split_stride, int rows, int I,
+                                const int32_t* n_rows, void* h, bool fp8, float* h_scale,
+                                hipStream_t st);
+// sum: -> y [rows, N] bf16.
+hipError_t launch_sum_reduce(const float* part, int S, long long split_stride, int rows, int N,
+                             const int32_t* n_rows, void* y, hipStream_t st);
+
+// Elements of K per stage of the grouped GEMM launched for (cfg, dtype, K): split-K
+// slices must be whole multiples of it.
+int gemm_k_step(GemmCfg cfg, bool fp8, bool i8, bool w4, int K);
+// Workgroups of the grouped GEMM launched for (cfg, fp8) that one CU holds at once.
+int gemm_wgs_per_cu(GemmCfg cfg, bool fp8);
 
 // fp32 path (plain FMA kernels; fp32 matrix and vector peaks are equal on gfx950)
 hipError_t launch_gemm_nt_f32(const float* A, const float* B, float* C, int M, int N, int K,

@@ -102,12 +102,17 @@ CONFIGS = {
     "c6_prefill_w8a8": MoEConfig(
         name="c6_prefill_w8a8", cid=6, T=8192, H=7168, E=256, k=8, I=2048, I_shared=2048,
         act="bf16", wt="int8",
-        description="the c2 prefill layer with W8A8 experts (static per-channel int8 weights, "
-                    "dynamic per-token int8 activations); bf16 shared expert"),
+        description="the c2 prefill layer with W8A8 experts and shared expert (static "
+                    "per-channel int8 weights, dynamic per-token int8 activations)"),
     "c7_decode_w8a8": MoEConfig(
         name="c7_decode_w8a8", cid=7, T=128, H=7168, E=256, k=8, I=2048, I_shared=2048,
         act="bf16", wt="int8", zipf_s=1.1, bias_alpha=0.5,
         description="the c4 decode batch with W8A8 experts"),
+    "c9_decode1_bf16": MoEConfig(
+        name="c9_decode1_bf16", cid=9, T=1, H=7168, E=256, k=8, I=2048, I_shared=2048,
+        act="bf16", wt="bf16", zipf_s=1.1, bias_alpha=0.5,
+        description="one-token decode step of the c4 layer: 8 routed experts of one row each, "
+                    "the expert GEMMs split along K"),
     "c8_decode_w4a8": MoEConfig(
         name="c8_decode_w4a8", cid=8, T=128, H=7168, E=256, k=8, I=2048, I_shared=2048,
         act="bf16", wt="int4", zipf_s=1.1, bias_alpha=0.5,
@@ -159,6 +164,20 @@ CONFIGS = {
         act="bf16", wt="int4", zipf_s=1.1, bias_alpha=0.5,
         description="reduced W4A8 decode with H and I multiples of 128 but not of 256 "
                     "(the 128-element weight stages)"),
+    # ---- split-K decode: a few tokens over long K, so the expert GEMMs store fp32
+    # partials of K slices (T=3, k=2: at most 6 units; slices of at least 16 stages) ----
+    "p10_split_bf16": MoEConfig(
+        name="p10_split_bf16", cid=40, T=3, H=2048, E=8, k=2, I=2048, I_shared=2048,
+        act="bf16", wt="bf16", description="three-token decode, both expert GEMMs split along K, bf16"),
+    "p11_split_fp8": MoEConfig(
+        name="p11_split_fp8", cid=41, T=3, H=4096, E=8, k=2, I=1024, I_shared=1024,
+        act="bf16", wt="fp8", description="three-token decode, split-K first expert GEMM, fp8"),
+    "p12_split_w8a8": MoEConfig(
+        name="p12_split_w8a8", cid=42, T=3, H=4096, E=8, k=2, I=1024, I_shared=1024,
+        act="bf16", wt="int8", description="three-token decode, split-K first expert GEMM, W8A8"),
+    "p13_split_w4a8": MoEConfig(
+        name="p13_split_w4a8", cid=43, T=3, H=8192, E=8, k=2, I=1024, I_shared=1024,
+        act="bf16", wt="int4", description="three-token decode, split-K first expert GEMM, W4A8"),
     "p1_small_fp32": MoEConfig(
         name="p1_small_fp32", cid=11, T=150, H=384, E=12, k=3, I=256, I_shared=128,
         act="f32", wt="f32", x_std=0.02, wg_std=0.02, w_std=0.02,
@@ -167,11 +186,12 @@ CONFIGS = {
 
 FULL_CONFIGS = ["c1_tiny_fp32", "c2_prefill_bf16", "c3_ep_rank_bf16",
                 "c4_decode_bf16", "c5_skewed_fp8", "c6_prefill_w8a8", "c7_decode_w8a8",
-                "c8_decode_w4a8"]
+                "c8_decode_w4a8", "c9_decode1_bf16"]
 SMALL_CONFIGS = ["c1_tiny_fp32", "p1_small_fp32", "p2_prefill_bf16", "p2b_prefill_bf16",
                  "p2c_prefill_bf16", "p3_ep_rank_bf16", "p4_decode_bf16", "p5_skewed_fp8",
                  "p6_prefill_w8a8", "p7_decode_w8a8", "p8_prefill_w4a8", "p9_decode_w4a8",
-                 "p9b_decode_w4a8"]
+                 "p9b_decode_w4a8", "p10_split_bf16", "p11_split_fp8", "p12_split_w8a8",
+                 "p13_split_w4a8"]
 
 
 def get(name: str, **overrides) -> MoEConfig:

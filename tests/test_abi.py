@@ -123,3 +123,32 @@ def test_router_validation_enqueues_nothing(L):
     # a valid router reaches the workspace check (still nothing launched)
     assert L.moe_gate_topk_ex(ctypes.byref(s), ctypes.byref(good), DUMMY, DUMMY, None, DUMMY, DUMMY, DUMMY,
                               DUMMY, 16, None) == M.MOE_EWORKSPACE
+
+
+def test_layer_plan_query(L):
+    """moe_layer_plan_of describes the launch plan from the shape alone (host logic)."""
+    from synth import configs
+
+    def plan(name, **kw):
+        return M.moe_layer_plan_of(M.shape_of(configs.get(name, **kw)))
+
+    p = plan("c2_prefill_bf16")       # prefill: tall tiles, shared expert merged, rows gathered
+    assert p == {"shared_merged": 1, "rows_gathered": 1, "ffn1_splits": 1, "ffn2_splits": 1, "block_m": 320}
+    p = plan("c5_skewed_fp8")         # fp8 experts beside a bf16 shared expert
+    assert p["shared_merged"] == 0 and p["rows_gathered"] == 0 and p["block_m"] == 256
+    assert plan("c6_prefill_w8a8")["shared_merged"] == 1      # int8 shared expert in the int8 launches
+    assert plan("c8_decode_w4a8")["shared_merged"] == 0       # int4 experts, int8 shared expert
+    p = plan("c4_decode_bf16")        # decode: short tiles, grid large enough not to split
+    assert p["block_m"] == 32 and p["ffn1_splits"] == 1 and p["shared_merged"] == 1
+    # one token of the DeepSeek shape keeps 128 workgroups per GEMM: no split
+    assert plan("c9_decode1_bf16")["ffn1_splits"] == 1
+    # a few tokens over long K split the expert GEMMs (the merged shared expert's rows
+    # take their own partials)
+    p = plan("p10_split_bf16")
+    assert p["ffn1_splits"] > 1 and p["ffn2_splits"] > 1 and p["shared_merged"] == 1
+    for name in ("p11_split_fp8", "p12_split_w8a8", "p13_split_w4a8"):
+        assert plan(name)["ffn1_splits"] > 1, name
+    assert plan("p4_decode_bf16")["ffn1_splits"] == 1        # short K: slices would be too thin
+    bad = M.shape(8, 100, 16, 2, 128, 128, "bf16", "bf16")   # H not a multiple of 128
+    with pytest.raises(M.MoEError):
+        M.moe_layer_plan_of(bad)

@@ -33,7 +33,8 @@ def M():
 
 def sample_tokens(T, seed):
     rng = np.random.default_rng(seed)
-    picks = {0, T - 1} | set(rng.choice(T, size=min(T, N_SAMPLE) - 2, replace=False).tolist())
+    ends = {0, T - 1}
+    picks = ends | set(rng.choice(T, size=max(0, min(T, N_SAMPLE) - len(ends)), replace=False).tolist())
     return np.array(sorted(picks))
 
 
@@ -56,7 +57,8 @@ def expert_dict(cfg, experts):
 
 
 @pytest.mark.parametrize("name", ["c1_tiny_fp32", "c2_prefill_bf16", "c4_decode_bf16", "c5_skewed_fp8",
-                                  "c6_prefill_w8a8", "c7_decode_w8a8", "c8_decode_w4a8"])
+                                  "c6_prefill_w8a8", "c7_decode_w8a8", "c8_decode_w4a8",
+                                  "c9_decode1_bf16"])
 def test_full_layer_sampled(M, name):
     cfg = configs.get(name)
     say("full layer", name, "upload")

@@ -371,10 +371,14 @@ def test_invalid_ids_are_flagged_and_dropped(M):
     assert M.moe_get_error(out["ws"]) == M.MOE_OK          # read-and-clear
 
 
-@pytest.mark.parametrize("T", [0, 1, 17])
-def test_small_token_counts(M, T):
-    cfg, d, g = case("p4_decode_bf16")
-    say("small T", T)
+# p4 keeps the unsplit decode tiles; the split workloads at one or two tokens take the
+# split-K expert GEMMs (and an unmerged, split shared expert) for every dtype
+@pytest.mark.parametrize("name,T", [("p4_decode_bf16", 0), ("p4_decode_bf16", 1), ("p4_decode_bf16", 17),
+                                    ("p10_split_bf16", 1), ("p11_split_fp8", 1),
+                                    ("p12_split_w8a8", 2), ("p13_split_w4a8", 1)])
+def test_small_token_counts(M, name, T):
+    cfg, d, g = case(name)
+    say("small T", name, T)
     if T == 0:
         s = M.shape(0, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared, cfg.act, cfg.wt)
         W = M.weights(g["w_gate"], g["w13"], g["w2"], g["sh_w13"], g["sh_w2"], None, None, g["bias"])

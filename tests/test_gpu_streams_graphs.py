@@ -18,9 +18,10 @@ pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
 # fp32 and fp8 layers and I_shared != I run the shared expert in launches of its own (the
 # side stream is used); p2 has it inside the routed launches (the side stream is not).
 # p6: the int8 shared expert is a group of the routed launches (side unused); p9: the int8
-# shared expert of a W4A8 layer quantizes x itself on the side stream
+# shared expert of a W4A8 layer quantizes x itself on the side stream; p10, p11: split-K
+# expert GEMMs with the shared expert (also split) on the side stream
 OVERLAP = ["p1_small_fp32", "p2_prefill_bf16", "p2c_prefill_bf16", "p5_skewed_fp8",
-           "p6_prefill_w8a8", "p9_decode_w4a8"]
+           "p6_prefill_w8a8", "p9_decode_w4a8", "p10_split_bf16", "p11_split_fp8"]
 
 
 @pytest.fixture(scope="module")
@@ -96,7 +97,8 @@ def new_x(cfg, g, seed):
 
 @pytest.mark.parametrize("name,overlap", [("p2_prefill_bf16", False), ("p5_skewed_fp8", False),
                                           ("p5_skewed_fp8", True), ("p4_decode_bf16", False),
-                                          ("p6_prefill_w8a8", False), ("p9_decode_w4a8", True)])
+                                          ("p6_prefill_w8a8", False), ("p9_decode_w4a8", True),
+                                          ("p12_split_w8a8", True)])
 def test_layer_graph_replay(M, name, overlap):
     """Capture the layer once, then replay it on new inputs written into the captured
     input buffer, with eager calls and synchronizations between replays; every replay
