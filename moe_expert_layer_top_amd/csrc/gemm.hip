@@ -15,10 +15,10 @@
 //   * Workgroups are dealt round-robin to the 8 XCDs; the block -> unit mapping
 //     keeps all N tiles of one unit on one XCD, so the unit's activation rows are
 //     fetched from HBM once and re-read from that XCD's L2.
-//   * Operands are both K-contiguous ([out, in] weights).  Each stage moves a
-//     128-byte K slice of BM activation rows and BN weight rows into LDS through
-//     registers (double-buffered, one barrier per stage), XOR-swizzled by row so
-//     the 16-byte fragment reads of 8 consecutive lanes hit distinct banks.
+//   * Operands are both K-contiguous ([out, in] weights).  Each stage moves a K slice
+//     of BM activation rows and BN weight rows straight into LDS (direct-to-LDS loads,
+//     an NST-deep ring, one barrier per stage), XOR-swizzled by row so the 16-byte
+//     fragment reads of 8 consecutive lanes hit distinct banks.
 //   * Wavefronts own 16-row tiles round-robin, so a partially filled unit spreads
 //     its valid rows over all wavefronts; tiles past the unit's rows are skipped.
 //   * bf16: v_mfma_f32_16x16x32_bf16.  fp8 (e4m3): one v_mfma 16x16x128 per
@@ -37,340 +37,9 @@
 
 namespace moe {
 
-template <int WM, int WN, int TM, int TN, int EPI, bool FP8, bool UNIFORM>
-__device__ __forceinline__ void gemm_body(const GemmArgs& p) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int BM = WM * TM * 16;
-  constexpr int BN = WN * TN * 16;
-  constexpr int ROWB = 128;              // bytes per operand row per stage
-  constexpr int KSTEP = FP8 ? 128 : 64;  // elements per stage
-  constexpr int EB = FP8 ? 1 : 2;        // operand element bytes
-  constexpr int A_CH = BM * 8 / NT;
-  constexpr int B_CH = BN * 8 / NT;
-  constexpr bool SWIGLU = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_FP8);
-  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile loads must divide evenly");
-  static_assert((NT / 8) % 8 == 0, "swizzle assumes row stride of loads multiple of 8");
-  static_assert(!SWIGLU || TN % 2 == 0, "swiglu needs gate/up tile pairs");
-
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * ROWB];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * ROWB];
-  __shared__ float lds_sa[FP8 ? 2 : 1][FP8 ? BM : 1];
-  __shared__ float lds_rmax[EPI == EPI_SWIGLU_FP8 ? WN : 1][EPI == EPI_SWIGLU_FP8 ? BM : 1];
-
-  // ---- block -> (unit, n tile, k split); all tiles of a unit stay on one XCD
-  const int bid = blockIdx.x;
-  const int xcd = bid % kXcds;
-  const int slot = bid / kXcds;
-  const int per_unit = p.n_tiles * p.splits;
-  const int u = (slot / per_unit) * kXcds + xcd;
-  const int rem = slot % per_unit;
-  const int nt = rem % p.n_tiles;
-  const int split = rem / p.n_tiles;
-  Unit un;
-  if constexpr (UNIFORM) {
-    if (u * BM >= p.uniform_rows) return;
-    un.group = 0;
-    un.row0 = u * BM;
-    un.rows = min(BM, p.uniform_rows - u * BM);
-  } else {
-    if (u >= *p.n_units) return;
-    un = p.units[u];
-  }
-  const int rows = un.rows;
-  if (rows <= 0) return;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WN;
-  const int wn = wave % WN;
-  const int mtiles = (rows + 15) >> 4;
-  int jcount = mtiles > wm ? (mtiles - wm + WM - 1) / WM : 0;
-  if (jcount > TM) jcount = TM;
-
-  const int k0 = split * p.k_chunk;
-  const int k1 = min(p.K, k0 + p.k_chunk);
-  const int nsteps = (k1 - k0) / KSTEP;
-
-  // ---- per-thread load plan (constant over K): global offsets and LDS offsets
-  const uint8_t* a_base = p.A + static_cast<long long>(un.row0) * p.lda + static_cast<long long>(k0) * EB;
-  const uint8_t* b_base = p.B + static_cast<long long>(un.group) * p.b_group + static_cast<long long>(k0) * EB;
-  const int ch = tid & 7;
-  const int sw = (ch ^ ((tid >> 3) & 7)) << 4;
-  // Rows past the unit and columns past N re-load a valid row (an L1/L2 hit) so every
-  // load and LDS store is unconditional; their results are never stored.
-  uint32_t a_off[A_CH], b_off[B_CH];
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int r = (tid >> 3) + i * (NT / 8);
-    const int rc = r < rows ? r : rows - 1;
-    a_off[i] = static_cast<uint32_t>(rc * p.lda + ch * 16);
-  }
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int j = (tid >> 3) + i * (NT / 8);
-    int col, grow;
-    if constexpr (SWIGLU) {
-      constexpr int WCOLS = TN * 16, HALF = TN * 8;
-      const int wn2 = j / WCOLS, jj = j % WCOLS;
-      col = nt * (BN / 2) + wn2 * HALF + (jj % HALF);
-      grow = (jj < HALF ? 0 : p.up_off) + col;
-    } else {
-      col = nt * BN + j;
-      grow = col;
-    }
-    if (col >= p.N) grow -= col - (p.N - 1);
-    b_off[i] = static_cast<uint32_t>(static_cast<long long>(grow) * p.ldb + ch * 16);
-  }
-
-  u32x4 ra[A_CH], rb[B_CH];
-  float rsa = 0.f;
-  // global -> registers for stage `step`
-#define MOE_GLOAD(step)                                                                        \
-  do {                                                                                         \
-    const long long kb_ = static_cast<long long>(step) * KSTEP * EB;                           \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                           \
-        ra[i] = *reinterpret_cast<const u32x4*>(a_base + a_off[i] + kb_);                      \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                           \
-        rb[i] = *reinterpret_cast<const u32x4*>(b_base + b_off[i] + kb_);                      \
-    if constexpr (FP8) {                                                                       \
-      if (tid < BM) {                                                                          \
-        const int r_ = tid < rows ? tid : rows - 1;                                            \
-        rsa = p.a_scale[static_cast<long long>(un.row0 + r_) * p.a_scale_ld + (k0 / KSTEP) +   \
-                        (step)];                                                               \
-      }                                                                                        \
-    }                                                                                          \
-  } while (0)
-  // registers -> LDS stage `stg` (row-swizzled 16-byte chunks)
-#define MOE_LSTORE(stg)                                                                        \
-  do {                                                                                         \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) {                                         \
-      const int r_ = (tid >> 3) + i * (NT / 8);                                                \
-      *reinterpret_cast<u32x4*>(&lds_a[stg][r_ * ROWB + sw]) = ra[i];                          \
-    }                                                                                          \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                         \
-      const int j_ = (tid >> 3) + i * (NT / 8);                                                \
-      *reinterpret_cast<u32x4*>(&lds_b[stg][j_ * ROWB + sw]) = rb[i];                          \
-    }                                                                                          \
-    if constexpr (FP8) {                                                                       \
-      if (tid < BM) lds_sa[stg][tid] = rsa;                                                    \
-    }                                                                                          \
-  } while (0)
-
-  f32x4 acc[TM][TN];
-#pragma unroll
-  for (int j = 0; j < TM; ++j)
-#pragma unroll
-    for (int i = 0; i < TN; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // weight-scale row bases for fp8 (one 128x128 block row per 16-row B tile)
-  long long sb_row[FP8 ? TN : 1];
-  if constexpr (FP8) {
-#pragma unroll
-    for (int i = 0; i < TN; ++i) {
-      const int j = wn * TN * 16 + 16 * i;
-      int grow;
-      if constexpr (SWIGLU) {
-        constexpr int WCOLS = TN * 16, HALF = TN * 8;
-        const int wn2 = j / WCOLS, jj = j % WCOLS;
-        const int col = nt * (BN / 2) + wn2 * HALF + (jj % HALF);
-        grow = (jj < HALF ? 0 : p.up_off) + col;
-      } else {
-        grow = min(nt * BN + j, p.N - 1);  // tiles past N read a valid scale, never stored
-      }
-      sb_row[i] = static_cast<long long>(un.group) * p.b_scale_group +
-                  static_cast<long long>(grow / kQBlock) * p.b_scale_ld + k0 / KSTEP;
-    }
-  }
-
-  const int frag_row = lane & 15;
-  const int kgrp = lane >> 4;
-
-  if (nsteps > 0) {
-    MOE_GLOAD(0);
-    MOE_LSTORE(0);
-  }
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < nsteps) MOE_GLOAD(s + 1);
-    const uint8_t* la = lds_a[cur];
-    const uint8_t* lb = lds_b[cur];
-    if constexpr (!FP8) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int c = kk * 4 + kgrp;
-        const int coff = (c ^ (lane & 7)) << 4;
-        bf16x8 bfr[TN];
-#pragma unroll
-        for (int i = 0; i < TN; ++i) {
-          const int rb_ = wn * TN * 16 + 16 * i + frag_row;
-          bfr[i] = *reinterpret_cast<const bf16x8*>(lb + rb_ * ROWB + coff);
-        }
-#pragma unroll
-        for (int j = 0; j < TM; ++j) {
-          if (j < jcount) {
-            const int ra_ = 16 * (j * WM + wm) + frag_row;
-            const bf16x8 afr = *reinterpret_cast<const bf16x8*>(la + ra_ * ROWB + coff);
-#pragma unroll
-            for (int i = 0; i < TN; ++i)
-              acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[i], acc[j][i], 0, 0, 0);
-          }
-        }
-      }
-    } else {
-      // one 16x16x128 fp8 product per (row tile, column tile) and K block, promoted
-      // into the fp32 accumulator with scale_a(row, kb) * scale_w(col block, kb)
-      const int c0 = 2 * kgrp;
-      const int off0 = (c0 ^ (lane & 7)) << 4;
-      const int off1 = ((c0 + 1) ^ (lane & 7)) << 4;
-      i32x8 afr[TM];
-      float sa[TM][4];
-#pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        if (j < jcount) {
-          const int t = j * WM + wm;
-          const int ra_ = 16 * t + frag_row;
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(la + ra_ * ROWB + off0);
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(la + ra_ * ROWB + off1);
-          afr[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sa[j][r] = lds_sa[cur][16 * t + 4 * kgrp + r];
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < TN; ++i) {
-        const int rb_ = wn * TN * 16 + 16 * i + frag_row;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(lb + rb_ * ROWB + off0);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(lb + rb_ * ROWB + off1);
-        const i32x8 bfr = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                                (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        const float sb = p.b_scale[sb_row[i] + s];
-#pragma unroll
-        for (int j = 0; j < TM; ++j) {
-          if (j < jcount) {
-            const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                afr[j], bfr, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[j][i][r] += part[r] * (sa[j][r] * sb);
-          }
-        }
-      }
-    }
-    if (s + 1 < nsteps) MOE_LSTORE(cur ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue.  C fragment of a 16x16 tile: lane holds column (lane & 15),
-  // rows 4 * (lane >> 4) + r, r = 0..3.
-  const int ccol = lane & 15;
-  if constexpr (EPI == EPI_STORE_BF16 || EPI == EPI_STORE_F32) {
-#pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      if (j >= jcount) continue;
-      const int rbase = 16 * (j * WM + wm) + 4 * kgrp;
-#pragma unroll
-      for (int i = 0; i < TN; ++i) {
-        const int col = nt * BN + wn * TN * 16 + 16 * i + ccol;
-        if (col >= p.N) continue;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = rbase + r;
-          if (row >= rows) continue;
-          const long long o = static_cast<long long>(un.row0 + row) * p.ldc + col;
-          if constexpr (EPI == EPI_STORE_BF16) {
-            static_cast<uint16_t*>(p.C)[o] = f32_to_bf16(acc[j][i][r]);
-          } else {
-            static_cast<float*>(p.C)[o + split * p.c_split] = acc[j][i][r];
-          }
-        }
-      }
-    }
-  } else {
-    constexpr int HT = TN / 2;
-    float hv[TM][HT][4];
-#pragma unroll
-    for (int j = 0; j < TM; ++j)
-#pragma unroll
-      for (int i = 0; i < HT; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float g = acc[j][i][r];
-          const float up = acc[j][i + HT][r];
-          hv[j][i][r] = g / (1.0f + __expf(-g)) * up;
-        }
-    if constexpr (EPI == EPI_SWIGLU_BF16) {
-#pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        if (j >= jcount) continue;
-        const int rbase = 16 * (j * WM + wm) + 4 * kgrp;
-#pragma unroll
-        for (int i = 0; i < HT; ++i) {
-          const int col = nt * (BN / 2) + wn * (TN * 8) + 16 * i + ccol;
-          if (col >= p.N) continue;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = rbase + r;
-            if (row >= rows) continue;
-            static_cast<uint16_t*>(p.C)[static_cast<long long>(un.row0 + row) * p.ldc + col] =
-                f32_to_bf16(hv[j][i][r]);
-          }
-        }
-      }
-    } else {
-      // 1x128 fp8 quantization of h: the block's BN/2 = 128 h columns are one scale
-      // block.  Row amax: lane-local over HT tiles, 16-lane butterfly, then across
-      // the WN wavefronts through LDS.
-      static_assert(EPI != EPI_SWIGLU_FP8 || BN / 2 == kQBlock, "h tile must be one scale block");
-#pragma unroll
-      for (int j = 0; j < TM; ++j) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float m = 0.f;
-#pragma unroll
-          for (int i = 0; i < HT; ++i) m = fmaxf(m, fabsf(hv[j][i][r]));
-#pragma unroll
-          for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
-          if (j < jcount && ccol == 0) lds_rmax[wn][16 * (j * WM + wm) + 4 * kgrp + r] = m;
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        if (j >= jcount) continue;
-        const int rbase = 16 * (j * WM + wm) + 4 * kgrp;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = rbase + r;
-          float amax = 0.f;
-#pragma unroll
-          for (int w = 0; w < WN; ++w) amax = fmaxf(amax, lds_rmax[w][row]);
-          const bool zero = amax == 0.f;
-          const float scale = zero ? 1.0f : amax / 448.0f;
-          const float inv = zero ? 0.0f : 448.0f / amax;
-          if (row >= rows) continue;
-          uint8_t* hrow = static_cast<uint8_t*>(p.C) + static_cast<long long>(un.row0 + row) * p.ldc;
-#pragma unroll
-          for (int i = 0; i < HT; ++i) {
-            const int col = nt * (BN / 2) + wn * (TN * 8) + 16 * i + ccol;
-            const uint32_t q = zero ? 0u : f32_to_e4m3(hv[j][i][r] * inv);
-            if (col < p.N) hrow[col] = static_cast<uint8_t>(q);
-          }
-          if (wn == 0 && ccol == 0)
-            p.c_scale[static_cast<long long>(un.row0 + row) * p.c_scale_ld + nt] = scale;
-        }
-      }
-    }
-  }
-}
-
-#undef MOE_GLOAD
-#undef MOE_LSTORE
-
-// ------------------------------------------------------------------ DMA pipeline (bf16)
-// Second pipeline for bf16 operands: global -> LDS with global_load_lds_dwordx4 (each
-// lane lands 16 bytes at lds + 16 * lane, no staging registers) into an NST-deep ring
+// ------------------------------------------------------------------ DMA pipeline
+// Global -> LDS with global_load_lds_dwordx4 (each lane lands 16 bytes at
+// lds + 16 * lane, no staging registers) into an NST-deep ring
 // of stage buffers; step s waits only for its own loads (vmcnt), so NST - 1 stages of
 // weight traffic are in flight per workgroup.  Stage = ROWB bytes of K for all BM
 // activation rows and BN weight rows.  The ring buffers are distinct LDS objects and
@@ -399,25 +68,10 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// 16 bytes per lane from `g` into lds_chunk + 16 * lane (global_load_lds_dwordx4; the
-// LDS base goes through M0).  Issued as inline assembly so the compiler does not
-// track it: it would otherwise wait for every in-flight DMA before any LDS read it
-// cannot prove disjoint.  Ordering is explicit instead: each step waits on vmcnt for
-// its own stage, and vmcnt completes in order, so extra in-flight DMAs can only make
-// compiler-generated waits stricter, never looser.
-__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_chunk) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-          (__attribute__((address_space(3))) uint8_t*)lds_chunk)));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(m0)
-               : "memory", "m0");
-}
-
-// Same as dma16 with the address split into a wave-uniform 64-bit base (scalar
-// registers) and a 32-bit per-lane byte offset: the per-lane address needs one VGPR
-// instead of two and no 64-bit add.
+// 16 bytes per lane (global_load_lds_dwordx4) into lds_chunk + 16 * lane, with the
+// address split into a wave-uniform 64-bit base (scalar registers) and a 32-bit per-lane
+// byte offset: the per-lane address needs one VGPR and no 64-bit add.  M0 holds the LDS
+// destination; the DMA is counted by vmcnt like any global load.
 // NT: non-temporal (streaming) cache policy, for data read once.
 template <bool NT = false>
 __device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint8_t* lds_chunk) {
@@ -445,18 +99,6 @@ __device__ __forceinline__ void dma4s(const void* base, uint32_t off, uint8_t* l
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
                :
                : "v"(off), "s"(base), "s"(m0)
-               : "memory", "m0");
-}
-
-// 4 bytes per lane from `g` into lds_chunk + 4 * lane (global_load_lds_dword); same
-// ordering rules as dma16.
-__device__ __forceinline__ void dma4(const void* g, uint8_t* lds_chunk) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-          (__attribute__((address_space(3))) uint8_t*)lds_chunk)));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
-               :
-               : "v"(g), "s"(m0)
                : "memory", "m0");
 }
 
@@ -508,10 +150,13 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   constexpr bool SWIGLU = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_FP8);
   // fp8: one stage = one 128-wide K block of e4m3 codes; its 1x128 activation scales and
   // the two 128x128 weight-block scales of the tile come into LDS with the stage.
-  static_assert(!FP8 || (NST == 2 && ROWB == kQBlock && BM % 64 == 0 && BM / 64 < WM * WN &&
-                         EPI != EPI_STORE_F32 && !UNIFORM),
-                "fp8 tiles: 2-deep ring of one scale block per stage");
-  static_assert(FP8 == (EPI == EPI_SWIGLU_FP8) || EPI == EPI_STORE_BF16, "epilogue matches operands");
+  // fp8: waves 0 .. ASW-1 DMA the stage's activation scales (64 rows each), wave ASW the
+  // two weight-block scales
+  constexpr int ASW = (BM + 63) / 64;
+  static_assert(!FP8 || (ROWB == kQBlock && (BM % 64 == 0 || BM == 32) && ASW < WM * WN && !UNIFORM),
+                "fp8 tiles: one scale block per stage");
+  static_assert(FP8 == (EPI == EPI_SWIGLU_FP8) || EPI == EPI_STORE_BF16 || EPI == EPI_STORE_F32,
+                "epilogue matches operands");
   // I8 (W8A8): int8 codes, exact int32 accumulation, one dequantization in the epilogue
   // with the activation row's scale and the weight column's scale
   static_assert(!Q8 || (!FP8 && !UNIFORM && (EPI == EPI_SWIGLU_BF16 || EPI == EPI_STORE_BF16 ||
@@ -526,8 +171,9 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st2[NST > 2 ? STAGE : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t st3[NST > 3 ? STAGE : 16];
-  __shared__ __attribute__((aligned(16))) float sa_st[2][FP8 ? BM : 1];   // activation scales
-  __shared__ __attribute__((aligned(16))) float sb_st[2][FP8 ? 64 : 1];   // weight-block scales
+  // per ring slot: activation scales (64 per scale wave) and weight-block scales
+  __shared__ __attribute__((aligned(16))) float sa_st[FP8 ? NST : 1][FP8 ? ASW * 64 : 1];
+  __shared__ __attribute__((aligned(16))) float sb_st[FP8 ? NST : 1][FP8 ? 64 : 1];
   // fp8: the per-lane DMA offsets live in LDS and are re-read (volatile) at each issue;
   // in registers they would be spilled, and a scratch reload waits on vmcnt(0), which
   // would drain the DMAs in flight.
@@ -627,7 +273,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   uint32_t sc_off = 0;
   if constexpr (FP8) {
     const int kb0 = k0 / kQBlock;
-    if (wave < BM / 64) {
+    if (wave < ASW) {
       const int r = 64 * wave + lane;
       const int rc = r < rows ? r : rows - 1;
       sc_base = p.a_scale + static_cast<long long>(un.row0) * p.a_scale_ld + kb0;
@@ -643,6 +289,12 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
       sc_base = p.b_scale + static_cast<long long>(un.group) * p.b_scale_group + kb0;
       sc_off = static_cast<uint32_t>(static_cast<long long>(blk) * p.b_scale_ld * 4);
     }
+    // one base per wavefront (the DMA takes it in scalar registers); each 32-bit half is
+    // widened as unsigned, so the low half's top bit never sign-extends into the high half
+    const uint64_t sb = reinterpret_cast<uint64_t>(sc_base);
+    const uint32_t sb_lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(sb)));
+    const uint32_t sb_hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(sb >> 32)));
+    sc_base = reinterpret_cast<const float*>((static_cast<uint64_t>(sb_hi) << 32) | sb_lo);
   }
   if constexpr (FP8) {
 #pragma unroll
@@ -671,8 +323,8 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
       for (int i = 0; i < B_PER; ++i) dma16s<false>(bk, lane_off_of(A_PER + i), buf + BM * ROWB + (wave + i * NW) * 1024);
     }
     if constexpr (FP8) {
-      if (wave < BM / 64) dma4s(sc_base + step, lane_off_of(LMAX), reinterpret_cast<uint8_t*>(&sa_st[b & 1][64 * wave]));
-      else if (wave == BM / 64) dma4s(sc_base + step, lane_off_of(LMAX), reinterpret_cast<uint8_t*>(&sb_st[b & 1][0]));
+      if (wave < ASW) dma4s(sc_base + step, lane_off_of(LMAX), reinterpret_cast<uint8_t*>(&sa_st[b][64 * wave]));
+      else if (wave == ASW) dma4s(sc_base + step, lane_off_of(LMAX), reinterpret_cast<uint8_t*>(&sb_st[b][0]));
     }
   };
 
@@ -721,8 +373,8 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
       };
       i32x8 bw[TN];
       float sb[TN];
-      const float sb0 = sb_st[b & 1][0];
-      const float sb1 = sb_st[b & 1][1];
+      const float sb0 = sb_st[b][0];
+      const float sb1 = sb_st[b][1];
 #pragma unroll
       for (int i = 0; i < TN; ++i) {
         bw[i] = frag(b_lo, b_hi, wn * TN + i);
@@ -733,7 +385,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const i32x8 at = frag(a_lo, a_hi, j * WM + wm);
-        const float sa = sa_st[b & 1][16 * (j * WM + wm) + (lane & 15)];
+        const float sa = sa_st[b][16 * (j * WM + wm) + (lane & 15)];
 #pragma unroll
         for (int i = 0; i < TN; ++i) {
           const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -788,16 +440,20 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
     }
   };
 
-  // per-wave count of DMA instructions per stage (wave-uniform)
-  const bool more = wave < (LREM == 0 ? NW : LREM);
+  // DMA instructions this wavefront issues per stage (wave-uniform): its tile chunks
+  // (LMAX, or LMAX - 1 for waves at or past LREM) plus, for fp8, one scale load on
+  // waves 0 .. ASW
+  constexpr int HI = FP8 ? LMAX + 1 : LMAX;
+  constexpr int LO = FP8 ? LMAX : LMAX - 1;
+  const bool hi = FP8 ? wave <= ASW : wave < (LREM == 0 ? NW : LREM);
   // wait until the loads of the current step landed; `later` = steps issued after it
   auto wait_step = [&](int later) __attribute__((always_inline)) {
     if (later >= NST - 2 && NST > 2) {
-      if (more) wait_vmcnt<(NST > 2 ? (NST - 2) * LMAX : 0)>();
-      else wait_vmcnt<(NST > 2 ? (NST - 2) * (LMAX - 1) : 0)>();
+      if (hi) wait_vmcnt<(NST > 2 ? (NST - 2) * HI : 0)>();
+      else wait_vmcnt<(NST > 2 ? (NST - 2) * LO : 0)>();
     } else if (later == 1 && NST > 3) {
-      if (more) wait_vmcnt<LMAX>();
-      else wait_vmcnt<LMAX - 1>();
+      if (hi) wait_vmcnt<HI>();
+      else wait_vmcnt<LO>();
     } else {
       wait_vmcnt<0>();
     }
@@ -1024,18 +680,6 @@ __global__ __launch_bounds__(WM* WN * 64) void dense_gemm_dma_kernel(GemmArgs p)
 }
 
 // Experts: units come from the device-built table.
-template <int WM, int WN, int TM, int TN, int EPI, bool FP8>
-__global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs p) {
-  gemm_body<WM, WN, TM, TN, EPI, FP8, false>(p);
-}
-
-// One group of `uniform_rows` rows (shared expert, gate projection): units are
-// consecutive BM-row slices, known without a table.
-template <int WM, int WN, int TM, int TN, int EPI, bool FP8>
-__global__ __launch_bounds__(WM* WN * 64) void dense_gemm_kernel(GemmArgs p) {
-  gemm_body<WM, WN, TM, TN, EPI, FP8, true>(p);
-}
-
 // ------------------------------------------------------------------ unit planner
 // One block: units per group = ceil(n / BM) near-equal slices (rows rounded up to
 // 16), prefix-summed over groups, then each group writes its slices.  When
@@ -1130,23 +774,6 @@ hipError_t launch_plan(const int32_t* offsets, int G, int rows_if_null, int extr
 
 // ------------------------------------------------------------------ dispatch
 namespace {
-template <int WM, int WN, int TM, int TN, int EPI, bool FP8>
-hipError_t go(const GemmArgs& a, int max_units, hipStream_t st) {
-  const long long per_unit = static_cast<long long>(a.n_tiles) * a.splits;
-  const long long slots = (static_cast<long long>(max_units) + kXcds - 1) / kXcds;
-  const long long blocks = slots * kXcds * per_unit;
-  if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (a.uniform_rows > 0) {
-    dense_gemm_kernel<WM, WN, TM, TN, EPI, FP8>
-        <<<static_cast<unsigned>(blocks), WM * WN * 64, 0, st>>>(a);
-  } else {
-    grouped_gemm_kernel<WM, WN, TM, TN, EPI, FP8>
-        <<<static_cast<unsigned>(blocks), WM * WN * 64, 0, st>>>(a);
-  }
-  return hipGetLastError();
-}
-
 template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST, bool FP8 = false, bool I8 = false,
           bool W4 = false>
 hipError_t go_dma(const GemmArgs& a, int max_units, hipStream_t st) {
@@ -1169,22 +796,6 @@ hipError_t go_dma(const GemmArgs& a, int max_units, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int WM, int WN, int TM, int TN>
-hipError_t go_epi(Epilogue epi, bool fp8, const GemmArgs& a, int max_units, hipStream_t st) {
-  if (fp8) {
-    switch (epi) {
-      case EPI_SWIGLU_FP8: return go<WM, WN, TM, TN, EPI_SWIGLU_FP8, true>(a, max_units, st);
-      case EPI_STORE_BF16: return go<WM, WN, TM, TN, EPI_STORE_BF16, true>(a, max_units, st);
-      case EPI_STORE_F32: return go<WM, WN, TM, TN, EPI_STORE_F32, true>(a, max_units, st);
-      default: return hipErrorInvalidValue;
-    }
-  }
-  switch (epi) {
-    case EPI_SWIGLU_BF16: return go<WM, WN, TM, TN, EPI_SWIGLU_BF16, false>(a, max_units, st);
-    case EPI_STORE_BF16: return go<WM, WN, TM, TN, EPI_STORE_BF16, false>(a, max_units, st);
-    default: return hipErrorInvalidValue;
-  }
-}
 }  // namespace
 
 int gemm_block_m(GemmCfg cfg, bool fp8) {
@@ -1197,10 +808,9 @@ int gemm_block_m(GemmCfg cfg, bool fp8) {
 
 int gemm_block_n(GemmCfg) { return 256; }
 
-int gemm_wgs_per_cu(GemmCfg cfg, bool fp8) {
-  // LDS per workgroup against the 160 KB of a CU: the bf16 / int8 / int4 short tiles hold
-  // 120-144 KB of ring (one per CU), the fp8 short tile 72 KB (two)
-  return (cfg == CFG_SMALL && fp8) ? 2 : 1;
+int gemm_wgs_per_cu(GemmCfg, bool) {
+  // LDS per workgroup against the 160 KB of a CU: every short tile holds a 120-156 KB ring
+  return 1;
 }
 
 int gemm_k_step(GemmCfg cfg, bool fp8, bool i8, bool w4, int K) {
@@ -1226,7 +836,13 @@ hipError_t launch_gemm(GemmCfg cfg, Epilogue epi, bool fp8, const GemmArgs& a, i
       if (epi == EPI_STORE_BF16) return go_dma<4, 2, 5, 8, EPI_STORE_BF16, 128, 2>(a, max_units, st);
       return hipErrorInvalidValue;
     case CFG_SMALL:
-      if (fp8) return go_epi<1, 4, 2, 4>(epi, fp8, a, max_units, st);
+      if (fp8) {
+        if (a.uniform_rows > 0) return hipErrorInvalidValue;
+        if (epi == EPI_SWIGLU_FP8) return go_dma<1, 4, 2, 4, EPI_SWIGLU_FP8, 128, 4, true>(a, max_units, st);
+        if (epi == EPI_STORE_BF16) return go_dma<1, 4, 2, 4, EPI_STORE_BF16, 128, 4, true>(a, max_units, st);
+        if (epi == EPI_STORE_F32) return go_dma<1, 4, 2, 4, EPI_STORE_F32, 128, 4, true>(a, max_units, st);
+        return hipErrorInvalidValue;
+      }
       if (epi == EPI_SWIGLU_BF16) return go_dma<1, 4, 2, 4, EPI_SWIGLU_BF16, 128, 4>(a, max_units, st);
       if (epi == EPI_STORE_BF16) return go_dma<1, 4, 2, 4, EPI_STORE_BF16, 128, 4>(a, max_units, st);
       if (epi == EPI_STORE_F32) return go_dma<1, 4, 2, 4, EPI_STORE_F32, 128, 4>(a, max_units, st);

@@ -113,6 +113,11 @@ CONFIGS = {
         act="bf16", wt="bf16", zipf_s=1.1, bias_alpha=0.5,
         description="one-token decode step of the c4 layer: 8 routed experts of one row each, "
                     "the expert GEMMs split along K"),
+    "c10_decode_fp8": MoEConfig(
+        name="c10_decode_fp8", cid=10, T=128, H=7168, E=256, k=8, I=2048, I_shared=2048,
+        act="bf16", wt="fp8", zipf_s=1.1, bias_alpha=0.5,
+        description="the c4 decode batch with fp8 e4m3 experts (128x128 scales); bf16 shared "
+                    "expert"),
     "c8_decode_w4a8": MoEConfig(
         name="c8_decode_w4a8", cid=8, T=128, H=7168, E=256, k=8, I=2048, I_shared=2048,
         act="bf16", wt="int4", zipf_s=1.1, bias_alpha=0.5,
@@ -143,6 +148,10 @@ CONFIGS = {
         name="p5_skewed_fp8", cid=15, T=700, H=512, E=16, k=4, I=256, I_shared=256,
         act="bf16", wt="fp8", zipf_s=1.2, bias_alpha=1.0,
         description="reduced skewed fp8 layer"),
+    "p5b_decode_fp8": MoEConfig(
+        name="p5b_decode_fp8", cid=25, T=24, H=512, E=64, k=8, I=256, I_shared=256,
+        act="bf16", wt="fp8", zipf_s=1.1, bias_alpha=0.5,
+        description="reduced fp8 decode: many experts with 0-2 rows (the 32-row fp8 tiles)"),
     "p6_prefill_w8a8": MoEConfig(
         name="p6_prefill_w8a8", cid=16, T=700, H=512, E=16, k=4, I=256, I_shared=256,
         act="bf16", wt="int8", zipf_s=1.2, bias_alpha=1.0,
@@ -186,9 +195,9 @@ CONFIGS = {
 
 FULL_CONFIGS = ["c1_tiny_fp32", "c2_prefill_bf16", "c3_ep_rank_bf16",
                 "c4_decode_bf16", "c5_skewed_fp8", "c6_prefill_w8a8", "c7_decode_w8a8",
-                "c8_decode_w4a8", "c9_decode1_bf16"]
+                "c8_decode_w4a8", "c9_decode1_bf16", "c10_decode_fp8"]
 SMALL_CONFIGS = ["c1_tiny_fp32", "p1_small_fp32", "p2_prefill_bf16", "p2b_prefill_bf16",
-                 "p2c_prefill_bf16", "p3_ep_rank_bf16", "p4_decode_bf16", "p5_skewed_fp8",
+                 "p2c_prefill_bf16", "p3_ep_rank_bf16", "p4_decode_bf16", "p5_skewed_fp8", "p5b_decode_fp8",
                  "p6_prefill_w8a8", "p7_decode_w8a8", "p8_prefill_w4a8", "p9_decode_w4a8",
                  "p9b_decode_w4a8", "p10_split_bf16", "p11_split_fp8", "p12_split_w8a8",
                  "p13_split_w4a8"]

@@ -58,7 +58,7 @@ def expert_dict(cfg, experts):
 
 @pytest.mark.parametrize("name", ["c1_tiny_fp32", "c2_prefill_bf16", "c4_decode_bf16", "c5_skewed_fp8",
                                   "c6_prefill_w8a8", "c7_decode_w8a8", "c8_decode_w4a8",
-                                  "c9_decode1_bf16"])
+                                  "c9_decode1_bf16", "c10_decode_fp8"])
 def test_full_layer_sampled(M, name):
     cfg = configs.get(name)
     say("full layer", name, "upload")
