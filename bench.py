@@ -133,16 +133,19 @@ def gathers_rows(cfg) -> bool:
 def launch_accounting(cfg, acc: dict) -> dict:
     """Work per timed launch class: with the shared expert merged, the ffn1 / ffn2
     launches also do the shared expert's two GEMMs and there is no shared stage; with
-    gathered rows there is no expand stage and ffn1 reads x (T rows) instead of the
-    expanded rows (R rows)."""
+    gathered rows ffn1 reads T token rows instead of R expanded rows, and the expand
+    stage writes nothing (bf16) or each token's codes once (fp8 / int8 activations:
+    x read, T x H codes and their scales written)."""
     out = {k: dict(v) for k, v in acc.items() if k not in ("shared1", "shared2")}
     if gathers_rows(cfg):
+        T, H, R = cfg.T, cfg.H, cfg.R
         ab = _bytes(cfg.act)
-        out["expand"] = dict(flops=0, bytes=0, dt=None)
-        out["ffn1"]["bytes"] += cfg.T * cfg.H * ab - cfg.R * cfg.H * ab
-    if shared_is_merged(cfg) and cfg.sh_wt == "int8":
-        # the expansion also writes the tokens' int8 codes in token order for the shared expert
-        out["expand"]["bytes"] += cfg.T * cfg.H + cfg.T * 4
+        fp8 = cfg.wt == "fp8"
+        q = fp8 or cfg.wt in ("int8", "int4")
+        eb = 1 if q else ab
+        sc_row = (H // 128) * 4 if fp8 else 4 if q else 0     # activation scale bytes per row
+        out["expand"] = dict(flops=0, bytes=(T * H * ab + T * H * eb + T * sc_row) if q else 0, dt=None)
+        out["ffn1"]["bytes"] += (T - R) * (H * eb + sc_row)
     if shared_is_merged(cfg):
         for k, sk in (("ffn1", "shared1"), ("ffn2", "shared2")):
             out[k] = dict(flops=out[k]["flops"] + acc[sk]["flops"],

@@ -194,10 +194,16 @@ bool merge_shared(const moe_shape* s) {
   return s->act == MOE_BF16 && (s->wt == MOE_BF16 || s->wt == MOE_INT8) && s->I_shared == s->I;
 }
 
-// bf16 layers gather the routed rows from x inside the first expert GEMM (32-bit
-// row offsets into x: T * H * 2 bytes must stay below 4 GiB).
+// The first expert GEMM gathers the routed rows from the token-order activations
+// through the sort's slot order, so the expanded copy is never written: x itself for
+// bf16 experts, x's per-token codes (fp8 1x128 blocks, int8 rows: one quantization per
+// token instead of k copies) for fp8 and W8A8 experts.  W4A8 experts keep the expanded
+// rows: their 256-element stages ran slower on gathered rows (decode GEMM1 +6%).
+// 32-bit row offsets: T * H * bytes per element must stay below 4 GiB.
 bool gather_rows(const moe_shape* s) {
-  return s->act == MOE_BF16 && s->wt == MOE_BF16 && 2LL * s->T * s->H < (1LL << 32);
+  if (s->act != MOE_BF16 || s->wt == MOE_INT4) return false;
+  const long long eb = s->wt == MOE_BF16 ? 2 : 1;
+  return eb * s->T * s->H < (1LL << 32);
 }
 
 struct FfnLayout {
@@ -276,14 +282,19 @@ Layout layer_layout(const moe_shape* s) {
   L.eri = o;           o += align_up(R * 4);
   L.sorted_src = o;    o += align_up(R * 4);
   const bool i8 = q8_weights(s);
-  L.ex = o;            if (!gather_rows(s)) o += align_up(R * H * (fp8 || i8 ? 1 : ab));
-  L.ex_scale = o;      if (fp8) o += align_up(R * (H / 128) * 4);
-                       if (i8) o += align_up(R * 4);
+  // expanded rows, or (gathered, quantized experts) the per-token codes in token order
+  const bool gathered = gather_rows(s);
+  const size_t qrows = gathered ? T : R;
+  L.ex = o;            if (!gathered) o += align_up(R * H * (fp8 || i8 ? 1 : ab));
+                       else if (fp8 || i8) o += align_up(T * H);
+  L.ex_scale = o;      if (fp8) o += align_up(qrows * (H / 128) * 4);
+                       if (i8) o += align_up(qrows * 4);
   L.y = o;             o += align_up(R * H * ab);
   const bool merged = merge_shared(s);
   L.ffn = o;           o += ffn_layout(s, s->E, static_cast<int>(R), s->I, merged ? s->T : 0).total;
   L.sh_out = o;        o += align_up(T * H * ab);
-  // W8A8 shared expert: the tokens' int8 codes and scales in token order
+  // W8A8 shared expert on the second stream (or beside expanded rows): its own int8
+  // codes and scales of the tokens in token order
   L.sh_xq = o;         if (i8) o += align_up(T * H);
   L.sh_xs = o;         if (i8) o += align_up(T * 4);
   const moe_shape sh = shared_shape(s);
@@ -635,7 +646,7 @@ static moe_status init_routing_impl(const moe_shape* s, const void* x, const int
                                     int32_t* expanded_row_idx, int32_t* sorted_src,
                                     int32_t* tokens_per_expert, int32_t* expert_offsets, void* ws,
                                     size_t ws_bytes, hipStream_t stream, const Prof& prof,
-                                    int8_t* tok_q = nullptr, float* tok_s = nullptr);
+                                    void* tok_q = nullptr, float* tok_s = nullptr);
 
 moe_status moe_init_routing(const moe_shape* s, const void* x, const int32_t* ids, int32_t e_base,
                             void* expanded_x, float* expanded_scale, int32_t* expanded_row_idx,
@@ -652,7 +663,7 @@ static moe_status init_routing_impl(const moe_shape* s, const void* x, const int
                                     int32_t* expanded_row_idx, int32_t* sorted_src,
                                     int32_t* tokens_per_expert, int32_t* expert_offsets, void* ws,
                                     size_t ws_bytes, hipStream_t stream, const Prof& prof,
-                                    int8_t* tok_q, float* tok_s) {
+                                    void* tok_q, float* tok_s) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   const bool fp8 = s->wt == MOE_FP8_E4M3;
@@ -673,12 +684,18 @@ static moe_status init_routing_impl(const moe_shape* s, const void* x, const int
   if (e != hipSuccess || prof.mark(MOE_EV_ROUTE, stream) != hipSuccess) return MOE_EHIP;
   if (expanded_x && s->T > 0) {
     // int8 (W8A8): each token quantized once per row, its codes copied to its k rows
-    // (and, for the layer's shared expert, once more in token order: tok_q / tok_s)
     e = i8 ? moe::launch_quant_rows_i8(x, s->T, s->H, s->k, expanded_row_idx, nullptr,
-                                       static_cast<int8_t*>(expanded_x), expanded_scale, stream,
-                                       tok_q, tok_s)
+                                       static_cast<int8_t*>(expanded_x), expanded_scale, stream)
            : moe::launch_expand(x, s->T, s->H, s->k, elem_bytes(s->act), fp8, expanded_row_idx,
                                 expanded_x, expanded_scale, stream);
+    if (e != hipSuccess) return MOE_EHIP;
+  }
+  if (tok_q && s->T > 0) {
+    // the per-token codes in token order (the layer's gathered first GEMM and its W8A8
+    // shared expert read them): one quantization per token
+    e = i8 ? moe::launch_quant_rows_i8(x, s->T, s->H, 1, nullptr, nullptr, static_cast<int8_t*>(tok_q),
+                                       tok_s, stream)
+           : moe::launch_expand(x, s->T, s->H, 1, 2, true, nullptr, tok_q, tok_s, stream);
     if (e != hipSuccess) return MOE_EHIP;
   }
   if (prof.mark(MOE_EV_EXPAND, stream) != hipSuccess) return MOE_EHIP;
@@ -791,29 +808,40 @@ static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const voi
   // communication overlap], Dispatch Overlap).  When it runs in launches of its own and
   // the caller gives a second stream, it starts there at once and overlaps the routing
   // kernels, which leave most of the machine idle; finalize waits for it.
-  // The W8A8 shared expert reads x as per-token int8 codes in token order: on the second
-  // stream it quantizes x itself, otherwise the expansion writes that copy as well.
+  // Token-order activations of the first expert GEMM and of the W8A8 shared expert: x
+  // for bf16 experts; for quantized experts the per-token codes, written once in the
+  // expansion's place (gathered rows) or beside the expanded rows.  A shared expert on
+  // the second stream quantizes its own copy there.
   const bool merged = merge_shared(s);
-  int8_t* sh_xq = q8 ? at<int8_t>(ws, L.sh_xq) : nullptr;
-  float* sh_xs = q8 ? at<float>(ws, L.sh_xs) : nullptr;
+  const bool gathered = gather_rows(s);
+  const bool quant_act = fp8 || q8;
+  const bool forked = side && !merged;
+  void* tok_q = nullptr;        // per-token codes written by the routing's expansion stage
+  float* tok_s = nullptr;
+  if (quant_act && gathered) {
+    tok_q = at<void>(ws, L.ex);
+    tok_s = at<float>(ws, L.ex_scale);
+  } else if (q8 && !forked) {
+    tok_q = at<void>(ws, L.sh_xq);
+    tok_s = at<float>(ws, L.sh_xs);
+  }
   FfnIo sio{x, nullptr, nullptr, w->sh_w13, nullptr, w->sh_w2, nullptr, at<void>(ws, L.sh_out)};
   if (q8) {
-    sio.a = sh_xq;
-    sio.a_scale = sh_xs;
+    sio.a = forked ? at<void>(ws, L.sh_xq) : tok_q;
+    sio.a_scale = forked ? at<float>(ws, L.sh_xs) : tok_s;
     sio.w13_scale = w->sh_w13_scale;
     sio.w2_scale = w->sh_w2_scale;
   }
   const moe_shape sh = shared_shape(s);
   SideFork sf;
-  const bool forked = side && !merged;
   if (forked) {
     if (hipEventCreateWithFlags(&sf.fork, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&sf.join, hipEventDisableTiming) != hipSuccess ||
         hipEventRecord(sf.fork, stream) != hipSuccess ||
         hipStreamWaitEvent(side, sf.fork, 0) != hipSuccess)
       return MOE_EHIP;
-    if (q8 && moe::launch_quant_rows_i8(x, s->T, s->H, 1, nullptr, nullptr, sh_xq, sh_xs,
-                                        side) != hipSuccess)
+    if (q8 && moe::launch_quant_rows_i8(x, s->T, s->H, 1, nullptr, nullptr, at<int8_t>(ws, L.sh_xq),
+                                        at<float>(ws, L.sh_xs), side) != hipSuccess)
       return MOE_EHIP;
     st = run_ffn(&sh, 1, s->T, s->I_shared, sio, at<void>(ws, L.sh_ffn), side);
     if (st != MOE_OK) return st;
@@ -822,26 +850,24 @@ static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const voi
   // gate + router  ([MND §Expert Parallelism], [MND §MoE Router])
   st = run_gate_topk(s, x, w->w_gate, w->bias, lg, idx, tw, at<float>(ws, L.part), stream, prof, ra);
   if (st != MOE_OK) return st;
-  // first routing: expand and sort by expert  ([R1P §MoE deployment strategy optimization]).
-  // bf16 layers never materialize the expanded rows: the first expert GEMM reads each
-  // row from x through the sort's slot order.
+  // first routing: sort by expert  ([R1P §MoE deployment strategy optimization]); the
+  // expanded rows are written only where the first expert GEMM cannot gather them
   int32_t* eri = at<int32_t>(ws, L.eri);
   int32_t* offs = at<int32_t>(ws, L.offsets);
   int32_t* ssrc = at<int32_t>(ws, L.sorted_src);
-  const bool gathered = gather_rows(s);
   st = init_routing_impl(s, x, idx, 0, gathered ? nullptr : at<void>(ws, L.ex),
-                         (fp8 || q8) ? at<float>(ws, L.ex_scale) : nullptr, eri, ssrc,
-                         at<int32_t>(ws, L.tpe), offs, ws, ws_bytes, stream, prof,
-                         forked ? nullptr : sh_xq, forked ? nullptr : sh_xs);
+                         (!gathered && quant_act) ? at<float>(ws, L.ex_scale) : nullptr, eri, ssrc,
+                         at<int32_t>(ws, L.tpe), offs, ws, ws_bytes, stream, prof, tok_q, tok_s);
   if (st != MOE_OK) return st;
   // routed experts as one grouped GEMM over the expert-sorted rows
   // The shared expert runs on every token ([MND §Expert Parallelism]: its output is
   // added); with the routed experts' shape it is one more group of the same launches.
   const int R = s->T * s->k;
-  FfnIo io{at<void>(ws, L.ex), (fp8 || q8) ? at<float>(ws, L.ex_scale) : nullptr, offs, w->w13,
+  FfnIo io{at<void>(ws, L.ex), quant_act ? at<float>(ws, L.ex_scale) : nullptr, offs, w->w13,
            w->w13_scale, w->w2, w->w2_scale, at<void>(ws, L.y)};
   if (gathered) {
-    io.a = x;
+    io.a = quant_act ? tok_q : x;
+    io.a_scale = quant_act ? tok_s : nullptr;
     io.gather = ssrc;
     io.gather_div = s->k;
   }

@@ -72,12 +72,10 @@ __device__ __forceinline__ void lds_barrier() {
 // address split into a wave-uniform 64-bit base (scalar registers) and a 32-bit per-lane
 // byte offset: the per-lane address needs one VGPR and no 64-bit add.  M0 holds the LDS
 // destination; the DMA is counted by vmcnt like any global load.
-// NT: non-temporal (streaming) cache policy, for data read once.
+// NT: non-temporal (streaming) cache policy, for data read once.  m0: the LDS byte
+// address of the 1 KB chunk (wave-uniform, in a scalar register).
 template <bool NT = false>
-__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint8_t* lds_chunk) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-          (__attribute__((address_space(3))) uint8_t*)lds_chunk)));
+__device__ __forceinline__ void dma16m(const void* base, uint32_t off, uint32_t m0) {
   if constexpr (NT) {
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                  :
@@ -274,10 +272,12 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   if constexpr (FP8) {
     const int kb0 = k0 / kQBlock;
     if (wave < ASW) {
+      // the scale row of this lane's activation row (gathered: the token's row)
       const int r = 64 * wave + lane;
       const int rc = r < rows ? r : rows - 1;
-      sc_base = p.a_scale + static_cast<long long>(un.row0) * p.a_scale_ld + kb0;
-      sc_off = static_cast<uint32_t>(static_cast<long long>(rc) * p.a_scale_ld * 4);
+      const long long src = gather ? gather[un.row0 + rc] / p.gather_div : un.row0 + rc;
+      sc_base = p.a_scale + kb0;
+      sc_off = static_cast<uint32_t>(src * p.a_scale_ld * 4);
     } else {
       int blk;
       if constexpr (SWIGLU) {
@@ -309,18 +309,31 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
     }
     else return i < LMAX ? goff[i] : 0u;
   };
+  // This wavefront's first 1 KB chunk of each ring buffer, as an LDS byte address
+  // (wave-uniform).  Each DMA's M0 is formed from it with a compile-time offset at the
+  // issue itself: the empty asm below makes the base a fresh value per issue, so the
+  // compiler cannot hoist the buffers x chunks M0 values out of the loop into scalar
+  // registers (it spilled them to vector lanes, inside the loop).
+  auto lds_addr = [&](const uint8_t* buf) __attribute__((always_inline)) {
+    return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) uint8_t*)buf)) + wave * 1024u);
+  };
   auto issue = [&](int step, uint8_t* buf, int b) __attribute__((always_inline)) {
     const long long kb = static_cast<long long>(step) * ROWB;
     const uint8_t* ak = a_base + kb;   // wave-uniform bases of this K step
     const uint8_t* bk = b_base + static_cast<long long>(step) * ROWB_B;
+    uint32_t m0w = lds_addr(buf);
+    asm volatile("" : "+s"(m0w));
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i) dma16s(ak, lane_off_of(i), buf + (wave + i * NW) * 1024);
+    for (int i = 0; i < A_PER; ++i) dma16m(ak, lane_off_of(i), m0w + i * NW * 1024u);
     if (NTW_OK && ntb) {
 #pragma unroll
-      for (int i = 0; i < B_PER; ++i) dma16s<true>(bk, lane_off_of(A_PER + i), buf + BM * ROWB + (wave + i * NW) * 1024);
+      for (int i = 0; i < B_PER; ++i)
+        dma16m<true>(bk, lane_off_of(A_PER + i), m0w + BM * ROWB + i * NW * 1024u);
     } else {
 #pragma unroll
-      for (int i = 0; i < B_PER; ++i) dma16s<false>(bk, lane_off_of(A_PER + i), buf + BM * ROWB + (wave + i * NW) * 1024);
+      for (int i = 0; i < B_PER; ++i)
+        dma16m<false>(bk, lane_off_of(A_PER + i), m0w + BM * ROWB + i * NW * 1024u);
     }
     if constexpr (FP8) {
       if (wave < ASW) dma4s(sc_base + step, lane_off_of(LMAX), reinterpret_cast<uint8_t*>(&sa_st[b][64 * wave]));
@@ -336,6 +349,21 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
 
   const int frag_row = lane & 15;
   const int kgrp = lane >> 4;
+
+  // int8 / int4: this lane's activation-row scales for the epilogue, loaded before the
+  // main loop (gathered rows take the scale of the token they read), so nothing of the
+  // gather stays live across the loop
+  float sa[Q8 ? TM : 1];
+  if constexpr (Q8) {
+    const float* sa_base = alt ? p.a_scale2 : p.a_scale;
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int row = 16 * (j * WM + wm) + (lane & 15);
+      sa[j] = (j < jcount && row < rows)
+                  ? sa_base[gather ? gather[un.row0 + row] / p.gather_div : un.row0 + row]
+                  : 0.f;
+    }
+  }
 
   // One stage of MFMAs for a wavefront owning J valid 16-row tiles.  J is a
   // compile-time constant (the main loop is instantiated per row-tile count), so
@@ -515,13 +543,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
     constexpr int HT = TN / 2;
     const float* sw_base =
         alt ? p.b_scale2 : p.b_scale + static_cast<long long>(un.group) * p.b_scale_group;
-    const float* sa_base = alt ? p.a_scale2 : p.a_scale;
-    float sa[TM];
-#pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      const int row = 16 * (j * WM + wm) + crow;
-      sa[j] = (j < jcount && row < rows) ? sa_base[row0_e + row] : 0.f;
-    }
+
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
       int col, ch;   // first output column of this lane in tile i, and its weight channel

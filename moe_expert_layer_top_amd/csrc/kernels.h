@@ -52,9 +52,10 @@ struct GemmArgs {
   // A2 (pitch lda2) and the single weight panel B2 (pitch ldb, like the primary groups),
   // and write C2 (pitch ldc2); int8 units take their scales from a_scale2 [rows] and
   // b_scale2 [Brows].  -1: none.
-  // Gathered activations (bf16 DMA kernels only): when set, row r of a unit of the
-  // primary groups is row gather[row0 + r] / gather_div of A (x indexed by token,
-  // through the slot order of the expert sort) instead of row row0 + r.
+  // Gathered activations (DMA kernels): when set, row r of a unit of the primary groups
+  // is row gather[row0 + r] / gather_div of A (x, or its per-token codes, indexed by
+  // token through the slot order of the expert sort) instead of row row0 + r; fp8 and
+  // int8 rows take their activation scales from the same token row of a_scale.
   const int32_t* gather = nullptr;
   int gather_div = 1;
   int alt_group = -1;
@@ -111,16 +112,16 @@ hipError_t launch_routing(const int32_t* ids, long long R, int e_base, int E, in
                           int32_t* seg_err, int32_t* err_word, int32_t* eri, int32_t* sorted_src,
                           int32_t* tpe, int32_t* offsets, hipStream_t st);
 
+// Writes token t's row (fp8: its 1x128 codes and scales) to rows eri[t*k .. t*k+k-1];
+// eri NULL (fp8, k = 1): to row t, the per-token codes in token order.
 hipError_t launch_expand(const void* x, int T, int H, int k, int act_bytes, bool quant_fp8,
                          const int32_t* eri, void* out, float* out_scale, hipStream_t st);
 
 // int8 per-row quantization of bf16 rows (W8A8 activations).  dst_rows [rows * k] or NULL
-// (in place); n_rows: device count of rows that hold data, or NULL (all); tok_out /
-// tok_scale (or NULL): a second copy of every row's codes and scale, in place.
+// (in place); n_rows: device count of rows that hold data, or NULL (all).
 hipError_t launch_quant_rows_i8(const void* src, int rows, int cols, int k, const int32_t* dst_rows,
                                 const int32_t* n_rows, int8_t* out, float* out_scale,
-                                hipStream_t st, int8_t* tok_out = nullptr,
-                                float* tok_scale = nullptr);
+                                hipStream_t st);
 
 hipError_t launch_finalize(const void* y, const void* skip, const float* w, const int32_t* eri,
                            void* out, int T, int H, int k, int act_bytes, hipStream_t st);

@@ -543,7 +543,8 @@ __global__ __launch_bounds__(256) void expand_quant_kernel(const uint16_t* __res
   const int nblk = H / kQBlock;
   const int lane16 = threadIdx.x & 15;
   const int grp = threadIdx.x >> 4;  // 16 groups of 16 lanes per block
-  const int32_t* dst = eri + static_cast<long long>(t) * k;  // uniform over the block
+  // uniform over the block; NULL: the token's own row (per-token codes in token order)
+  const int32_t* dst = eri ? eri + static_cast<long long>(t) * k : nullptr;
   for (int b = grp; b < nblk; b += 16) {
     const uint4 raw = reinterpret_cast<const uint4*>(x + static_cast<long long>(t) * H +
                                                      b * kQBlock)[lane16];
@@ -570,7 +571,7 @@ __global__ __launch_bounds__(256) void expand_quant_kernel(const uint16_t* __res
     if (zero) lo = hi = 0;
     const uint2 q = make_uint2(lo, hi);
     for (int j = 0; j < k; ++j) {
-      const int32_t d = dst[j];
+      const int32_t d = dst ? dst[j] : t;
       if (d < 0) continue;
       reinterpret_cast<uint2*>(out + static_cast<long long>(d) * H + b * kQBlock)[lane16] = q;
       if (lane16 == 0) out_scale[static_cast<long long>(d) * nblk + b] = scale;
@@ -583,9 +584,7 @@ __global__ __launch_bounds__(256) void expand_quant_kernel(const uint16_t* __res
 // round-half-even(x * (127 / amax)) with scale amax / 127 (a zero row: scale 1, codes 0),
 // all in float32.  dst_rows [rows * k] sends row r to rows dst_rows[r*k + j] (the
 // token expansion; negative entries are skipped); NULL writes row r in place of itself.
-// tok_out / tok_scale (or NULL) receive one more copy of row r in place (the tokens in
-// their own order, for the shared expert).  n_rows (device, or NULL) bounds the rows
-// that hold data.  Rows of up to 8192 columns are read from memory once: each thread
+// n_rows (device, or NULL) bounds the rows that hold data.  Rows of up to 8192 columns are read from memory once: each thread
 // keeps its 8-column vectors in registers between the amax and the coding pass.
 constexpr int kQuantKeep = 4;  // 8-column vectors a thread keeps (256 threads: 8192 columns)
 
@@ -615,9 +614,7 @@ __global__ __launch_bounds__(256) void quant_rows_i8_kernel(const uint16_t* __re
                                                             const int32_t* __restrict__ dst_rows,
                                                             const int32_t* __restrict__ n_rows,
                                                             int8_t* __restrict__ out,
-                                                            float* __restrict__ out_scale,
-                                                            int8_t* __restrict__ tok_out,
-                                                            float* __restrict__ tok_scale) {
+                                                            float* __restrict__ out_scale) {
   __shared__ float wmax[4];
   const int r = blockIdx.x;
   if (n_rows && r >= *n_rows) return;
@@ -645,7 +642,6 @@ __global__ __launch_bounds__(256) void quant_rows_i8_kernel(const uint16_t* __re
       if (d < 0) continue;
       *reinterpret_cast<uint2*>(out + static_cast<long long>(d) * cols + c) = qq;
     }
-    if (tok_out) *reinterpret_cast<uint2*>(tok_out + static_cast<long long>(r) * cols + c) = qq;
   };
 #pragma unroll
   for (int it = 0; it < kQuantKeep; ++it) {
@@ -659,23 +655,23 @@ __global__ __launch_bounds__(256) void quant_rows_i8_kernel(const uint16_t* __re
       const int32_t d = dst_rows ? dst_rows[static_cast<long long>(r) * k + j] : r;
       if (d >= 0) out_scale[d] = scale;
     }
-    if (tok_scale) tok_scale[r] = scale;
   }
 }
 
 hipError_t launch_quant_rows_i8(const void* src, int rows, int cols, int k, const int32_t* dst_rows,
                                 const int32_t* n_rows, int8_t* out, float* out_scale,
-                                hipStream_t st, int8_t* tok_out, float* tok_scale) {
+                                hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  if (cols % 8 || (tok_out == nullptr) != (tok_scale == nullptr)) return hipErrorInvalidValue;
+  if (cols % 8) return hipErrorInvalidValue;
   quant_rows_i8_kernel<<<rows, 256, 0, st>>>(static_cast<const uint16_t*>(src), cols, k, dst_rows,
-                                             n_rows, out, out_scale, tok_out, tok_scale);
+                                             n_rows, out, out_scale);
   return hipGetLastError();
 }
 
 hipError_t launch_expand(const void* x, int T, int H, int k, int act_bytes, bool quant_fp8,
                          const int32_t* eri, void* out, float* out_scale, hipStream_t st) {
   if (T == 0) return hipSuccess;
+  if (!eri && (!quant_fp8 || k != 1)) return hipErrorInvalidValue;   // in place: fp8 codes only
   if (quant_fp8) {
     expand_quant_kernel<<<T, 256, 0, st>>>(static_cast<const uint16_t*>(x), H, k, eri,
                                            static_cast<uint8_t*>(out), out_scale);

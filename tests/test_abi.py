@@ -52,9 +52,10 @@ def test_workspace_query(L):
     # the routed outputs (R x H bf16); a bf16 layer gathers its routed rows from x and
     # keeps no expanded copy of them
     assert 65536 * 7168 * 2 <= n < 2 * 65536 * 7168 * 2
-    # an fp8 layer keeps the quantized expanded rows (R x H bytes) as well
+    # an fp8 layer quantizes each token once (T x H codes) and gathers its routed rows from
+    # them: no expanded copy either
     c5 = M.shape(8192, 7168, 256, 8, 2048, 2048, "bf16", "fp8")
-    assert M.moe_workspace_bytes(c5) >= 65536 * 7168 * (2 + 1)
+    assert 65536 * 7168 * 2 + 8192 * 7168 <= M.moe_workspace_bytes(c5) < 65536 * 7168 * (2 + 1)
     small = M.shape(100, 7168, 256, 8, 2048, 2048, "bf16", "bf16")
     assert 0 < M.moe_workspace_bytes(small) < n
     assert M.moe_workspace_bytes(M.shape(8, 128, 4, 5, 128, 128)) == 0          # k > E
@@ -63,9 +64,11 @@ def test_workspace_query(L):
     assert M.moe_workspace_bytes(M.shape(8, 128, 4, 2, 128, 128, "f32", "bf16")) == 0
     assert M.moe_workspace_bytes(M.shape(8, 128, 4, 2, 128, 128, "bf16", "fp8")) > 0
     assert M.moe_grouped_ffn_workspace_bytes(c2, 256, 65536) > 65536 * 2048 * 2
-    # W8A8: int8 expanded rows (R x H) and row scales; h staged in bf16 and quantized per row
+    # W8A8: per-token int8 codes (T x H) and row scales, gathered like fp8; h staged in bf16
+    # and quantized per row
     c6 = M.shape(8192, 7168, 256, 8, 2048, 2048, "bf16", "int8")
-    assert M.moe_workspace_bytes(c6) >= 65536 * 7168 * (2 + 1)
+    assert M.moe_workspace_bytes(c6) >= 65536 * 7168 * 2 + 8192 * 7168 + 65536 * 2048 * (2 + 1)
+    assert M.moe_layer_plan_of(c6)["rows_gathered"] == 1
     assert M.moe_grouped_ffn_workspace_bytes(c6, 256, 65536) >= 65536 * 2048 * (2 + 1)
     assert M.moe_workspace_bytes(M.shape(8, 128, 4, 2, 128, 128, "f32", "int8")) == 0
     c8 = M.shape(128, 7168, 256, 8, 2048, 2048, "bf16", "int4")
@@ -134,8 +137,8 @@ def test_layer_plan_query(L):
 
     p = plan("c2_prefill_bf16")       # prefill: tall tiles, shared expert merged, rows gathered
     assert p == {"shared_merged": 1, "rows_gathered": 1, "ffn1_splits": 1, "ffn2_splits": 1, "block_m": 320}
-    p = plan("c5_skewed_fp8")         # fp8 experts beside a bf16 shared expert
-    assert p["shared_merged"] == 0 and p["rows_gathered"] == 0 and p["block_m"] == 256
+    p = plan("c5_skewed_fp8")         # fp8 experts beside a bf16 shared expert; rows gathered
+    assert p["shared_merged"] == 0 and p["rows_gathered"] == 1 and p["block_m"] == 256
     assert plan("c6_prefill_w8a8")["shared_merged"] == 1      # int8 shared expert in the int8 launches
     assert plan("c8_decode_w4a8")["shared_merged"] == 0       # int4 experts, int8 shared expert
     p = plan("c4_decode_bf16")        # decode: short tiles, grid large enough not to split

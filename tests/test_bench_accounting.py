@@ -72,10 +72,15 @@ def test_launch_accounting_merged_and_gathered():
     shared1 = 2 * I * H * 2 + T * H * 2 + T * I * 2
     assert la["ffn1"]["bytes"] == w_routed + T * H * 2 + cfg.R * I * 2 + shared1
     assert la["ffn2"]["flops"] == acc["ffn2"]["flops"] + 2 * T * I * H
-    # fp8 layers keep the expanded rows and the separate shared stage
+    # fp8 layers keep the separate shared stage; their expand stage quantizes each token once
+    # (x read, T x H codes and T x H/128 scales written) and ffn1 gathers T token rows
     c5 = configs.get("c5_skewed_fp8")
-    l5 = bench.launch_accounting(c5, bench.account(c5, np.full(c5.E, c5.T * c5.k // c5.E)))
-    assert "shared" in l5 and l5["expand"]["bytes"] > 0
+    a5 = bench.account(c5, np.full(c5.E, c5.T * c5.k // c5.E))
+    l5 = bench.launch_accounting(c5, a5)
+    T5, H5 = c5.T, c5.H
+    assert "shared" in l5
+    assert l5["expand"]["bytes"] == T5 * H5 * 2 + T5 * H5 + T5 * (H5 // 128) * 4
+    assert l5["ffn1"]["bytes"] == a5["ffn1"]["bytes"] - (c5.R - T5) * (H5 + (H5 // 128) * 4)
 
 
 def test_measured_traffic_requires_matching_sources(tmp_path, monkeypatch):
