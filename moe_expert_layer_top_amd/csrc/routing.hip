@@ -396,12 +396,13 @@ __global__ __launch_bounds__(256) void route_place_kernel(const int32_t* __restr
 }
 
 // Single-launch routing for a few segments (decode batches, one rank's share): wave w of
-// one 1024-thread block owns segment w.  Its keys stay in registers from the count to
+// one 1024-thread block owns segment w (`seg` consecutive slots, a multiple of 64 up to
+// kSegSlots).  Its keys stay in registers from the count to
 // the placement and the per-segment counts and their prefix stay in LDS, so the three
 // launches above become one; the order of the result is the same stable slot order.
 __global__ __launch_bounds__(1024) void route_small_kernel(const int32_t* __restrict__ ids,
                                                            long long R, int e_base, int E, int bits,
-                                                           int nseg, int32_t* __restrict__ tpe,
+                                                           int nseg, int seg, int32_t* __restrict__ tpe,
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ err_word,
                                                            int32_t* __restrict__ eri,
@@ -413,15 +414,17 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const int32_t* __rest
   const bool owner = wave < nseg;
   int32_t* cnt = cnt_lds + wave * E;
   int err = 0;
-  const long long s0 = static_cast<long long>(wave) * kSegSlots;
+  const long long s0 = static_cast<long long>(wave) * seg;
+  const int batches = seg / 64;   // 64-slot batches of this wave's segment
   uint32_t keys[kSegSlots / 64];
   if (owner) {
     for (int e = lane; e < E; e += 64) cnt[e] = 0;
 #pragma unroll
     for (int it = 0; it < kSegSlots / 64; ++it)
-      keys[it] = local_key(ids, s0 + it * 64 + lane, R, e_base, E, &err);
+      keys[it] = it < batches ? local_key(ids, s0 + it * 64 + lane, R, e_base, E, &err) : 0u;
 #pragma unroll
     for (int it = 0; it < kSegSlots / 64; ++it) {
+      if (it >= batches) break;
       const long long s = s0 + it * 64 + lane;
       const uint32_t key = keys[it];
       const uint64_t active = __ballot(s < R);
@@ -461,6 +464,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(const int32_t* __rest
   if (!owner) return;
 #pragma unroll
   for (int it = 0; it < kSegSlots / 64; ++it) {
+    if (it >= batches) break;
     const long long s = s0 + it * 64 + lane;
     const uint64_t active = __ballot(s < R);
     if (active == 0) break;
@@ -489,12 +493,17 @@ hipError_t launch_routing(const int32_t* ids, long long R, int e_base, int E, in
   const int nseg = static_cast<int>((R + kSegSlots - 1) / kSegSlots);
   int bits = 0;
   while ((1 << bits) <= E) ++bits;  // keys 0..E (E = invalid sentinel)
-  // up to 16 segments whose counts fit in 60 KB of LDS: one launch
-  const size_t small_lds = static_cast<size_t>(nseg) * E * sizeof(int32_t);
-  if (nseg <= 16 && small_lds <= kSmallRouteLds) {
-    route_small_kernel<<<1, 1024, small_lds, st>>>(ids, R, e_base, E, bits, nseg, tpe, offsets,
-                                                    err_word, eri, sorted_src);
-    return hipGetLastError();
+  // up to 16 x kSegSlots slots: one launch, the slots cut into 16 near-equal segments of
+  // whole 64-slot batches (one per wavefront), if their counts fit in 60 KB of LDS
+  if (nseg <= 16) {
+    const int seg = static_cast<int>(std::max<long long>(64, (((R + 15) / 16) + 63) / 64 * 64));
+    const int nseg_s = static_cast<int>((R + seg - 1) / seg);
+    const size_t small_lds = static_cast<size_t>(nseg_s) * E * sizeof(int32_t);
+    if (small_lds <= kSmallRouteLds) {
+      route_small_kernel<<<1, 1024, small_lds, st>>>(ids, R, e_base, E, bits, nseg_s, seg, tpe,
+                                                      offsets, err_word, eri, sorted_src);
+      return hipGetLastError();
+    }
   }
   const size_t lds = 4 * static_cast<size_t>(E) * sizeof(int32_t);
   if (nseg > 0) {
