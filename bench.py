@@ -267,9 +267,11 @@ EP_STAGES = ["route", "ffn", "unsort", "shared"]
 
 
 def run_gpu_ep(cfg, steps, warmup):
-    """One expert-parallel rank's share (pretagged rows): the re-routing sort with the row
-    copy (moe_init_routing, k = 1), the grouped experts over the rank's experts
-    (moe_grouped_ffn), the un-sort back to arrival order (moe_finalize_routing, k = 1) and
+    """One expert-parallel rank's share (pretagged rows): the re-routing sort
+    (moe_init_routing, k = 1, no row copy), the grouped experts over the rank's experts
+    reading the received rows in place through the sort's slot order
+    (moe_grouped_ffn_gathered), the un-sort back to arrival order (moe_finalize_routing,
+    k = 1) and
     the shared expert on the rank's local tokens (moe_grouped_ffn, G = 1).  The shared
     expert needs none of the routed work, so it runs on a second stream beside it
     ([MND §Computation and communication overlap], Dispatch Overlap); the stages are
@@ -288,7 +290,6 @@ def run_gpu_ep(cfg, steps, warmup):
     R, H, E = cfg.T, cfg.H, cfg.E
     act_dt = torch.float32 if cfg.act == "f32" else torch.int16
     ws = torch.empty(M.moe_workspace_bytes(s), dtype=torch.uint8, device=dev)
-    ex = torch.empty((R, H), dtype=act_dt, device=dev)
     eri = torch.empty(R, dtype=torch.int32, device=dev)
     ssrc = torch.empty(R, dtype=torch.int32, device=dev)
     tpe = torch.empty(E, dtype=torch.int32, device=dev)
@@ -310,9 +311,10 @@ def run_gpu_ep(cfg, steps, warmup):
         with torch.cuda.stream(side):
             M.moe_grouped_ffn(s_sh, 1, cfg.T_local, g["x_local"], None, offs1, g["sh_w13"], None,
                               g["sh_w2"], None, sh, ws2)
-        M.moe_init_routing(s, g["x"], g["ids"], cfg.e_base, ex, None, eri, ssrc, tpe, offs, ws)
+        M.moe_init_routing(s, None, g["ids"], cfg.e_base, None, None, eri, ssrc, tpe, offs, ws)
         mark(1)
-        M.moe_grouped_ffn(s, E, R, ex, None, offs, g["w13"], None, g["w2"], None, y, wsf)
+        M.moe_grouped_ffn_gathered(s, E, R, g["x"], R, None, ssrc, 1, offs, g["w13"], None, g["w2"],
+                                   None, y, wsf)
         mark(2)
         M.moe_finalize_routing(s, y, None, None, eri, y_arr)
         mark(3)
@@ -345,7 +347,7 @@ def account_ep(cfg, tpe) -> dict:
     active = int(np.count_nonzero(tpe))
     R = int(np.sum(tpe))
     return {
-        "route": dict(flops=0, bytes=T * 4 + T * H * ab + R * H * ab + 2 * R * 4 + E * 8, dt=None),
+        "route": dict(flops=0, bytes=T * 4 + 2 * R * 4 + E * 8, dt=None),   # ids in, maps out
         "ffn": dict(flops=2 * R * H * 2 * I + 2 * R * I * H,
                     bytes=active * 3 * I * H * ab + R * H * ab + 2 * R * I * ab + R * H * ab, dt=cfg.act),
         "unsort": dict(flops=0, bytes=2 * R * H * ab + R * 4, dt=None),

@@ -194,6 +194,26 @@ moe_status moe_grouped_ffn(const moe_shape* s, int32_t G, int32_t R_max, const v
                            const float* w2_scale, void* y, void* ws, size_t ws_bytes,
                            hipStream_t stream);
 
+/* moe_grouped_ffn on activations that are not in expert order: expert-sorted row r is
+ * row row_of[r] / row_div of `a`, read in place by the first GEMM, so the sorted copy of
+ * the rows is never written (the row copy of [R1P §MoE deployment strategy optimization]'s
+ * re-routing folded into the grouped GEMM).  row_of is typically sorted_src from
+ * moe_init_routing: row_div = 1 for re-routed rows (k = 1), row_div = k to read tokens.
+ *   a        [a_rows, H]  act, or fp8 / int8 codes as in moe_grouped_ffn, any row order
+ *   a_scale  per row of `a`: fp32 [a_rows, H/128] (fp8), [a_rows] (int8, int4), else NULL
+ *   row_of   [R_max] int32 device array; every entry r < group_offsets[G] must satisfy
+ *            0 <= row_of[r] / row_div < a_rows (the routing's sorted_src does)
+ *   row_div  >= 1
+ * Everything else as moe_grouped_ffn (same workspace).  y equals moe_grouped_ffn's on the
+ * rows gathered into expert order, bit for bit.  MOE_EUNSUPPORTED for fp32 activations
+ * and when a_rows * H element bytes reaches 4 GiB (32-bit row offsets).               */
+moe_status moe_grouped_ffn_gathered(const moe_shape* s, int32_t G, int32_t R_max, const void* a,
+                                    int32_t a_rows, const float* a_scale, const int32_t* row_of,
+                                    int32_t row_div, const int32_t* group_offsets,
+                                    const void* w13, const float* w13_scale, const void* w2,
+                                    const float* w2_scale, void* y, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
+
 /* Un-permute and combine.  [R1P §MoE deployment strategy optimization]:
  * finalize-routing restores token order through expanded_row_idx and forms
  * the weighted sum of the routed outputs plus the shared-expert output:

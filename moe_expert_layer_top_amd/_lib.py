@@ -24,7 +24,7 @@ EXPORTS = [
     "moe_workspace_bytes", "moe_grouped_ffn_workspace_bytes", "moe_gate_topk", "moe_gate_topk_ex",
     "moe_init_routing", "moe_grouped_ffn", "moe_finalize_routing", "moe_layer", "moe_layer_ex",
     "moe_layer_overlap", "moe_layer_profiled", "moe_get_error", "moe_status_str",
-    "moe_layer_plan_of",
+    "moe_layer_plan_of", "moe_grouped_ffn_gathered",
 ]
 SCORING = {"sigmoid": 0, "softmax": 1}
 EV_NAMES = ["start", "gate", "topk", "route", "expand", "plan", "ffn1", "ffn2", "shared", "finalize"]
@@ -101,6 +101,7 @@ def lib() -> ctypes.CDLL:
             "moe_get_error": (I32, [P, P]),
             "moe_status_str": (ctypes.c_char_p, [I32]),
             "moe_layer_plan_of": (I32, [S, ctypes.POINTER(moe_layer_plan)]),
+            "moe_grouped_ffn_gathered": (I32, [S, I32, I32, P, I32, P, P, I32, P, P, P, P, P, P, P, SZ, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -184,6 +185,15 @@ def moe_grouped_ffn(s, G, R_max, a, a_scale, group_offsets, w13, w13_scale, w2, 
                                  _ptr(group_offsets), _ptr(w13), _ptr(w13_scale), _ptr(w2),
                                  _ptr(w2_scale), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
                                  _stream(stream)), "moe_grouped_ffn")
+
+
+def moe_grouped_ffn_gathered(s, G, R_max, a, a_rows, a_scale, row_of, row_div, group_offsets, w13,
+                             w13_scale, w2, w2_scale, y, ws, stream=None):
+    _check(lib().moe_grouped_ffn_gathered(ctypes.byref(s), int(G), int(R_max), _ptr(a), int(a_rows),
+                                          _ptr(a_scale), _ptr(row_of), int(row_div), _ptr(group_offsets),
+                                          _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(y),
+                                          _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_grouped_ffn_gathered")
 
 
 def moe_finalize_routing(s, y, skip, topk_w, expanded_row_idx, out, stream=None):

@@ -365,8 +365,8 @@ struct FfnIo {
   const void* w2;
   const float* w2_scale;
   void* y;
-  // bf16 only: row r of `a` is token gather[r] / gather_div of x (a = x), so the
-  // expert-sorted copy of the tokens is never written
+  // when set, sorted row r is row gather[r] / gather_div of `a` (x or its per-token
+  // codes, or rows in any order), so the expert-sorted copy is never written
   const int32_t* gather = nullptr;
   int gather_div = 1;
 };
@@ -716,6 +716,30 @@ moe_status moe_grouped_ffn(const moe_shape* s, int32_t G, int32_t R_max, const v
   if (scaled && R_max > 0 && (!a_scale || !w13_scale || !w2_scale)) return MOE_EINVAL;
   if (ws_bytes < moe_grouped_ffn_workspace_bytes(s, G, R_max)) return MOE_EWORKSPACE;
   FfnIo io{a, a_scale, group_offsets, w13, w13_scale, w2, w2_scale, y};
+  return run_ffn(s, G, R_max, s->I, io, ws, stream);
+}
+
+moe_status moe_grouped_ffn_gathered(const moe_shape* s, int32_t G, int32_t R_max, const void* a,
+                                    int32_t a_rows, const float* a_scale, const int32_t* row_of,
+                                    int32_t row_div, const int32_t* group_offsets,
+                                    const void* w13, const float* w13_scale, const void* w2,
+                                    const float* w2_scale, void* y, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if ((st = check_inter(s, s->I)) != MOE_OK) return st;
+  if (G < 1 || R_max < 0 || a_rows < 0 || row_div < 1) return MOE_EINVAL;
+  if (s->act == MOE_F32) return MOE_EUNSUPPORTED;   // the fp32 kernels read rows in order
+  const bool fp8 = s->wt == MOE_FP8_E4M3, scaled = fp8 || q8_weights(s);
+  const long long eb = (fp8 || q8_weights(s)) ? 1 : 2;
+  if (eb * a_rows * s->H >= (1LL << 32)) return MOE_EUNSUPPORTED;
+  if (!group_offsets || !ws) return MOE_EINVAL;
+  if (R_max > 0 && (!a || !row_of || !w13 || !w2 || !y)) return MOE_EINVAL;
+  if (scaled && R_max > 0 && (!a_scale || !w13_scale || !w2_scale)) return MOE_EINVAL;
+  if (ws_bytes < moe_grouped_ffn_workspace_bytes(s, G, R_max)) return MOE_EWORKSPACE;
+  FfnIo io{a, a_scale, group_offsets, w13, w13_scale, w2, w2_scale, y};
+  io.gather = row_of;
+  io.gather_div = row_div;
   return run_ffn(s, G, R_max, s->I, io, ws, stream);
 }
 

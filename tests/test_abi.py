@@ -98,6 +98,18 @@ def test_validation_errors_enqueue_nothing(L):
     assert L.moe_grouped_ffn(ctypes.byref(fp8), 8, 32, DUMMY, None, DUMMY, DUMMY, None, DUMMY, None,
                              DUMMY, DUMMY, 1 << 30, None) == M.MOE_EINVAL   # fp8 needs scales
     assert L.moe_finalize_routing(ctypes.byref(s), None, None, None, DUMMY, DUMMY, None) == M.MOE_EINVAL
+    # gathered FFN: row_div >= 1, a row map, no fp32, row offsets of `a` within 32 bits
+    gat = [8, 32, DUMMY, 64, None, DUMMY]
+    rest = [DUMMY, DUMMY, None, DUMMY, None, DUMMY, DUMMY, 1 << 30, None]
+    assert L.moe_grouped_ffn_gathered(ctypes.byref(s), *gat, 0, *rest) == M.MOE_EINVAL
+    assert L.moe_grouped_ffn_gathered(ctypes.byref(s), 8, 32, DUMMY, 64, None, None, 1, *rest) == M.MOE_EINVAL
+    f32 = M.shape(16, 256, 8, 2, 128, 128, "f32", "f32")
+    assert L.moe_grouped_ffn_gathered(ctypes.byref(f32), *gat, 1, *rest) == M.MOE_EUNSUPPORTED
+    wide = M.shape(16, 8192, 8, 2, 128, 128)
+    assert L.moe_grouped_ffn_gathered(ctypes.byref(wide), 8, 32, DUMMY, 1 << 18, None, DUMMY, 1,
+                                      *rest) == M.MOE_EUNSUPPORTED   # 2^18 rows x 16 KB = 4 GiB
+    assert L.moe_grouped_ffn_gathered(ctypes.byref(fp8), 8, 32, DUMMY, 64, None, DUMMY, 1, DUMMY, DUMMY,
+                                      None, DUMMY, None, DUMMY, DUMMY, 1 << 30, None) == M.MOE_EINVAL
     w = M.moe_weights()
     assert L.moe_layer(ctypes.byref(s), ctypes.byref(w), DUMMY, DUMMY, None, None, None, DUMMY, 1 << 30,
                        None) == M.MOE_EINVAL

@@ -142,16 +142,17 @@ def test_ep_rank_share_full(M):
     s = M.shape_of(cfg)
     R, H, E = cfg.T, cfg.H, cfg.E
     ws = torch.empty(M.moe_workspace_bytes(s), dtype=torch.uint8, device="cuda")
-    ex = torch.empty((R, H), dtype=torch.int16, device="cuda")
     eri = torch.empty(R, dtype=torch.int32, device="cuda")
     ssrc = torch.empty(R, dtype=torch.int32, device="cuda")
     tpe = torch.empty(E, dtype=torch.int32, device="cuda")
     offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
     say("ep share full run")
-    M.moe_init_routing(s, g["x"], g["ids"], cfg.e_base, ex, None, eri, ssrc, tpe, offs, ws)
+    # re-routing without a sorted copy: the expert GEMM reads the received rows in place
+    M.moe_init_routing(s, None, g["ids"], cfg.e_base, None, None, eri, ssrc, tpe, offs, ws)
     y = empty_act((R, H), cfg.act)
     wsf = torch.empty(M.moe_grouped_ffn_workspace_bytes(s, E, R), dtype=torch.uint8, device="cuda")
-    M.moe_grouped_ffn(s, E, R, ex, None, offs, g["w13"], None, g["w2"], None, y, wsf)
+    M.moe_grouped_ffn_gathered(s, E, R, g["x"], R, None, ssrc, 1, offs, g["w13"], None, g["w2"], None, y,
+                               wsf)
     y_arr = empty_act((R, H), cfg.act)
     M.moe_finalize_routing(s, y, None, None, eri, y_arr)
     s_sh = M.shape(cfg.T_local, H, 1, 1, cfg.I_shared, cfg.I_shared, cfg.act, cfg.act)

@@ -281,11 +281,13 @@ def test_ep_rank_share(M):
     cfg, d, g = case("p3_ep_rank_bf16")
     say("ep rank share")
     R, H = cfg.T, cfg.H
-    rr = run_init_routing(M, cfg, g, g["ids"], cfg.T, 1, cfg.E, cfg.e_base)
+    # the re-routing writes no sorted copy: the expert GEMM reads the received rows in place
+    rr = run_init_routing(M, cfg, g, g["ids"], cfg.T, 1, cfg.E, cfg.e_base, with_rows=False)
     s = M.shape_of(cfg)
     y = poison_(empty_act((R, H), cfg.act))
     ws = torch.empty(M.moe_grouped_ffn_workspace_bytes(s, cfg.E, R), dtype=torch.uint8, device="cuda")
-    M.moe_grouped_ffn(s, cfg.E, R, rr["ex"], None, rr["offs"], g["w13"], None, g["w2"], None, y, ws)
+    M.moe_grouped_ffn_gathered(s, cfg.E, R, g["x"], R, None, rr["ssrc"], 1, rr["offs"], g["w13"], None,
+                               g["w2"], None, y, ws)
     y_arr = poison_(empty_act((R, H), cfg.act))
     M.moe_finalize_routing(s, y, None, None, rr["eri"], y_arr)
     # shared expert: one group of T_local rows
@@ -305,6 +307,48 @@ def test_ep_rank_share(M):
     # the arrival-order output is the page's index_select(y_sorted, argsort(gathered_ids_unsort))
     y_sorted_bits = host(y).view(np.uint16)
     assert np.array_equal(host(y_arr).view(np.uint16), O.unsort(y_sorted_bits, host(rr["ssrc"])))
+
+
+# Tall and short tiles, split-K, and every weight type.
+GATHERED = ["p2_prefill_bf16", "p4_decode_bf16", "p5_skewed_fp8", "p5b_decode_fp8", "p6_prefill_w8a8",
+            "p8_prefill_w4a8", "p9_decode_w4a8", "p10_split_bf16", "p11_split_fp8", "p12_split_w8a8"]
+
+
+@pytest.mark.parametrize("name", GATHERED)
+def test_grouped_ffn_gathered_matches_copied_rows(M, name):
+    """The gathered grouped FFN reads sorted row r as row row_of[r] / row_div of its input.
+    On the same rows it equals moe_grouped_ffn on the sorted copy, bit for bit: for tokens in
+    token order (row_of = sorted_src, row_div = k) and for the sorted rows shuffled
+    (row_of = the inverse shuffle, row_div = 1)."""
+    cfg, d, g = case(name)
+    say("gathered ffn", name)
+    ids = routing_ids(cfg, d)
+    T, k = ids.shape
+    R = T * k
+    rr = run_init_routing(M, cfg, g, to_dev(np.ascontiguousarray(ids, dtype=np.int32)), T, k, cfg.E, cfg.e_base)
+    s = M.shape(T, cfg.H, cfg.E, k, cfg.I, cfg.I_shared, cfg.act, cfg.wt)
+    ex, exs = rr["ex"], rr["exs"]
+    ws = torch.empty(M.moe_grouped_ffn_workspace_bytes(s, cfg.E, R), dtype=torch.uint8, device="cuda")
+    w = (g["w13"], g.get("w13_scale"), g["w2"], g.get("w2_scale"))
+    want = poison_(empty_act((R, cfg.H), cfg.act))
+    M.moe_grouped_ffn(s, cfg.E, R, ex, exs, rr["offs"], w[0], w[1], w[2], w[3], want, ws)
+    torch.cuda.synchronize()
+    want = host(want).view(np.uint8)
+    # each token's row (codes and scales for quantized activations) is its first slot's row
+    first = rr["eri"].view(T, k)[:, 0].long()
+    tok, tok_s = ex[first].contiguous(), (exs[first].contiguous() if exs is not None else None)
+    y = poison_(empty_act((R, cfg.H), cfg.act))
+    M.moe_grouped_ffn_gathered(s, cfg.E, R, tok, T, tok_s, rr["ssrc"], k, rr["offs"], *w, y, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y).view(np.uint8), want)
+    # sorted rows in a shuffled order: shuffled row i is sorted row p[i]
+    p = torch.randperm(R, generator=torch.Generator().manual_seed(cfg.cid)).to("cuda")
+    inv = torch.argsort(p).to(torch.int32)
+    sh, sh_s = ex[p].contiguous(), (exs[p].contiguous() if exs is not None else None)
+    y = poison_(empty_act((R, cfg.H), cfg.act))
+    M.moe_grouped_ffn_gathered(s, cfg.E, R, sh, R, sh_s, inv, 1, rr["offs"], *w, y, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y).view(np.uint8), want)
 
 
 # ----------------------------------------------------------------------------- edge cases
