@@ -579,11 +579,11 @@ def main_ep(cfg, args):
                       "note": "ms = time the main stream waited for the shared expert"}
     dk = kern["ffn"]
     if dk["bound"] == "mfma":
-        roof = {"kernel": "ffn (plan + GEMM1 + GEMM2 of moe_grouped_ffn)", "bound": "mfma",
+        roof = {"kernel": "ffn (plan + GEMM1 + GEMM2 of moe_grouped_ffn_gathered)", "bound": "mfma",
                 "achieved": acc["ffn"]["flops"] / (r["stage_ms"]["ffn"] / 1e3) / 1e12,
                 "peak": PEAK_TFLOPS[acc["ffn"]["dt"]], "unit": "TFLOP/s"}
     else:
-        roof = {"kernel": "ffn (plan + GEMM1 + GEMM2 of moe_grouped_ffn)", "bound": "hbm",
+        roof = {"kernel": "ffn (plan + GEMM1 + GEMM2 of moe_grouped_ffn_gathered)", "bound": "hbm",
                 "achieved": acc["ffn"]["bytes"] / (r["stage_ms"]["ffn"] / 1e3) / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
