@@ -94,9 +94,11 @@ size_t moe_grouped_ffn_workspace_bytes(const moe_shape* s, int32_t G, int32_t R_
  *   shared_merged  1: the shared expert is one more group of the routed expert launches
  *   rows_gathered  1: the first expert GEMM reads x through the sort (no expanded copy)
  *   block_m        rows per unit of the routed expert GEMMs
+ *   ffn2_tiles_per_wg  output tiles each workgroup of the down projection computes
+ *                  one after another (1 for the decode tiles and fp8)
  * Returns MOE_EINVAL / MOE_EUNSUPPORTED for the shapes moe_layer rejects.           */
 typedef struct {
-  int32_t shared_merged, rows_gathered, ffn1_splits, ffn2_splits, block_m;
+  int32_t shared_merged, rows_gathered, ffn1_splits, ffn2_splits, block_m, ffn2_tiles_per_wg;
 } moe_layer_plan;
 moe_status moe_layer_plan_of(const moe_shape* s, moe_layer_plan* out);
 

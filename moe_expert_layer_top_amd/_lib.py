@@ -53,7 +53,7 @@ class moe_weights(ctypes.Structure):
 class moe_layer_plan(ctypes.Structure):
     _fields_ = [("shared_merged", ctypes.c_int32), ("rows_gathered", ctypes.c_int32),
                 ("ffn1_splits", ctypes.c_int32), ("ffn2_splits", ctypes.c_int32),
-                ("block_m", ctypes.c_int32)]
+                ("block_m", ctypes.c_int32), ("ffn2_tiles_per_wg", ctypes.c_int32)]
 
 
 def moe_layer_plan_of(s) -> dict:

@@ -177,14 +177,26 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   // would drain the DMAs in flight.
   __shared__ uint32_t off_tab[FP8 ? (LMAX + 1) : 1][FP8 ? NT : 1];
 
+  // A workgroup computes TPW consecutive N tiles of one unit (one K split); its ring runs
+  // on from one tile's K steps into the next's, so the next tile's first stage is in
+  // flight while this one's epilogue stores.  Only for plain stores (the down
+  // projection) where the ring is two deep (every wait drains the counter, so the
+  // epilogue's stores cannot shift it) and without fp8.
+  constexpr bool MULTI = !UNIFORM && !FP8 && NST == 2 && (EPI == EPI_STORE_BF16 || EPI == EPI_STORE_F32);
+  const int tpw = MULTI ? p.tiles_per_wg : 1;
+  // tiles past the first address their weight rows by a fixed offset from the first's,
+  // which needs whole tiles along N (the launcher enforces it)
+  if (tpw > 1 && p.N % (SWIGLU ? BN / 2 : BN) != 0) return;
   const int bid = blockIdx.x;
   const int xcd = bid % kXcds;
   const int slot = bid / kXcds;
-  const int per_unit = p.n_tiles * p.splits;
+  const int n_grp = (p.n_tiles + tpw - 1) / tpw;
+  const int per_unit = n_grp * p.splits;
   const int u = (slot / per_unit) * kXcds + xcd;
   const int rem = slot % per_unit;
-  const int nt = rem % p.n_tiles;
-  const int split = rem / p.n_tiles;
+  const int nt0 = (rem % n_grp) * tpw;           // first N tile of this workgroup
+  const int ntc = min(tpw, p.n_tiles - nt0);     // N tiles it computes
+  const int split = rem / n_grp;
   Unit un;
   if constexpr (UNIFORM) {
     if (u * BM >= p.uniform_rows) return;
@@ -254,10 +266,10 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
     if constexpr (SWIGLU) {
       constexpr int WCOLS = TN * 16, HALF = TN * 8;
       const int wn2 = j / WCOLS, jj = j % WCOLS;
-      col = nt * (BN / 2) + wn2 * HALF + (jj % HALF);
+      col = nt0 * (BN / 2) + wn2 * HALF + (jj % HALF);
       grow = (jj < HALF ? 0 : p.up_off) + col;
     } else {
-      col = nt * BN + j;
+      col = nt0 * BN + j;
       grow = col;
     }
     if (col >= p.N) grow -= col - (p.N - 1);
@@ -281,10 +293,10 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
     } else {
       int blk;
       if constexpr (SWIGLU) {
-        blk = (lane == 1) ? p.up_off / kQBlock + nt : nt;          // gate, up block
+        blk = (lane == 1) ? p.up_off / kQBlock + nt0 : nt0;        // gate, up block
       } else {
         const int nb = (p.N + kQBlock - 1) / kQBlock;
-        blk = min(2 * nt + (lane == 1 ? 1 : 0), nb - 1);           // two column blocks
+        blk = min(2 * nt0 + (lane == 1 ? 1 : 0), nb - 1);          // two column blocks
       }
       sc_base = p.b_scale + static_cast<long long>(un.group) * p.b_scale_group + kb0;
       sc_off = static_cast<uint32_t>(static_cast<long long>(blk) * p.b_scale_ld * 4);
@@ -318,10 +330,13 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
     return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
         (const __attribute__((address_space(3))) uint8_t*)buf)) + wave * 1024u);
   };
-  auto issue = [&](int step, uint8_t* buf, int b) __attribute__((always_inline)) {
+  // weight rows between one N tile and the next (the offsets above address tile nt0)
+  const long long tile_b = static_cast<long long>(SWIGLU ? BN / 2 : BN) * p.ldb;
+  auto issue = [&](int t, int step, uint8_t* buf, int b) __attribute__((always_inline)) {
     const long long kb = static_cast<long long>(step) * ROWB;
     const uint8_t* ak = a_base + kb;   // wave-uniform bases of this K step
     const uint8_t* bk = b_base + static_cast<long long>(step) * ROWB_B;
+    if constexpr (MULTI) bk += t * tile_b;
     uint32_t m0w = lds_addr(buf);
     asm volatile("" : "+s"(m0w));
 #pragma unroll
@@ -342,10 +357,6 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   };
 
   f32x4 acc[TM][TN];
-#pragma unroll
-  for (int j = 0; j < TM; ++j)
-#pragma unroll
-    for (int i = 0; i < TN; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int frag_row = lane & 15;
   const int kgrp = lane >> 4;
@@ -487,43 +498,63 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
     }
   };
 
-  // prologue: steps 0 .. NST-2
-#pragma unroll
-  for (int b = 0; b < NST - 1; ++b) {
-    if (b < nsteps) issue(b, b == 0 ? st0 : b == 1 ? st1 : b == 2 ? st2 : st3, b);
-  }
-  auto mainloop = [&](auto Jc) __attribute__((always_inline)) {
+  // The ring runs on across this workgroup's N tiles when each tile's step count is a
+  // whole number of ring turns (step s of every tile then lands in buffer s % NST);
+  // otherwise every tile starts its own ring.
+  const bool chain = MULTI && nsteps % NST == 0;
+  auto buf_of = [&](int b) __attribute__((always_inline)) {
+    return b == 0 ? st0 : b == 1 ? st1 : b == 2 ? st2 : st3;
+  };
+  auto mainloop = [&](auto Jc, int t) __attribute__((always_inline)) {
+    // last step (counted over the workgroup's tiles) that is loaded by this ring
+    const int last = (chain ? ntc : t + 1) * nsteps - 1;
     for (int s0 = 0; s0 < nsteps; s0 += NST) {
 #pragma unroll
       for (int b = 0; b < NST; ++b) {
         const int s = s0 + b;
         if (s < nsteps) {
-          const int issued_after = min(nsteps - 1, s + NST - 2) - s;
+          const int g = t * nsteps + s;
+          const int issued_after = min(last, g + NST - 2) - g;
           wait_step(issued_after);
           lds_barrier();
-          // refill the buffer consumed at step s - 1 with step s + NST - 1
+          // refill the buffer consumed at step s - 1 with step s + NST - 1 (of the next
+          // tile once this one has none left)
           const int nb = (b + NST - 1) % NST;
-          if (s + NST - 1 < nsteps) issue(s + NST - 1, nb == 0 ? st0 : nb == 1 ? st1 : nb == 2 ? st2 : st3, nb);
-          compute(b == 0 ? st0 : b == 1 ? st1 : b == 2 ? st2 : st3, b, Jc);
+          if (s + NST - 1 < nsteps) issue(t, s + NST - 1, buf_of(nb), nb);
+          else if (chain && t + 1 < ntc) issue(t + 1, s + NST - 1 - nsteps, buf_of(nb), nb);
+          compute(buf_of(b), b, Jc);
         }
       }
     }
   };
+  for (int t = 0; t < ntc; ++t) {
+  const int nt = nt0 + t;
+  if (t == 0 || !chain) {
+    // prologue: steps 0 .. NST-2 of this tile
+#pragma unroll
+    for (int b = 0; b < NST - 1; ++b) {
+      if (b < nsteps) issue(t, b, buf_of(b), b);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < TM; ++j)
+#pragma unroll
+    for (int i = 0; i < TN; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   // jcount is wave-uniform and at most TM; every instantiation runs the same
   // sequence of barriers, so wavefronts with different counts stay in step.
   static_assert(TM <= 10, "row-tile dispatch covers TM <= 10");
   switch (jcount) {
-    case 10: if constexpr (TM >= 10) mainloop(std::integral_constant<int, (TM >= 10 ? 10 : 0)>{}); break;
-    case 9: if constexpr (TM >= 9) mainloop(std::integral_constant<int, (TM >= 9 ? 9 : 0)>{}); break;
-    case 8: if constexpr (TM >= 8) mainloop(std::integral_constant<int, (TM >= 8 ? 8 : 0)>{}); break;
-    case 7: if constexpr (TM >= 7) mainloop(std::integral_constant<int, (TM >= 7 ? 7 : 0)>{}); break;
-    case 6: if constexpr (TM >= 6) mainloop(std::integral_constant<int, (TM >= 6 ? 6 : 0)>{}); break;
-    case 5: if constexpr (TM >= 5) mainloop(std::integral_constant<int, (TM >= 5 ? 5 : 0)>{}); break;
-    case 4: if constexpr (TM >= 4) mainloop(std::integral_constant<int, (TM >= 4 ? 4 : 0)>{}); break;
-    case 3: if constexpr (TM >= 3) mainloop(std::integral_constant<int, (TM >= 3 ? 3 : 0)>{}); break;
-    case 2: if constexpr (TM >= 2) mainloop(std::integral_constant<int, (TM >= 2 ? 2 : 0)>{}); break;
-    case 1: mainloop(std::integral_constant<int, 1>{}); break;
-    default: mainloop(std::integral_constant<int, 0>{}); break;
+    case 10: if constexpr (TM >= 10) mainloop(std::integral_constant<int, (TM >= 10 ? 10 : 0)>{}, t); break;
+    case 9: if constexpr (TM >= 9) mainloop(std::integral_constant<int, (TM >= 9 ? 9 : 0)>{}, t); break;
+    case 8: if constexpr (TM >= 8) mainloop(std::integral_constant<int, (TM >= 8 ? 8 : 0)>{}, t); break;
+    case 7: if constexpr (TM >= 7) mainloop(std::integral_constant<int, (TM >= 7 ? 7 : 0)>{}, t); break;
+    case 6: if constexpr (TM >= 6) mainloop(std::integral_constant<int, (TM >= 6 ? 6 : 0)>{}, t); break;
+    case 5: if constexpr (TM >= 5) mainloop(std::integral_constant<int, (TM >= 5 ? 5 : 0)>{}, t); break;
+    case 4: if constexpr (TM >= 4) mainloop(std::integral_constant<int, (TM >= 4 ? 4 : 0)>{}, t); break;
+    case 3: if constexpr (TM >= 3) mainloop(std::integral_constant<int, (TM >= 3 ? 3 : 0)>{}, t); break;
+    case 2: if constexpr (TM >= 2) mainloop(std::integral_constant<int, (TM >= 2 ? 2 : 0)>{}, t); break;
+    case 1: mainloop(std::integral_constant<int, 1>{}, t); break;
+    default: mainloop(std::integral_constant<int, 0>{}, t); break;
   }
 
   // ---- epilogue.  Transposed C fragment of a 16x16 tile: lane holds token row
@@ -688,6 +719,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
         p.c_scale[static_cast<long long>(row0_e + row) * p.c_scale_ld + nt] = scale;
     }
   }
+  }  // N tiles of this workgroup
 }
 
 template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST, bool FP8, bool I8 = false,
@@ -799,7 +831,15 @@ namespace {
 template <int WM, int WN, int TM, int TN, int EPI, int ROWB, int NST, bool FP8 = false, bool I8 = false,
           bool W4 = false>
 hipError_t go_dma(const GemmArgs& a, int max_units, hipStream_t st) {
-  const long long per_unit = static_cast<long long>(a.n_tiles) * a.splits;
+  constexpr int BN = WN * TN * 16;
+  constexpr bool SWIGLU = EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_FP8;
+  const int tpw = a.tiles_per_wg;
+  if (tpw < 1) return hipErrorInvalidValue;
+  // several N tiles per workgroup: grouped two-deep rings with plain stores, without fp8,
+  // whole tiles along N
+  if (tpw > 1 && (FP8 || NST != 2 || SWIGLU || a.uniform_rows > 0 || a.N % BN != 0))
+    return hipErrorInvalidValue;
+  const long long per_unit = static_cast<long long>((a.n_tiles + tpw - 1) / tpw) * a.splits;
   const long long slots = (static_cast<long long>(max_units) + kXcds - 1) / kXcds;
   const long long blocks = slots * kXcds * per_unit;
   if (blocks <= 0) return hipSuccess;

@@ -46,6 +46,10 @@ struct GemmArgs {
   int K;                    // reduction length in elements
   int up_off;               // swiglu: first row of the up projection (= I)
   int n_tiles;              // output tiles along N
+  // N tiles each workgroup computes one after another (its load ring running on from one
+  // tile into the next); > 1 only for grouped plain-store tiles with a two-deep ring, no
+  // fp8, and N a whole number of tiles
+  int tiles_per_wg = 1;
   int splits;               // split-k factor
   int k_chunk;              // elements of K per split (multiple of the stage depth)
   // Alternate group (bf16 and int8 DMA kernels): units whose group equals alt_group read

@@ -187,6 +187,19 @@ CONFIGS = {
     "p13_split_w4a8": MoEConfig(
         name="p13_split_w4a8", cid=43, T=3, H=8192, E=8, k=2, I=1024, I_shared=1024,
         act="bf16", wt="int4", description="three-token decode, split-K first expert GEMM, W4A8"),
+    # ---- prefill with enough experts (128) for the down projection to compute several
+    # output tiles per workgroup: H = 1280 is five 256-column tiles, so the workgroups
+    # take four tiles and then one; I = 384 gives the int8 / int4 down projection an odd
+    # number of K stages (each tile starts its own load ring) ----
+    "p14_multi_bf16": MoEConfig(
+        name="p14_multi_bf16", cid=44, T=1125, H=1280, E=128, k=8, I=256, I_shared=256,
+        act="bf16", wt="bf16", description="prefill, 128 experts, four down-projection tiles per workgroup"),
+    "p15_multi_w8a8": MoEConfig(
+        name="p15_multi_w8a8", cid=45, T=1125, H=1280, E=128, k=8, I=384, I_shared=384,
+        act="bf16", wt="int8", description="W8A8 prefill, 128 experts, several tiles per workgroup, odd K stages"),
+    "p16_multi_w4a8": MoEConfig(
+        name="p16_multi_w4a8", cid=46, T=1125, H=1280, E=128, k=8, I=384, I_shared=384,
+        act="bf16", wt="int4", description="W4A8 prefill, 128 experts, several tiles per workgroup, odd K stages"),
     "p1_small_fp32": MoEConfig(
         name="p1_small_fp32", cid=11, T=150, H=384, E=12, k=3, I=256, I_shared=128,
         act="f32", wt="f32", x_std=0.02, wg_std=0.02, w_std=0.02,
@@ -200,7 +213,7 @@ SMALL_CONFIGS = ["c1_tiny_fp32", "p1_small_fp32", "p2_prefill_bf16", "p2b_prefil
                  "p2c_prefill_bf16", "p3_ep_rank_bf16", "p4_decode_bf16", "p5_skewed_fp8", "p5b_decode_fp8",
                  "p6_prefill_w8a8", "p7_decode_w8a8", "p8_prefill_w4a8", "p9_decode_w4a8",
                  "p9b_decode_w4a8", "p10_split_bf16", "p11_split_fp8", "p12_split_w8a8",
-                 "p13_split_w4a8"]
+                 "p13_split_w4a8", "p14_multi_bf16", "p15_multi_w8a8", "p16_multi_w4a8"]
 
 
 def get(name: str, **overrides) -> MoEConfig:

@@ -309,9 +309,11 @@ def test_ep_rank_share(M):
     assert np.array_equal(host(y_arr).view(np.uint16), O.unsort(y_sorted_bits, host(rr["ssrc"])))
 
 
-# Tall and short tiles, split-K, and every weight type.
+# Tall and short tiles, split-K, several down-projection tiles per workgroup, and every
+# weight type.
 GATHERED = ["p2_prefill_bf16", "p4_decode_bf16", "p5_skewed_fp8", "p5b_decode_fp8", "p6_prefill_w8a8",
-            "p8_prefill_w4a8", "p9_decode_w4a8", "p10_split_bf16", "p11_split_fp8", "p12_split_w8a8"]
+            "p8_prefill_w4a8", "p9_decode_w4a8", "p10_split_bf16", "p11_split_fp8", "p12_split_w8a8",
+            "p14_multi_bf16", "p15_multi_w8a8", "p16_multi_w4a8"]
 
 
 @pytest.mark.parametrize("name", GATHERED)
