@@ -197,12 +197,6 @@ bool merge_shared(const moe_shape* s) {
   return s->act == MOE_BF16 && (s->wt == MOE_BF16 || s->wt == MOE_INT8) && s->I_shared == s->I;
 }
 
-// The first expert GEMM gathers the routed rows from the token-order activations
-// through the sort's slot order, so the expanded copy is never written: x itself for
-// bf16 experts, x's per-token codes (fp8 1x128 blocks, int8 rows: one quantization per
-// token instead of k copies) for fp8 and W8A8 experts.  W4A8 experts keep the expanded
-// rows: their 256-element stages ran slower on gathered rows (decode GEMM1 +6%).
-// 32-bit row offsets: T * H * bytes per element must stay below 4 GiB.
 // N tiles per workgroup of the unsplit down projection with tall bf16 or int8 tiles: the
 // ring's one stage in flight carries on across a tile boundary (the next tile's first
 // stage loads while this tile's epilogue stores) and the workgroup's start-up (unit
@@ -210,7 +204,8 @@ bool merge_shared(const moe_shape* s) {
 // grid still holds a round of workgroups for the CUs (c2's down projection: 2.40 ->
 // 2.32 ms).  The gate / up projection keeps one tile per workgroup: there a second tile
 // re-reads the unit's activation rows (14 KB each at H = 7168), which cost more than the
-// start-up saved (measured +1% at c2, +8% at the EP rank share).
+// start-up saved (measured +1% at c2, +8% at the EP rank share).  The decode tiles keep
+// one tile per workgroup in both GEMMs: grouping four measured 3-7% slower (c7, c8).
 int down_tiles_per_wg(moe::GemmCfg cfg, bool fp8, long long units, int N, int bn) {
   if (cfg != moe::CFG_BIG || fp8 || N % bn != 0) return 1;
   const long long tiles = N / bn;
@@ -219,6 +214,12 @@ int down_tiles_per_wg(moe::GemmCfg cfg, bool fp8, long long units, int N, int bn
   return 1;
 }
 
+// The first expert GEMM gathers the routed rows from the token-order activations
+// through the sort's slot order, so the expanded copy is never written: x itself for
+// bf16 experts, x's per-token codes (fp8 1x128 blocks, int8 rows: one quantization per
+// token instead of k copies) for fp8 and W8A8 experts.  W4A8 experts keep the expanded
+// rows: their 256-element stages ran slower on gathered rows (decode GEMM1 +6%).
+// 32-bit row offsets: T * H * bytes per element must stay below 4 GiB.
 bool gather_rows(const moe_shape* s) {
   if (s->act != MOE_BF16 || s->wt == MOE_INT4) return false;
   const long long eb = s->wt == MOE_BF16 ? 2 : 1;
