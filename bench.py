@@ -547,7 +547,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8" if cfg.wt == "int4" else cfg.wt if cfg.wt in ("fp8", "int8") else cfg.act,
-        "data": "synthetic (seeded; see DESIGN.md input recipe)",
+        "data": "synthetic (seeded generators of synth/inputs.py)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
                    "I_shared": cfg.I_shared, "act": cfg.act, "wt": cfg.wt},
         "roofline": roof,
@@ -604,7 +604,7 @@ def main_ep(cfg, args):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.act,
-        "data": "synthetic (seeded; see DESIGN.md input recipe)",
+        "data": "synthetic (seeded generators of synth/inputs.py)",
         "config": {"workload": cfg.name, "rows": cfg.T, "T_local": cfg.T_local, "H": cfg.H, "E": cfg.E,
                    "e_base": cfg.e_base, "I": cfg.I, "I_shared": cfg.I_shared, "act": cfg.act, "wt": cfg.wt},
         "rows_per_s": cfg.T * 1e3 / ms,
