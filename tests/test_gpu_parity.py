@@ -353,6 +353,22 @@ def test_grouped_ffn_gathered_matches_copied_rows(M, name):
     assert np.array_equal(host(y).view(np.uint8), want)
 
 
+def test_grouped_ffn_gathered_no_rows(M):
+    """No rows at all (every group empty): the call succeeds without a row pointer or a
+    row map and leaves the output as it was."""
+    cfg, d, g = case("p4_decode_bf16")
+    say("gathered ffn, no rows")
+    s = M.shape(0, cfg.H, cfg.E, cfg.k, cfg.I, cfg.I_shared, cfg.act, cfg.wt)
+    offs = torch.zeros(cfg.E + 1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(M.moe_grouped_ffn_workspace_bytes(s, cfg.E, 0), dtype=torch.uint8, device="cuda")
+    y = poison_(empty_act((4, cfg.H), cfg.act))
+    torch.cuda.synchronize()
+    before = host(y).copy()
+    M.moe_grouped_ffn_gathered(s, cfg.E, 0, None, 0, None, None, 1, offs, g["w13"], None, g["w2"], None, y, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y).view(np.uint8), before.view(np.uint8))
+
+
 # ----------------------------------------------------------------------------- edge cases
 
 def test_all_tokens_to_one_expert(M):
