@@ -98,12 +98,15 @@ struct GatePlan {
   int splits, k_chunk;
 };
 
+// The gate's 64-row tiles split K until the grid holds about one workgroup per CU (at most
+// kGateMaxSplits slices): prefill keeps its partials small (c2: 2 slices, gate 0.063 ->
+// 0.058 ms against 4), decode gets enough workgroups to stream x and the gate matrix.
 GatePlan gate_plan(const moe_shape* s) {
   if (s->act == MOE_F32) return {1, s->H};
   const int bm = moe::gemm_block_m(moe::CFG_GATE, false);
   const int mtiles = std::max(1, (s->T + bm - 1) / bm);
   const int ksteps = s->H / 64;
-  int splits = std::min(ksteps, std::max(1, 512 / mtiles));
+  int splits = std::min(ksteps, std::max(1, static_cast<int>(kCus) / mtiles));
   splits = std::min(splits, kGateMaxSplits);
   const int steps_per = (ksteps + splits - 1) / splits;
   splits = (ksteps + steps_per - 1) / steps_per;
