@@ -108,6 +108,11 @@ def test_validation_errors_enqueue_nothing(L):
     wide = M.shape(16, 8192, 8, 2, 128, 128)
     assert L.moe_grouped_ffn_gathered(ctypes.byref(wide), 8, 32, DUMMY, 1 << 18, None, DUMMY, 1,
                                       *rest) == M.MOE_EUNSUPPORTED   # 2^18 rows x 16 KB = 4 GiB
+    # int8 codes are one byte: the same limit falls at twice the rows
+    wide8 = M.shape(16, 8192, 8, 2, 128, 128, "bf16", "int8")
+    sc = [DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 1 << 30, None]
+    assert L.moe_grouped_ffn_gathered(ctypes.byref(wide8), 8, 32, DUMMY, 1 << 19, DUMMY, DUMMY, 1,
+                                      *sc) == M.MOE_EUNSUPPORTED
     assert L.moe_grouped_ffn_gathered(ctypes.byref(fp8), 8, 32, DUMMY, 64, None, DUMMY, 1, DUMMY, DUMMY,
                                       None, DUMMY, None, DUMMY, DUMMY, 1 << 30, None) == M.MOE_EINVAL
     w = M.moe_weights()
