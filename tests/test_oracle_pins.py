@@ -608,3 +608,171 @@ def test_bf16_decode_exact():
     # 0x7F7F is the largest finite bf16: (2 - 2^-7) * 2^127
     assert moe.bf16_bits_to_f64(np.array([0x3F80, 0xC000, 0x0000, 0x7F7F], np.uint16)).tolist() == \
         [1.0, -2.0, 0.0, (2.0 - 2.0 ** -7) * 2.0 ** 127]
+
+
+# ----------------------------------------------------------------------------- group -> expert mapping
+
+def _expert_of_row(offsets, r):
+    """The group that holds sorted row r, found by scanning the offsets (no search routine)."""
+    for e in range(len(offsets) - 1):
+        if offsets[e] <= r < offsets[e + 1]:
+            return e
+    raise AssertionError(f"row {r} outside every group")
+
+
+def _row_swiglu(a_row, w13, w2):
+    I = w13.shape[0] // 2
+    g = np.array([np.dot(w13[i], a_row) for i in range(I)])
+    u = np.array([np.dot(w13[I + i], a_row) for i in range(I)])
+    h = g / (1.0 + np.exp(-g)) * u
+    return np.array([np.dot(w2[o], h) for o in range(w2.shape[0])])
+
+
+# uneven groups with an empty one in the middle and one at the end
+_GROUP_SIZES = [3, 0, 5, 1, 2, 0]
+
+
+def test_grouped_ffn_uses_each_groups_own_weights():
+    """[MND §Roofline / GroupGEMM]: group i multiplies its own m_i rows by its own
+    weights.  Distinct random weights per group and uneven group sizes (two empty
+    groups): every output row equals the SwiGLU FFN of that row with the weights of
+    the group whose offset range holds the row, found by scanning the offsets."""
+    rng = np.random.default_rng(31)
+    G, H, I = len(_GROUP_SIZES), 6, 4
+    offs = np.concatenate([[0], np.cumsum(_GROUP_SIZES)]).astype(np.int32)
+    a = rng.standard_normal((int(offs[-1]), H))
+    w13 = rng.standard_normal((G, 2 * I, H))
+    w2 = rng.standard_normal((G, H, I))
+    asked = []
+
+    def weights(e):
+        asked.append(e)
+        return w13[e], w2[e]
+    y = moe.grouped_ffn(a, offs, weights)
+    # only non-empty groups are asked for their weights, each once
+    assert asked == [e for e, n in enumerate(_GROUP_SIZES) if n > 0]
+    for r in range(a.shape[0]):
+        e = _expert_of_row(offs, r)
+        assert np.allclose(y[r], _row_swiglu(a[r], w13[e], w2[e]), rtol=1e-12, atol=1e-12), (r, e)
+    # a wrong mapping is visible: the rows of group 2 differ from group 3's FFN of them
+    assert not np.allclose(y[3:8], np.stack([_row_swiglu(a[r], w13[3], w2[3]) for r in range(3, 8)]))
+
+
+def _fp8_dequant_by_index(codes, scale):
+    """Independent dequantization: torch's e4m3fn decode times the scale of the 128x128
+    block holding each element, picked by integer index arrays."""
+    v = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).float().numpy()
+    N, K = codes.shape
+    rows = np.arange(N) // 128
+    cols = np.arange(K) // 128
+    return v.astype(np.float64) * scale.astype(np.float64)[rows][:, cols]
+
+
+def _int4_unpack_loops(packed, K):
+    """Per 16 elements of K: byte i holds element i (low nibble) and 8 + i (high nibble);
+    each nibble is a 4-bit two's-complement code."""
+    out = np.zeros((packed.shape[0], K), dtype=np.int64)
+    for n in range(packed.shape[0]):
+        for b in range(K // 2):
+            byte = int(packed[n, b])
+            grp, i = divmod(b, 8)
+            lo, hi = byte & 0xF, byte >> 4
+            out[n, 16 * grp + i] = lo - 16 if lo >= 8 else lo
+            out[n, 16 * grp + 8 + i] = hi - 16 if hi >= 8 else hi
+    return out
+
+
+@pytest.mark.parametrize("wt", ["fp8", "int8", "int4"])
+def test_expert_weights_adapter_maps_each_expert(wt):
+    """The per-expert float64 weights that the layer hands to the grouped FFN are expert
+    e's own codes times expert e's own scales, for every quantized weight type; with
+    them the grouped FFN of uneven groups (two empty) matches the per-row FFN of each
+    row's own expert."""
+    rng = np.random.default_rng({"fp8": 41, "int8": 42, "int4": 43}[wt])
+    G, H, I = len(_GROUP_SIZES), 128, 128
+    cfg = configs.get("c1_tiny_fp32", H=H, I=I, E=G, wt=wt, act="bf16")
+    inp = {"cfg": cfg}
+    ref = {}
+    if wt == "fp8":
+        # codes of finite values only (0x7F / 0xFF are NaN); scales differ per block and expert
+        def codes(shape):
+            c = rng.integers(0, 0x7F, size=shape).astype(np.uint8)
+            return c | (rng.integers(0, 2, size=shape).astype(np.uint8) << 7)
+        w13 = codes((G, 2 * I, H))
+        w2 = codes((G, H, I))
+        s13 = np.exp2(rng.integers(-12, -6, size=(G, 2 * I // 128, H // 128))).astype(np.float32)
+        s2 = np.exp2(rng.integers(-12, -6, size=(G, H // 128, I // 128))).astype(np.float32)
+        for e in range(G):
+            ref[e] = (_fp8_dequant_by_index(w13[e], s13[e]), _fp8_dequant_by_index(w2[e], s2[e]))
+    else:
+        if wt == "int8":
+            w13 = rng.integers(-127, 128, size=(G, 2 * I, H)).astype(np.int8)
+            w2 = rng.integers(-127, 128, size=(G, H, I)).astype(np.int8)
+            u13 = w13.astype(np.int64)
+            u2 = w2.astype(np.int64)
+        else:
+            w13 = rng.integers(0, 256, size=(G, 2 * I, H // 2)).astype(np.uint8)
+            w2 = rng.integers(0, 256, size=(G, H, I // 2)).astype(np.uint8)
+            u13 = [_int4_unpack_loops(w13[e], H) for e in range(G)]
+            u2 = [_int4_unpack_loops(w2[e], I) for e in range(G)]
+        s13 = (rng.random((G, 2 * I)) * 0.01 + 0.001).astype(np.float32)
+        s2 = (rng.random((G, H)) * 0.01 + 0.001).astype(np.float32)
+        for e in range(G):
+            ref[e] = (u13[e] * s13[e].astype(np.float64)[:, None], u2[e] * s2[e].astype(np.float64)[:, None])
+    inp.update(w13=w13, w2=w2, w13_scale=s13, w2_scale=s2)
+    get = moe.expert_weights_f64(inp)
+    for e in range(G):
+        g13, g2 = get(e)
+        assert np.array_equal(g13, ref[e][0]), e
+        assert np.array_equal(g2, ref[e][1]), e
+    offs = np.concatenate([[0], np.cumsum(_GROUP_SIZES)]).astype(np.int32)
+    a = rng.standard_normal((int(offs[-1]), H)) * 0.5
+    y = moe.grouped_ffn(a, offs, get)
+    for r in range(a.shape[0]):
+        e = _expert_of_row(offs, r)
+        want = _row_swiglu(a[r], *ref[e])
+        assert np.allclose(y[r], want, rtol=1e-10, atol=1e-10 * np.abs(want).max()), (r, e)
+
+
+# ----------------------------------------------------------------------------- bf16 rounding
+
+def test_round_to_bf16_matches_library_cast():
+    """Independent routine: torch's float32 -> bfloat16 cast (round to nearest even) on
+    random float32 values over many binades and on exact ties."""
+    rng = np.random.default_rng(51)
+    v = (rng.standard_normal(300_000) * np.exp2(rng.integers(-60, 60, 300_000))).astype(np.float32)
+    # exact halfway cases: low 16 bits 0x8000 with even and odd kept halves
+    ties = (rng.integers(0, 2 ** 31, 2000, dtype=np.uint32) & 0xFFFF0000) | 0x8000
+    v = np.concatenate([v, ties.view(np.float32)])
+    v = v[np.isfinite(v) & (np.abs(v) < 3.3e38)]
+    ref = torch.from_numpy(v.copy()).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(moe.round_to_bf16(v), ref)
+
+
+def test_round_to_bf16_closed_form_points():
+    one_plus_tie = np.array([1.0 + 2.0 ** -8], dtype=np.float32)      # halfway between 1 and 1 + 2^-7
+    assert moe.round_to_bf16(one_plus_tie)[0] == 1.0                   # even kept half
+    three_tie = np.array([1.0 + 3 * 2.0 ** -8], dtype=np.float32)     # between 1 + 2^-7 and 1 + 2^-6
+    assert moe.round_to_bf16(three_tie)[0] == np.float32(1.0 + 2.0 ** -6)
+    assert moe.round_to_bf16(np.array([-0.0], dtype=np.float32)).view(np.uint32)[0] == 0x80000000
+    bf = np.arange(0, 65536, 7, dtype=np.uint32) << 16                 # bf16 values stay put
+    bf = bf.view(np.float32)[np.isfinite(bf.view(np.float32))]
+    assert np.array_equal(moe.round_to_bf16(bf), bf)
+
+
+def test_w8a8_h_codes_come_from_bf16_h():
+    """The W8A8 down projection's input codes are the per-row int8 quantization of h
+    rounded to bf16 (the precision the GPU holds h in when it takes that decision)."""
+    rng = np.random.default_rng(52)
+    a = rng.standard_normal((5, 32))
+    w13 = rng.standard_normal((16, 32)) * 0.3
+    w2 = np.eye(8)                                   # y = dequantized h
+    I = 8
+    g, u = a @ w13[:I].T, a @ w13[I:].T
+    h = g / (1.0 + np.exp(-g)) * u
+    hb = torch.from_numpy(h.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    amax = np.abs(hb).max(axis=1)
+    scale = (amax / np.float32(127)).astype(np.float32)
+    codes = np.rint(hb * (np.float32(127) / amax)[:, None].astype(np.float32))
+    want = codes * scale.astype(np.float64)[:, None]
+    assert np.array_equal(moe.swiglu_ffn(a, w13, w2, quant_h="int8"), want)
