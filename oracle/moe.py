@@ -47,6 +47,22 @@ def bf16_bits_to_f64(u16: np.ndarray) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
+def round_to_bf16(v32: np.ndarray) -> np.ndarray:
+    """float32 -> the nearest bf16 value (ties to even), returned as float32.
+
+    bf16 keeps the sign, the 8 exponent bits and the top 7 mantissa bits of a float32,
+    so rounding works on the float32 bit pattern: the low 16 bits are dropped after
+    adding half a bf16 step (0x7FFF) plus the kept half's last bit (ties to even).
+    Finite inputs only (the GPU path never rounds a NaN or an infinity here).
+    """
+    x = np.asarray(v32, dtype=np.float32)
+    if not np.isfinite(x).all():
+        raise ValueError("the oracle rounds finite values only")
+    u = x.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
 def fp8_e4m3fn_decode(codes: np.ndarray) -> np.ndarray:
     """OCP FP8 E4M3FN code -> float64.
 
@@ -54,14 +70,25 @@ def fp8_e4m3fn_decode(codes: np.ndarray) -> np.ndarray:
     subnormal (m/8 * 2^-6); the all-ones pattern S.1111.111 is NaN and there are
     no infinities, so the largest finite magnitude is 1.75 * 2^8 = 448.
     """
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
-    sign = np.where(c & 0x80, -1.0, 1.0)
-    exp = (c >> 3) & 0xF
-    man = (c & 0x7).astype(np.float64)
-    val = np.where(exp == 0, man / 8.0 * 2.0 ** -6,
-                   (1.0 + man / 8.0) * np.exp2(exp.astype(np.float64) - 7.0))
-    val = np.where((c & 0x7F) == 0x7F, np.nan, val)
-    return sign * val
+    return _fp8_decode_table()[np.asarray(codes, dtype=np.uint8)]
+
+
+_FP8_DECODE = []
+
+
+def _fp8_decode_table() -> np.ndarray:
+    """The decode of every one of the 256 codes (the formula above, evaluated once); a
+    tensor of codes is decoded by indexing it."""
+    if not _FP8_DECODE:
+        c = np.arange(256, dtype=np.int64)
+        sign = np.where(c & 0x80, -1.0, 1.0)
+        exp = (c >> 3) & 0xF
+        man = (c & 0x7).astype(np.float64)
+        val = np.where(exp == 0, man / 8.0 * 2.0 ** -6,
+                       (1.0 + man / 8.0) * np.exp2(exp.astype(np.float64) - 7.0))
+        val = np.where((c & 0x7F) == 0x7F, np.nan, val)
+        _FP8_DECODE.append(sign * val)
+    return _FP8_DECODE[0]
 
 
 def fp8_e4m3fn_encode(v: np.ndarray) -> np.ndarray:
@@ -337,14 +364,20 @@ def swiglu_ffn(a: np.ndarray, w13: np.ndarray, w2: np.ndarray, quant_h=False) ->
     [MND §Quantization]: the SiLU output is quantized per 1x128 block for the
     fp8 down projection; ``quant_h`` True (or "fp8") applies that quantization
     (float32 values, then :func:`quant_1x128`) before the down projection, and
-    "int8" the per-token int8 quantization of W8A8 (:func:`quant_per_token_int8`).
+    "int8" the per-token int8 quantization of W8A8 (:func:`quant_per_token_int8`) of
+    h rounded to bf16 (:func:`round_to_bf16`).
     """
     I = w13.shape[0] // 2
     g = a @ w13[:I].T
     u = a @ w13[I:].T
     h = g * sigmoid(g) * u
     if quant_h == "int8":
-        q, s = quant_per_token_int8(h.astype(np.float32))
+        # The row's int8 codes are decided from h held in bf16 (float32 h rounded to the
+        # nearest bf16): the page fixes no precision for h before its A8 quantization, so
+        # the decision is taken in the precision the kernels hold h in (they store h in
+        # bf16 and quantize each row from those values; a row's amax spans all I columns,
+        # which no single kernel tile holds).
+        q, s = quant_per_token_int8(round_to_bf16(h.astype(np.float32)))
         h = dequant_rows(q, s)
     elif quant_h:
         q, s = quant_1x128(h.astype(np.float32))
@@ -417,20 +450,32 @@ def expert_weights_f64(inp: dict):
     return get
 
 
-def shared_expert(x: np.ndarray, inp: dict) -> np.ndarray:
+def shared_weights_f64(inp: dict):
+    """The shared expert's float64 (w13, w2): dequantized int8 codes beside W8A8 / W4A8
+    experts, else the activation-dtype weights."""
+    cfg = inp["cfg"]
+    if cfg.sh_wt == "int8":
+        return (dequant_rows(inp["sh_w13"], inp["sh_w13_scale"]),
+                dequant_rows(inp["sh_w2"], inp["sh_w2_scale"]))
+    return to_f64(inp["sh_w13"], cfg.sh_wt), to_f64(inp["sh_w2"], cfg.sh_wt)
+
+
+def shared_expert(x: np.ndarray, inp: dict, weights=None) -> np.ndarray:
     """The shared expert on float64 tokens x: the same SwiGLU FFN with the shared
     weights ([MND §Expert Parallelism]).  Beside W8A8 or W4A8 routed experts it is
     W8A8 ([V32 §quantization strategy] quantizes the shared expert W8A8 in both): per-
-    token int8 tokens, int8 weights with per-channel scales, h requantized per row."""
+    token int8 tokens, int8 weights with per-channel scales, h requantized per row.
+    ``weights``: the float64 (w13, w2) of :func:`shared_weights_f64`, if already made."""
     cfg = inp["cfg"]
+    w13, w2 = shared_weights_f64(inp) if weights is None else weights
     if cfg.sh_wt == "int8":
         xq, xs = quant_per_token_int8(x.astype(np.float32))
-        return swiglu_ffn(dequant_rows(xq, xs), dequant_rows(inp["sh_w13"], inp["sh_w13_scale"]),
-                          dequant_rows(inp["sh_w2"], inp["sh_w2_scale"]), quant_h="int8")
-    return swiglu_ffn(x, to_f64(inp["sh_w13"], cfg.sh_wt), to_f64(inp["sh_w2"], cfg.sh_wt))
+        return swiglu_ffn(dequant_rows(xq, xs), w13, w2, quant_h="int8")
+    return swiglu_ffn(x, w13, w2)
 
 
-def moe_layer(inp: dict, logits32_override=None, router=None) -> dict:
+def moe_layer(inp: dict, logits32_override=None, router=None, expert_weights=None,
+              shared_weights=None) -> dict:
     """The whole layer on one GPU's share, step by step.
 
     Token path ([MND §Expert Parallelism], [R1P §MoE deployment strategy
@@ -443,6 +488,9 @@ def moe_layer(inp: dict, logits32_override=None, router=None) -> dict:
     ``logits32_override`` lets a test route on another float32 logit matrix
     (the routing policy is exact only given identical float32 logits); ``router``
     selects a variant of the router (route_grouped), default the workload's.
+    ``expert_weights`` (e -> float64 (w13, w2), default :func:`expert_weights_f64`) and
+    ``shared_weights`` (float64 (w13, w2), default :func:`shared_weights_f64`) let a
+    caller hand in weights it has already converted, e.g. one expert at a time.
     """
     cfg = inp["cfg"]
     fp8 = cfg.wt == "fp8"
@@ -481,11 +529,11 @@ def moe_layer(inp: dict, logits32_override=None, router=None) -> dict:
     else:
         res["expanded_x"] = expand_rows(inp["x"], rt["sorted_src"], k)
         a = expand_rows(x, rt["sorted_src"], k)
-    y = grouped_ffn(a, rt["expert_offsets"], expert_weights_f64(inp),
+    y = grouped_ffn(a, rt["expert_offsets"], expert_weights or expert_weights_f64(inp),
                     quant_h="int8" if int8 else fp8)
     res["y_sorted"] = y
     sx = to_f64(inp["x_local"], cfg.act) if cfg.pretagged else x
-    s = shared_expert(sx, inp)
+    s = shared_expert(sx, inp, shared_weights)
     res["shared"] = s
     if cfg.pretagged:
         res["y_arrival"] = finalize(y, rt["expanded_row_idx"], 1)

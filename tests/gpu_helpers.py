@@ -7,9 +7,17 @@ import sys
 import numpy as np
 import torch
 
-# max relative error bounds: bf16 2e-2, fp8 6e-2, fp32 1e-5 (the workload statement);
-# W8A8 6e-2 (its own quantization error against unquantized activations is <= 2.5%)
-TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "int8": 6e-2, "int4": 6e-2}
+# max relative error bounds: bf16 2e-2, fp8 6e-2, fp32 1e-5 (the workload statement).
+# W8A8 / W4A8: 2e-2, the bf16 bound.  Their integer work is exact on both sides (int8
+# codes of the tokens bit for bit, int32 accumulation); the oracle decides h's int8 codes
+# from h rounded to bf16, the precision the kernels hold h in, so a code differs only
+# where the two float32 h values straddle a bf16 rounding boundary (about one element in
+# 4000, by one code step, i.e. at most 1/127 of the row's amax times one weight); what
+# remains is the bf16 rounding of h and y, as in the bf16 layer.
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "int8": 2e-2, "int4": 2e-2}
+
+# (test, workload, observed max row relative error, bound) of every checked float output
+ERRS = []
 
 
 def say(*a):
@@ -68,3 +76,13 @@ def poison_(t: torch.Tensor):
     else:
         t.fill_(0x7F)  # fp8 NaN code
     return t
+
+
+def check_close(label: str, got: np.ndarray, ref: np.ndarray, tol: float) -> float:
+    """max_row_rel_err(got, ref) <= tol; the observed error is printed and recorded so
+    the run's summary lists every workload's margin."""
+    err = max_row_rel_err(got, ref)
+    ERRS.append((label, err, tol))
+    say(f"  {label}: max row rel err {err:.3e} (bound {tol:.0e})")
+    assert err <= tol, f"{label}: {err:.3e} > {tol:.0e}"
+    return err
