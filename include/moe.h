@@ -108,7 +108,8 @@ moe_status moe_layer_plan_of(const moe_shape* s, moe_layer_plan* out);
  *   x       [T, H]  act           tokens
  *   w_gate  [E, H]  act           gate matrix
  *   bias    [E]     fp32 or NULL  added to the logits: z = logit + bias
- *   logits  [T, E]  fp32          OUT: x . w_gate^T (fp32 accumulate), required
+ *   logits  [T, E]  fp32 or NULL  OUT: x . w_gate^T (fp32 accumulate); NULL: kept in
+ *                                 the workspace only
  *   topk_idx[T, k]  int32         OUT: the k largest z, descending; equal z -> lower id
  *   topk_w  [T, k]  fp32          OUT: sigmoid(z) of the selected, renormalized to sum 1
  *   ws      workspace of moe_workspace_bytes(s) bytes                          */
@@ -249,6 +250,11 @@ typedef struct {
 
 /* The whole layer: gate + top-k, init-routing, grouped experts, shared expert
  * and finalize-routing, enqueued on one stream with no host synchronization.
+ * [MND §Expert Parallelism]: each token goes to k different routed experts, whose
+ * outputs are summed with the router's weights, and the shared expert's output is
+ * added; [R1P §MoE deployment strategy optimization]: the layer's token path is
+ * init-routing (expand and sort by expert), the grouped expert GEMMs, and
+ * finalize-routing (un-permute, weighted sum, plus the shared-expert output).
  *   x        [T, H] act
  *   out      [T, H] act  OUT
  *   topk_idx [T, k] int32 OUT or NULL;  topk_w [T, k] fp32 OUT or NULL;
@@ -269,8 +275,8 @@ moe_status moe_layer(const moe_shape* s, const moe_weights* w, const void* x, vo
  * work is ordered before anything enqueued later on `stream`, as with moe_layer; the
  * results are bit-identical to moe_layer's.  side == NULL or side == stream: same as
  * moe_layer.  The call creates two events and releases them before returning.  Both
- * streams must belong to the current device.  On an error return, work already
- * enqueued on `side` may still run and `stream` does not wait for it.                 */
+ * streams must belong to the current device.  An error return after the fork still
+ * joins: `stream` waits for whatever was enqueued on `side`.                            */
 moe_status moe_layer_overlap(const moe_shape* s, const moe_weights* w, const void* x,
                              void* out, int32_t* topk_idx, float* topk_w, float* logits,
                              void* ws, size_t ws_bytes, hipStream_t stream, hipStream_t side);

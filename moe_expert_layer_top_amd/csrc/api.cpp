@@ -13,6 +13,7 @@
 #include <cstdint>
 
 #include "../../include/moe.h"
+#include "addr.h"
 #include "kernels.h"
 
 namespace {
@@ -225,8 +226,7 @@ int down_tiles_per_wg(moe::GemmCfg cfg, bool fp8, long long units, int N, int bn
 // 32-bit row offsets: T * H * bytes per element must stay below 4 GiB.
 bool gather_rows(const moe_shape* s) {
   if (s->act != MOE_BF16 || s->wt == MOE_INT4) return false;
-  const long long eb = s->wt == MOE_BF16 ? 2 : 1;
-  return eb * s->T * s->H < (1LL << 32);
+  return moe::lane_offsets_fit_u32(s->wt == MOE_BF16 ? 2 : 1, s->T, s->H);
 }
 
 struct FfnLayout {
@@ -662,15 +662,16 @@ moe_status moe_gate_topk_ex(const moe_shape* s, const moe_router* router, const 
   if (st != MOE_OK) return st;
   moe::RouterArgs ra;
   if (!router_args(s, router, &ra)) return MOE_EINVAL;
-  if (s->T > 0 && (!x || !w_gate || !logits || !topk_idx || !topk_w)) return MOE_EINVAL;
+  if (s->T > 0 && (!x || !w_gate || !topk_idx || !topk_w)) return MOE_EINVAL;
   if (!ws) return MOE_EINVAL;
   const size_t need = moe_workspace_bytes(s);
   if (need == 0) return MOE_EINVAL;
   if (ws_bytes < need) return MOE_EWORKSPACE;
   if (s->T == 0) return MOE_OK;
   const Layout L = layer_layout(s);
-  return run_gate_topk(s, x, w_gate, bias, logits, topk_idx, topk_w, at<float>(ws, L.part), stream,
-                       Prof(), ra);
+  // without a caller buffer the logits go to the workspace (as in moe_layer)
+  return run_gate_topk(s, x, w_gate, bias, logits ? logits : at<float>(ws, L.logits), topk_idx, topk_w,
+                       at<float>(ws, L.part), stream, Prof(), ra);
 }
 
 static moe_status init_routing_impl(const moe_shape* s, const void* x, const int32_t* ids,
@@ -763,8 +764,7 @@ moe_status moe_grouped_ffn_gathered(const moe_shape* s, int32_t G, int32_t R_max
   if (G < 1 || R_max < 0 || a_rows < 0 || row_div < 1) return MOE_EINVAL;
   if (s->act == MOE_F32) return MOE_EUNSUPPORTED;   // the fp32 kernels read rows in order
   const bool fp8 = s->wt == MOE_FP8_E4M3, scaled = fp8 || q8_weights(s);
-  const long long eb = (fp8 || q8_weights(s)) ? 1 : 2;
-  if (eb * a_rows * s->H >= (1LL << 32)) return MOE_EUNSUPPORTED;
+  if (!moe::lane_offsets_fit_u32((fp8 || q8_weights(s)) ? 1 : 2, a_rows, s->H)) return MOE_EUNSUPPORTED;
   if (!group_offsets || !ws) return MOE_EINVAL;
   if (R_max > 0 && (!a || !row_of || !w13 || !w2 || !y)) return MOE_EINVAL;
   if (scaled && R_max > 0 && (!a_scale || !w13_scale || !w2_scale)) return MOE_EINVAL;
@@ -825,10 +825,22 @@ moe_status moe_layer_profiled(const moe_shape* s, const moe_weights* w, const vo
 
 // Fork/join of the shared expert onto a second stream: two events, created for this call
 // and released once enqueued (a recorded event that streams still wait on is freed by the
-// runtime when it completes).
+// runtime when it completes).  Once `side` waits on the fork, the join is owed: a return
+// that leaves before the layer's own join (an error in any later launch) still records the
+// join on `side` and makes `stream` wait for it, so the side work never outlives the call's
+// ordering on `stream` (and a capture in progress keeps both streams joined).
 struct SideFork {
   hipEvent_t fork = nullptr, join = nullptr;
+  hipStream_t stream = nullptr, side = nullptr;
+  bool owed = false;
+  hipError_t rejoin() {
+    owed = false;
+    hipError_t e = hipEventRecord(join, side);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, join, 0);
+    return e;
+  }
   ~SideFork() {
+    if (owed) (void)rejoin();
     if (fork) (void)hipEventDestroy(fork);
     if (join) (void)hipEventDestroy(join);
   }
@@ -891,17 +903,19 @@ static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const voi
   const moe_shape sh = shared_shape(s);
   SideFork sf;
   if (forked) {
+    sf.stream = stream;
+    sf.side = side;
     if (hipEventCreateWithFlags(&sf.fork, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&sf.join, hipEventDisableTiming) != hipSuccess ||
         hipEventRecord(sf.fork, stream) != hipSuccess ||
         hipStreamWaitEvent(side, sf.fork, 0) != hipSuccess)
       return MOE_EHIP;
+    sf.owed = true;
     if (q8 && moe::launch_quant_rows_i8(x, s->T, s->H, 1, nullptr, nullptr, at<int8_t>(ws, L.sh_xq),
                                         at<float>(ws, L.sh_xs), side) != hipSuccess)
       return MOE_EHIP;
     st = run_ffn(&sh, 1, s->T, s->I_shared, sio, at<void>(ws, L.sh_ffn), side);
     if (st != MOE_OK) return st;
-    if (hipEventRecord(sf.join, side) != hipSuccess) return MOE_EHIP;
   }
   // gate + router  ([MND §Expert Parallelism], [MND §MoE Router])
   st = run_gate_topk(s, x, w->w_gate, w->bias, lg, idx, tw, at<float>(ws, L.part), stream, prof, ra);
@@ -931,7 +945,7 @@ static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const voi
                MOE_EV_FFN2, merged ? &sio : nullptr, merged ? s->T : 0);
   if (st != MOE_OK) return st;
   if (forked) {
-    if (hipStreamWaitEvent(stream, sf.join, 0) != hipSuccess) return MOE_EHIP;
+    if (sf.rejoin() != hipSuccess) return MOE_EHIP;
   } else if (!merged) {
     st = run_ffn(&sh, 1, s->T, s->I_shared, sio, at<void>(ws, L.sh_ffn), stream);
     if (st != MOE_OK) return st;

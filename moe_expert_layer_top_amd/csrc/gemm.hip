@@ -32,6 +32,7 @@
 
 #include <type_traits>
 
+#include "addr.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -301,12 +302,12 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
       sc_base = p.b_scale + static_cast<long long>(un.group) * p.b_scale_group + kb0;
       sc_off = static_cast<uint32_t>(static_cast<long long>(blk) * p.b_scale_ld * 4);
     }
-    // one base per wavefront (the DMA takes it in scalar registers); each 32-bit half is
-    // widened as unsigned, so the low half's top bit never sign-extends into the high half
+    // one base per wavefront (the DMA takes it in scalar registers), rebuilt from its two
+    // wave-uniform 32-bit halves
     const uint64_t sb = reinterpret_cast<uint64_t>(sc_base);
-    const uint32_t sb_lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(sb)));
-    const uint32_t sb_hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(sb >> 32)));
-    sc_base = reinterpret_cast<const float*>((static_cast<uint64_t>(sb_hi) << 32) | sb_lo);
+    sc_base = reinterpret_cast<const float*>(
+        join_u32_halves(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(sb)),
+                        __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(sb >> 32))));
   }
   if constexpr (FP8) {
 #pragma unroll

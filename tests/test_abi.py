@@ -105,14 +105,29 @@ def test_validation_errors_enqueue_nothing(L):
     assert L.moe_grouped_ffn_gathered(ctypes.byref(s), 8, 32, DUMMY, 64, None, None, 1, *rest) == M.MOE_EINVAL
     f32 = M.shape(16, 256, 8, 2, 128, 128, "f32", "f32")
     assert L.moe_grouped_ffn_gathered(ctypes.byref(f32), *gat, 1, *rest) == M.MOE_EUNSUPPORTED
+    # the 32-bit lane offsets of `a`: these calls pass a 16-byte workspace, so a call that
+    # got past the bound check would stop at the workspace check (MOE_EWORKSPACE) and
+    # never launch on the dummy pointers
+    tiny = [DUMMY, DUMMY, None, DUMMY, None, DUMMY, DUMMY, 16, None]
     wide = M.shape(16, 8192, 8, 2, 128, 128)
     assert L.moe_grouped_ffn_gathered(ctypes.byref(wide), 8, 32, DUMMY, 1 << 18, None, DUMMY, 1,
-                                      *rest) == M.MOE_EUNSUPPORTED   # 2^18 rows x 16 KB = 4 GiB
+                                      *tiny) == M.MOE_EUNSUPPORTED   # 2^18 rows x 16 KB = 4 GiB
     # int8 codes are one byte: the same limit falls at twice the rows
     wide8 = M.shape(16, 8192, 8, 2, 128, 128, "bf16", "int8")
-    sc = [DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 1 << 30, None]
+    sc = [DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 16, None]
     assert L.moe_grouped_ffn_gathered(ctypes.byref(wide8), 8, 32, DUMMY, 1 << 19, DUMMY, DUMMY, 1,
                                       *sc) == M.MOE_EUNSUPPORTED
+    # exactly at the limit (H = 128): 2^32 bytes of `a` is refused, 128 bytes fewer is not
+    narrow8 = M.shape(16, 128, 8, 2, 128, 128, "bf16", "int8")
+    assert L.moe_grouped_ffn_gathered(ctypes.byref(narrow8), 8, 32, DUMMY, 1 << 25, DUMMY, DUMMY, 1,
+                                      *sc) == M.MOE_EUNSUPPORTED
+    assert L.moe_grouped_ffn_gathered(ctypes.byref(narrow8), 8, 32, DUMMY, (1 << 25) - 1, DUMMY, DUMMY, 1,
+                                      *sc) == M.MOE_EWORKSPACE
+    narrow = M.shape(16, 128, 8, 2, 128, 128)
+    assert L.moe_grouped_ffn_gathered(ctypes.byref(narrow), 8, 32, DUMMY, 1 << 24, None, DUMMY, 1,
+                                      *tiny) == M.MOE_EUNSUPPORTED
+    assert L.moe_grouped_ffn_gathered(ctypes.byref(narrow), 8, 32, DUMMY, (1 << 24) - 1, None, DUMMY, 1,
+                                      *tiny) == M.MOE_EWORKSPACE
     assert L.moe_grouped_ffn_gathered(ctypes.byref(fp8), 8, 32, DUMMY, 64, None, DUMMY, 1, DUMMY, DUMMY,
                                       None, DUMMY, None, DUMMY, DUMMY, 1 << 30, None) == M.MOE_EINVAL
     w = M.moe_weights()
@@ -180,3 +195,18 @@ def test_layer_plan_query(L):
     bad = M.shape(8, 100, 16, 2, 128, 128, "bf16", "bf16")   # H not a multiple of 128
     with pytest.raises(M.MoEError):
         M.moe_layer_plan_of(bad)
+
+
+def test_address_helpers_on_the_cpu(tmp_path):
+    """The 64-bit base rebuilt from two 32-bit halves (the fp8 scale loads of the grouped
+    GEMM) and the 32-bit lane-offset bound, compiled from the kernels' own header by the
+    host compiler and checked on the CPU: a low half with bit 31 set must not spill into
+    the high half, and the bound must fall exactly at 2^32 bytes."""
+    exe = tmp_path / "addr_check"
+    src = os.path.join(ROOT, "tests", "csrc", "addr_check.cpp")
+    inc = os.path.join(ROOT, "moe_expert_layer_top_amd", "csrc")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-Werror", "-I", inc, src, "-o", str(exe)],
+                   check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "all address checks passed" in r.stdout
