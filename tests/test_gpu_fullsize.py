@@ -1,12 +1,23 @@
 """GPU parity at the full workload sizes, in the launch configuration the bench times.
 
-The whole layer runs on the GPU at full size; the oracle then recomputes a sample
-of tokens one by one (every step of the layer is separable per token, so the
-sample's outputs equal the full layer's outputs for those tokens).  Routing
-integers (top-k ids, counts, offsets, both permutations) are compared bit for
-bit at full size, and the expanded rows of the sampled tokens byte for byte.
+The whole layer runs on the GPU at full size; the oracle then recomputes a sample of
+tokens (every step of the layer is separable per token, so the sample's outputs equal
+the full layer's outputs for those tokens).  Routing integers (top-k ids, counts,
+offsets, both permutations) are compared bit for bit at full size, and the expanded
+rows of the sampled tokens byte for byte.
+
+The sample reaches every active expert: it holds the tokens of the first and the last
+row of every work unit the grouped GEMMs cut each expert's rows into (a prefill expert
+of up to one tile of rows is one unit; a hot expert is several), the first and last
+token of every row slice of the shared expert, and the first and last token.  Decode
+batches (at most 128 tokens) are checked on every token.  The oracle computes the
+sample expert by expert: each expert's weights are drawn and converted to float64 on a
+thread pool a few experts ahead of the grouped FFN that consumes them, so host memory
+holds a bounded number of experts at a time.
 """
 import dataclasses
+from collections import deque
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -14,12 +25,13 @@ import torch
 
 from oracle import moe as O
 from synth import configs, inputs
-from synth.device import to_dev, upload_layer
-from tests.gpu_helpers import act_to_f64, empty_act, host, max_row_rel_err, say, tol_of
+from synth.device import upload_layer
+from tests.gpu_helpers import act_to_f64, check_close, empty_act, host, say, tol_of
 
-pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
-N_SAMPLE = 6
+ALL_TOKENS_UP_TO = 128       # batches this small are checked on every token
+WORKERS = 16                 # host threads drawing / converting expert weights
 
 
 @pytest.fixture(scope="module")
@@ -31,34 +43,122 @@ def M():
     return m
 
 
-def sample_tokens(T, seed):
-    rng = np.random.default_rng(seed)
-    ends = {0, T - 1}
-    picks = ends | set(rng.choice(T, size=max(0, min(T, N_SAMPLE) - len(ends)), replace=False).tolist())
+def unit_bounds(offsets, bm):
+    """First and last sorted row of every work unit of the grouped GEMM: an expert of n
+    rows is cut into ceil(n / bm) near-equal slices of a multiple of 16 rows."""
+    rows = []
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        n = hi - lo
+        if n == 0:
+            continue
+        nu = -(-n // bm)
+        per = (-(-n // nu) + 15) & ~15
+        for i in range(nu):
+            r0 = lo + i * per
+            if r0 >= hi:
+                break
+            rows += [r0, min(r0 + per, hi) - 1]
+    return rows
+
+
+def slice_bounds(T, bm):
+    """First and last row of each of the near-equal row slices of a dense T-row GEMM."""
+    nx = -(-T // bm)
+    per = (-(-T // nx) + 15) & ~15
+    out = []
+    for i in range(nx):
+        r0 = i * per
+        if r0 < T:
+            out += [r0, min(r0 + per, T) - 1]
+    return out
+
+
+def sample_tokens(cfg, rt, block_m, shared_block_m):
+    """Tokens whose rows cover every unit's first and last row (hence every active
+    expert), every shared-expert slice's first and last token, and tokens 0 and T-1."""
+    T, k = cfg.T, cfg.k
+    if T <= ALL_TOKENS_UP_TO:
+        return np.arange(T)
+    rows = unit_bounds(rt["expert_offsets"], block_m)
+    picks = {0, T - 1}
+    picks |= {int(rt["sorted_src"][r]) // k for r in rows}
+    picks |= set(slice_bounds(T, shared_block_m))
     return np.array(sorted(picks))
 
 
-def expert_dict(cfg, experts):
-    w13, w2, s13, s2 = {}, {}, {}, {}
-    for e, v in inputs.for_each_expert(cfg, inputs.expert_w13, experts):
-        if cfg.wt in ("fp8", "int8", "int4"):
-            w13[e], s13[e] = v
-        else:
-            w13[e] = v
-    for e, v in inputs.for_each_expert(cfg, inputs.expert_w2, experts):
-        if cfg.wt in ("fp8", "int8", "int4"):
-            w2[e], s2[e] = v
-        else:
-            w2[e] = v
-    d = {"w13": w13, "w2": w2}
+def block_rows(M, cfg):
+    """Rows per unit of the routed expert GEMMs and of the shared expert's GEMMs, from the
+    library's own launch plan (the shared expert alone is a one-group FFN over T rows)."""
+    p = M.moe_layer_plan_of(M.shape_of(cfg))
+    if p["shared_merged"]:
+        return p["block_m"], p["block_m"]
+    sh = M.moe_layer_plan_of(M.shape(cfg.T, cfg.H, 1, 1, cfg.I_shared, cfg.I_shared, cfg.act, cfg.sh_wt))
+    return p["block_m"], sh["block_m"]
+
+
+def weights_one(cfg, e):
+    """Expert e's weights as the oracle's per-expert float64 (w13, w2)."""
+    w13 = inputs.expert_w13(cfg, e)
+    w2 = inputs.expert_w2(cfg, e)
+    d = {"cfg": cfg}
     if cfg.wt in ("fp8", "int8", "int4"):
-        d.update(w13_scale=s13, w2_scale=s2)
-    return d
+        d.update(w13={e: w13[0]}, w13_scale={e: w13[1]}, w2={e: w2[0]}, w2_scale={e: w2[1]})
+    else:
+        d.update(w13={e: w13}, w2={e: w2})
+    return O.expert_weights_f64(d)(e)
 
 
-@pytest.mark.parametrize("name", ["c1_tiny_fp32", "c2_prefill_bf16", "c4_decode_bf16", "c5_skewed_fp8",
-                                  "c6_prefill_w8a8", "c7_decode_w8a8", "c8_decode_w4a8",
-                                  "c9_decode1_bf16", "c10_decode_fp8"])
+class ExpertStream:
+    """e -> float64 (w13, w2) for the oracle's grouped FFN, which asks for the non-empty
+    experts in increasing order: each is drawn and converted on a thread pool, at most
+    `ahead` experts in advance."""
+
+    def __init__(self, cfg, experts, ahead=WORKERS):
+        self.cfg = cfg
+        self.order = list(experts)
+        self.pool = ThreadPoolExecutor(WORKERS)
+        self.pending = deque()
+        self.next = 0
+        for _ in range(ahead):
+            self._submit()
+
+    def _submit(self):
+        if self.next < len(self.order):
+            e = self.order[self.next]
+            self.pending.append((e, self.pool.submit(weights_one, self.cfg, e)))
+            self.next += 1
+
+    def __call__(self, e):
+        want, fut = self.pending.popleft()
+        assert want == e, (want, e)
+        self._submit()
+        return fut.result()
+
+    def close(self):
+        self.pool.shutdown(wait=True)
+
+
+def oracle_on_sample(cfg, S, logits_s, bias):
+    """The oracle layer on tokens S, routed on the given float32 logits of those tokens."""
+    idx, _ = O.route_topk(logits_s, bias, cfg.k)
+    experts = sorted(set(idx.reshape(-1).tolist()))
+    d = {"cfg": dataclasses.replace(cfg, T=len(S)), "x": inputs.tokens(cfg)[S], "w_gate": inputs.gate_weight(cfg),
+         "bias": bias, **inputs.shared_weights(cfg)}
+    stream = ExpertStream(cfg, experts)
+    try:
+        ref = O.moe_layer(d, logits32_override=logits_s, expert_weights=stream)
+    finally:
+        stream.close()
+    assert not stream.pending and stream.next == len(experts)    # every expert drawn once
+    return ref, experts
+
+
+FULL = ["c1_tiny_fp32", "c2_prefill_bf16", "c4_decode_bf16", "c5_skewed_fp8", "c6_prefill_w8a8",
+        "c7_decode_w8a8", "c8_decode_w4a8", "c9_decode1_bf16", "c10_decode_fp8"]
+
+
+@pytest.mark.parametrize("name", FULL)
 def test_full_layer_sampled(M, name):
     cfg = configs.get(name)
     say("full layer", name, "upload")
@@ -100,9 +200,12 @@ def test_full_layer_sampled(M, name):
     assert np.array_equal(host(eri), rt["expanded_row_idx"])
     assert np.array_equal(host(ssrc), rt["sorted_src"])
     # sampled tokens through the oracle
-    S = sample_tokens(T, cfg.cid)
-    x_all = inputs.tokens(cfg)
-    xs = x_all[S]
+    bm, bm_sh = block_rows(M, cfg)
+    S = sample_tokens(cfg, rt, bm or 64, bm_sh or 64)
+    active = np.nonzero(rt["tokens_per_expert"])[0]
+    covered = set(i_gpu[S].reshape(-1).tolist())
+    assert covered >= set(active.tolist())            # every active expert has a checked row
+    xs = inputs.tokens(cfg)[S]
     rows = rt["expanded_row_idx"].reshape(T, k)[S].reshape(-1)
     if fp8:
         q, sc = O.quant_1x128(O.to_f64(xs, cfg.act).astype(np.float32))
@@ -117,25 +220,24 @@ def test_full_layer_sampled(M, name):
         if cfg.act == "bf16":
             got = got.view(np.uint16)
         assert np.array_equal(got, np.repeat(xs, k, axis=0))
-    experts = sorted(set(i_gpu[S].reshape(-1).tolist()))
-    say("full layer", name, f"oracle on tokens {S.tolist()} ({len(experts)} experts)")
-    d = {"cfg": dataclasses.replace(cfg, T=len(S)), "x": xs, "w_gate": inputs.gate_weight(cfg),
-         "bias": bias, **inputs.shared_weights(cfg)}
-    d.update(expert_dict(cfg, experts))
-    ref = O.moe_layer(d, logits32_override=l_gpu[S])
-    err = max_row_rel_err(act_to_f64(out, cfg.act)[S], ref["out"])
-    say("full layer", name, f"max row rel err {err:.3e}")
-    assert err <= tol_of(cfg), err
+    del ex, exs
+    say("full layer", name, f"oracle on {len(S)} of {T} tokens ({len(active)} active experts, "
+        f"{len(unit_bounds(rt['expert_offsets'], bm or 64)) // 2} units)")
+    ref, experts = oracle_on_sample(cfg, S, l_gpu[S], bias)
+    assert len(experts) == len(active)
+    check_close(f"full layer {name} ({len(S)} tokens)", act_to_f64(out, cfg.act)[S], ref["out"], tol_of(cfg))
     lerr = np.abs(l_gpu[S] - ref["logits"]).max(axis=1) / np.abs(ref["logits"]).max(axis=1)
     assert lerr.max() <= 1e-5
-    del g, ws, ex
+    del g, ws
     torch.cuda.empty_cache()
 
 
 def test_ep_rank_share_full(M):
     """One expert-parallel rank at ep=8: 8192 received rows tagged with experts 96..127,
     re-routed, run through the 32 local experts, un-sorted back to arrival order; plus
-    the shared expert on the 1024 local tokens."""
+    the shared expert on the 1024 local tokens.  Checked rows: the first and last row of
+    every unit of every local expert, and the first and last local token of every row
+    slice of the shared expert."""
     cfg = configs.get("c3_ep_rank_bf16")
     say("ep share full upload")
     g = upload_layer(cfg)
@@ -171,20 +273,25 @@ def test_ep_rank_share_full(M):
     assert np.array_equal(host(ssrc), rt["sorted_src"])
     # un-sort is exact: arrival row a is sorted row expanded_row_idx[a]
     assert np.array_equal(host(y_arr), host(y)[rt["expanded_row_idx"]])
-    S = sample_tokens(R, cfg.cid)
+    bm = M.moe_layer_plan_of(M.shape(R, H, E, 1, cfg.I, cfg.I, cfg.act, cfg.wt))["block_m"]
+    sorted_rows = unit_bounds(rt["expert_offsets"], bm)
+    S = np.array(sorted({int(rt["sorted_src"][r]) for r in sorted_rows} | {0, R - 1}))
+    assert set((ids[S, 0] - cfg.e_base).tolist()) == set(range(E))    # every local expert
     x = inputs.tokens(cfg)
-    experts = sorted(set((ids[S, 0] - cfg.e_base).tolist()))
-    wd = expert_dict(cfg, experts)
-    ref = np.stack([O.swiglu_ffn(O.to_f64(x[a:a + 1], cfg.act),
-                                 O.to_f64(wd["w13"][int(ids[a, 0]) - cfg.e_base], cfg.wt),
-                                 O.to_f64(wd["w2"][int(ids[a, 0]) - cfg.e_base], cfg.wt))[0] for a in S])
-    err = max_row_rel_err(act_to_f64(y_arr, cfg.act)[S], ref)
-    say("ep share full", f"routed max row rel err {err:.3e}")
-    assert err <= tol_of(cfg)
-    L = sample_tokens(cfg.T_local, cfg.cid + 1)
+    # the oracle's grouped FFN on the sampled arrival rows, routed by their own ids
+    sub_rt = O.init_routing(ids[S], E, cfg.e_base)
+    stream = ExpertStream(cfg, [e for e in range(E) if sub_rt["tokens_per_expert"][e] > 0])
+    try:
+        y_sorted = O.grouped_ffn(O.to_f64(x[S], cfg.act)[sub_rt["sorted_src"]], sub_rt["expert_offsets"], stream)
+    finally:
+        stream.close()
+    ref = O.finalize(y_sorted, sub_rt["expanded_row_idx"], 1)
+    say("ep share full", f"{len(S)} of {R} rows, {E} experts")
+    check_close(f"ep rank share full routed ({len(S)} rows)", act_to_f64(y_arr, cfg.act)[S], ref, tol_of(cfg))
+    L = np.array(sorted(set(slice_bounds(cfg.T_local, bm))))
     xl = inputs.local_tokens(cfg)[L]
     sref = O.swiglu_ffn(O.to_f64(xl, cfg.act), O.to_f64(inputs.shared_w13(cfg), cfg.act),
                         O.to_f64(inputs.shared_w2(cfg), cfg.act))
-    assert max_row_rel_err(act_to_f64(sh, cfg.act)[L], sref) <= tol_of(cfg)
+    check_close(f"ep rank share full shared ({len(L)} tokens)", act_to_f64(sh, cfg.act)[L], sref, tol_of(cfg))
     del g, ws, wsf
     torch.cuda.empty_cache()

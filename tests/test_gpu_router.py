@@ -8,7 +8,7 @@ import torch
 
 from oracle import moe as O
 from synth import configs
-from tests.gpu_helpers import act_to_f64, empty_act, host, max_row_rel_err, poison_, say, tol_of
+from tests.gpu_helpers import act_to_f64, check_close, empty_act, host, poison_, say, tol_of
 from tests.test_gpu_parity import case, ws_for
 
 pytestmark = pytest.mark.gpu
@@ -100,11 +100,10 @@ def test_layer_router(M, name, rname):
     torch.cuda.synchronize()
     ref = O.moe_layer(d, logits32_override=host(logits), router=r)
     assert np.array_equal(host(idx), ref["topk_idx"])
-    err = max_row_rel_err(act_to_f64(out, cfg.act), ref["out"])
-    say(f"  max row rel err {err:.3e}")
     # the combine's weights sum to `scale` instead of 1: the tolerance is relative to the
     # output rows, which scale with it
-    assert err <= tol_of(cfg), err
+    check_close(f"router layer {cfg.name} {sorted(r.items())}", act_to_f64(out, cfg.act), ref["out"],
+                tol_of(cfg))
 
 
 def test_layer_ex_default_router_is_moe_layer(M):
