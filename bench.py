@@ -372,89 +372,155 @@ def blas_threads() -> int:
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(cfg, target_s=15.0, max_tokens=None):
-    """Time the oracle (as it stands) on the first T_s tokens of the workload.
+def _expert_f64(cfg, e):
+    """Expert e's float64 (w13, w2) through the oracle's own per-expert adapter."""
+    from oracle import moe as O
+    from synth import inputs
+    w13, w2 = inputs.expert_w13(cfg, e), inputs.expert_w2(cfg, e)
+    d = {"cfg": cfg}
+    if cfg.wt in ("fp8", "int8", "int4"):
+        d.update(w13={e: w13[0]}, w13_scale={e: w13[1]}, w2={e: w2[0]}, w2_scale={e: w2[1]})
+    else:
+        d.update(w13={e: w13}, w2={e: w2})
+    return O.expert_weights_f64(d)(e)
 
-    Inputs of the sample -- the tokens, the gate, and the weights of the experts
-    the sample routes to -- are drawn first and not timed, like the GPU side."""
-    import dataclasses
 
+def _ffn_sample(cfg, offsets, a_rows_of, target_s):
+    """Time the oracle's grouped FFN on the whole row sets of the first m active experts
+    (the realized rows per expert of the full routing), m grown until the timed part
+    takes about target_s; each expert's float64 weights are made beforehand (resident
+    weights, as on the GPU).  Returns (seconds, rows timed, experts timed)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import moe as O
+    n = np.diff(offsets)
+    active = [int(e) for e in np.nonzero(n)[0]]
+    m = min(4, len(active))
+    while True:
+        chosen = active[:m]
+        with ThreadPoolExecutor(16) as ex:
+            wts = dict(zip(chosen, ex.map(lambda e: _expert_f64(cfg, e), chosen)))
+        rows = np.concatenate([np.arange(offsets[e], offsets[e + 1]) for e in chosen])
+        a = a_rows_of(rows)
+        sub_offs = np.concatenate([[0], np.cumsum([n[e] for e in chosen])])
+        t0 = time.perf_counter()
+        O.grouped_ffn(a, sub_offs, lambda j: wts[chosen[j]],
+                      quant_h="int8" if cfg.wt in ("int8", "int4") else cfg.wt == "fp8")
+        dt = time.perf_counter() - t0
+        if dt >= 0.5 * target_s or m == len(active):
+            return dt, int(rows.size), m
+        m = min(len(active), max(m + 1, int(m * min(4.0, target_s / max(dt, 1e-3)))))
+        del wts, a
+
+
+def cpu_baseline(cfg, target_s=15.0):
+    """Time the oracle (as it stands) stage by stage on a bounded sample of the workload
+    and scale each stage to the full layer: the gate projection, the router, the
+    routing sort and the row expansion over all T tokens; the grouped SwiGLU experts on
+    the whole row sets of m experts (scaled by rows); the shared expert and the combine
+    on a sample of tokens (scaled by tokens).  Weights are converted to float64 before
+    the timers start, as the GPU's are resident in HBM."""
     from oracle import moe as O
     from synth import inputs
 
-    x_all = inputs.tokens(cfg)
     if cfg.pretagged:
-        return cpu_baseline_ep(cfg, x_all, target_s)
-    wg = inputs.gate_weight(cfg)
+        return cpu_baseline_ep(cfg, target_s)
+    T, k = cfg.T, cfg.k
+    x_all = inputs.tokens(cfg)
+    wg64 = O.to_f64(inputs.gate_weight(cfg), cfg.act)
     bias = inputs.expert_bias(cfg)
+    fp8 = cfg.wt == "fp8"
+    q8 = cfg.wt in ("int8", "int4")
+    stages = {}
+    t0 = time.perf_counter()
+    x64 = O.to_f64(x_all, cfg.act)
+    l32 = O.gate_logits(x64, wg64).astype(np.float32)
+    stages["gate"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    idx, w = O.route_topk(l32, bias, k)
+    rt = O.init_routing(idx, cfg.E)
+    stages["router+sort"] = time.perf_counter() - t0
+    # the expert inputs of every row: the tokens themselves, or their fp8 / int8 codes
+    t0 = time.perf_counter()
+    if fp8:
+        q, sc = O.quant_1x128(x64.astype(np.float32))
+        a_rows_of = lambda r: O.dequant_1x128(O.expand_rows(q, rt["sorted_src"][r], k),   # noqa: E731
+                                              O.expand_rows(sc, rt["sorted_src"][r], k))
+    elif q8:
+        q, sc = O.quant_per_token_int8(x64.astype(np.float32))
+        a_rows_of = lambda r: O.dequant_rows(O.expand_rows(q, rt["sorted_src"][r], k),    # noqa: E731
+                                             O.expand_rows(sc[:, None], rt["sorted_src"][r], k)[:, 0])
+    else:
+        a_rows_of = lambda r: O.expand_rows(x64, rt["sorted_src"][r], k)                 # noqa: E731
+    stages["quant"] = time.perf_counter() - t0
+    R = int(rt["expert_offsets"][-1])
+    t_ffn, rows_s, m = _ffn_sample(cfg, rt["expert_offsets"], a_rows_of, target_s * 0.6)
+    stages["experts (scaled)"] = t_ffn * R / rows_s
+    # expansion of every row (a gather of R rows), timed on the sampled experts' rows
+    t0 = time.perf_counter()
+    a_rows_of(np.arange(min(R, rows_s)))
+    stages["expand (scaled)"] = (time.perf_counter() - t0) * R / min(R, rows_s)
+    # shared expert and combine on a token sample
+    inp = {"cfg": cfg, **inputs.shared_weights(cfg)}
+    shw = O.shared_weights_f64(inp)
+    ts = min(T, max(64, rows_s // k))
+    t0 = time.perf_counter()
+    sh = O.shared_expert(x64[:ts], inp, shw)
+    stages["shared (scaled)"] = (time.perf_counter() - t0) * T / ts
+    y = np.zeros((ts * k, cfg.H))
+    eri = np.arange(ts * k, dtype=np.int32)
+    t0 = time.perf_counter()
+    O.finalize(y, eri, k, w[:ts], sh)
+    stages["combine (scaled)"] = (time.perf_counter() - t0) * T / ts
+    total = sum(stages.values())
+    return {"value": T / total, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "seconds_per_layer": total,
+            "stages_s": {kk: round(v, 3) for kk, v in stages.items()},
+            "sample": f"float64 oracle on {cfg.name}: gate, router, routing sort and activation "
+                      f"quantization over all {T} tokens; the grouped experts on the whole row sets of "
+                      f"{m} experts ({rows_s} of {R} rows, scaled by rows); shared expert and combine on "
+                      f"{ts} tokens (scaled by tokens); weights in float64 before timing"}
 
-    def prepare(ts):
-        sub = dataclasses.replace(cfg, T=ts)
-        d = {"cfg": sub, "x": x_all[:ts], "w_gate": wg, "bias": bias, **inputs.shared_weights(cfg)}
-        xl = O.to_f64(d["x"], cfg.act)
-        idx, _ = O.route_topk(O.gate_logits(xl, O.to_f64(wg, cfg.act)).astype(np.float32), bias, cfg.k)
-        experts = sorted(set(idx.reshape(-1).tolist()))
-        w13, w2, w13s, w2s = {}, {}, {}, {}
-        for e, v in inputs.for_each_expert(cfg, inputs.expert_w13, experts):
-            if cfg.wt in ("fp8", "int8", "int4"):
-                w13[e], w13s[e] = v
-            else:
-                w13[e] = v
-        for e, v in inputs.for_each_expert(cfg, inputs.expert_w2, experts):
-            if cfg.wt in ("fp8", "int8", "int4"):
-                w2[e], w2s[e] = v
-            else:
-                w2[e] = v
-        d.update(w13=w13, w2=w2)
-        if cfg.wt in ("fp8", "int8", "int4"):
-            d.update(w13_scale=w13s, w2_scale=w2s)
-        return d
 
-    ts = 2
-    while True:
-        d = prepare(ts)
-        t0 = time.perf_counter()
-        O.moe_layer(d)
-        dt = time.perf_counter() - t0
-        if dt >= target_s * 0.5 or ts >= (max_tokens or cfg.T):
-            break
-        ts = min(max_tokens or cfg.T, max(ts + 1, int(ts * min(8.0, target_s / max(dt, 1e-3)))))
-    return {"value": ts / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
-            "sample": f"first {ts} of the {cfg.T} tokens of {cfg.name} through the float64 oracle "
-                      f"(gate, top-k, routing, grouped SwiGLU experts, shared expert, combine); "
-                      f"{dt:.1f} s"}
-
-
-def cpu_baseline_ep(cfg, x_all, target_s):
-    """The oracle on the first rows of a rank share: rows[:ts] with their ids, and the
-    same fraction of the local tokens for the shared expert; local tokens per second."""
-    import dataclasses
-
+def cpu_baseline_ep(cfg, target_s):
+    """The oracle on a rank share, stage by stage: the re-routing sort over all received
+    rows; the grouped experts on the whole row sets of m local experts (scaled by rows);
+    the un-sort and the shared expert on samples (scaled); local tokens per second."""
     from oracle import moe as O
     from synth import inputs
 
-    ids_all = inputs.pretagged_ids(cfg)
+    ids = inputs.pretagged_ids(cfg)
+    x_all = inputs.tokens(cfg)
     xl_all = inputs.local_tokens(cfg)
-    ts = 8
-    while True:
-        tl = max(1, ts * cfg.T_local // cfg.T)
-        ids = ids_all[:ts]
-        experts = sorted(set((ids[:, 0] - cfg.e_base).tolist()))
-        d = {"cfg": dataclasses.replace(cfg, T=ts, T_local=tl), "x": x_all[:ts], "ids": ids,
-             "x_local": xl_all[:tl], "bias": None,
-             **inputs.shared_weights(cfg),
-             "w13": dict(inputs.for_each_expert(cfg, inputs.expert_w13, experts)),
-             "w2": dict(inputs.for_each_expert(cfg, inputs.expert_w2, experts))}
-        t0 = time.perf_counter()
-        O.moe_layer(d)
-        dt = time.perf_counter() - t0
-        if dt >= target_s * 0.5 or ts >= cfg.T:
-            break
-        ts = min(cfg.T, max(ts + 8, int(ts * min(8.0, target_s / max(dt, 1e-3)))))
-    return {"value": tl / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
-            "sample": f"first {ts} of the {cfg.T} received rows of {cfg.name} with {tl} of its "
-                      f"{cfg.T_local} local tokens through the float64 oracle (re-routing, grouped "
-                      f"experts, un-sort, shared expert); {dt:.1f} s"}
+    stages = {}
+    t0 = time.perf_counter()
+    rt = O.init_routing(ids, cfg.E, cfg.e_base)
+    stages["re-route"] = time.perf_counter() - t0
+    R = int(rt["expert_offsets"][-1])
+
+    def a_rows_of(r):
+        src = rt["sorted_src"][r]
+        return O.to_f64(x_all[src], cfg.act)
+    t_ffn, rows_s, m = _ffn_sample(cfg, rt["expert_offsets"], a_rows_of, target_s * 0.6)
+    stages["experts (scaled)"] = t_ffn * R / rows_s
+    y = np.zeros((rows_s, cfg.H))
+    t0 = time.perf_counter()
+    O.unsort(y, np.random.default_rng(0).permutation(rows_s))
+    stages["un-sort (scaled)"] = (time.perf_counter() - t0) * R / rows_s
+    inp = {"cfg": cfg, **inputs.shared_weights(cfg)}
+    shw = O.shared_weights_f64(inp)
+    tl = min(cfg.T_local, max(64, rows_s // 8))
+    t0 = time.perf_counter()
+    O.shared_expert(O.to_f64(xl_all[:tl], cfg.act), inp, shw)
+    stages["shared (scaled)"] = (time.perf_counter() - t0) * cfg.T_local / tl
+    total = sum(stages.values())
+    return {"value": cfg.T_local / total, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "seconds_per_layer": total,
+            "stages_s": {kk: round(v, 3) for kk, v in stages.items()},
+            "sample": f"float64 oracle on {cfg.name}: re-routing sort over all {cfg.T} received rows; the "
+                      f"grouped experts on the whole row sets of {m} of the {cfg.E} local experts "
+                      f"({rows_s} of {R} rows, scaled by rows); un-sort and shared expert on samples "
+                      f"(scaled); weights in float64 before timing"}
 
 
 def copy_calibration(nbytes=1 << 30, reps=3):
@@ -472,12 +538,19 @@ def copy_calibration(nbytes=1 << 30, reps=3):
 
 # ----------------------------------------------------------------------------- main
 
-def main():
+DEFAULT_ALSO = "c5_skewed_fp8,c3_ep_rank_bf16,c4_decode_bf16"
+
+
+def parse_args(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c2_prefill_bf16")
+    ap.add_argument("--also", default=None,
+                    help="comma-separated workloads timed after the main one in the same run and "
+                         f"reported under 'other_workloads' (default with the c2 layer: {DEFAULT_ALSO}; "
+                         "'none' for none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--flush", action="store_true",
@@ -486,7 +559,11 @@ def main():
                     help="run the shared expert's own launches on the layer's stream")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (scales the HBM byte counters)")
-    args = ap.parse_args()
+    return ap.parse_args(argv)
+
+
+def main():
+    args = parse_args()
     if args.copy_calibration:
         copy_calibration()
         return
@@ -497,11 +574,45 @@ def main():
 
     from synth import configs
     cfg = configs.get(args.config)
-    if cfg.pretagged:
-        main_ep(cfg, args)
-        return
-    r = run_gpu(cfg, args.steps, args.warmup, two_streams=not args.one_stream, flush=args.flush)
-    ms = r["total_ms"] / args.steps
+    line = ep_line(cfg, args.steps, args.warmup) if cfg.pretagged else layer_line(cfg, args)
+    also = args.also if args.also is not None else (DEFAULT_ALSO if args.config == "c2_prefill_bf16" else "none")
+    others = [n for n in also.split(",") if n and n != "none" and n != cfg.name]
+    if others:
+        import torch
+        line["other_workloads"] = {}
+        for name in others:
+            torch.cuda.empty_cache()
+            ocfg = configs.get(name)
+            steps, warm = min(args.steps, 10), min(args.warmup, 2)
+            o = ep_line(ocfg, steps, warm) if ocfg.pretagged else layer_line(ocfg, args, steps, warm)
+            line["other_workloads"][name] = summary_of(o)
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+def summary_of(line: dict) -> dict:
+    """The figures of a bench line that another workload's entry carries."""
+    roof = line["roofline"]
+    out = {"ms_per_step": line["ms_per_step"], "tokens_per_s": line["value"], "steps": line["steps"],
+           "dtype": line["dtype"], "config": line["config"],
+           "roofline": {k: roof[k] for k in ("kernel", "bound", "achieved", "peak", "unit", "frac", "traffic",
+                                              "mfma_frac")},
+           "ffn_mfma_frac": line["ffn_mfma_frac"], "permute_combine_hbm_frac": line["permute_combine_hbm_frac"],
+           "kernels_ms": {k: round(v["ms"], 4) for k, v in line["kernels"].items()}}
+    if "rows_per_s" in line:
+        out["rows_per_s"] = line["rows_per_s"]
+    return out
+
+
+def layer_line(cfg, args, steps=None, warmup=None) -> dict:
+    """Bench line (without the CPU baseline) of a gated layer workload."""
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
+    r = run_gpu(cfg, steps, warmup, two_streams=not args.one_stream, flush=args.flush)
+    ms = r["total_ms"] / steps
     tokens = cfg.shared_rows
     acc = launch_accounting(cfg, account(cfg, r["tpe"]))
     kern = {name: roofline_entry(acc[name], r["stage_ms"][name]) for name in acc}
@@ -540,8 +651,8 @@ def main():
         "value": tokens * 1e3 / ms,
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
@@ -557,22 +668,19 @@ def main():
         "shared_expert": shared_mode,
         "active_experts": int(np.count_nonzero(r["tpe"])),
         "max_rows_per_expert": int(r["tpe"].max()),
-        "wall_ms_per_step": r["wall_s"] * 1e3 / args.steps,
+        "wall_ms_per_step": r["wall_s"] * 1e3 / steps,
         "cold_ms_per_step": r["cold_ms"],
         "setup_s": r["setup_s"],
     }
-    if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
-    else:
-        line["cpu_baseline"] = None
-    print(json.dumps(line), flush=True)
+    return line
 
 
-def main_ep(cfg, args):
-    """Bench line of an expert-parallel rank share: value = local tokens/s; the received
-    rows/s beside it."""
-    r = run_gpu_ep(cfg, args.steps, args.warmup)
-    ms = r["total_ms"] / args.steps
+
+def ep_line(cfg, steps, warmup) -> dict:
+    """Bench line (without the CPU baseline) of an expert-parallel rank share: value =
+    local tokens/s; the received rows/s beside it."""
+    r = run_gpu_ep(cfg, steps, warmup)
+    ms = r["total_ms"] / steps
     acc = account_ep(cfg, r["tpe"])
     kern = {name: roofline_entry(acc[name], r["stage_ms"][name]) for name in acc if name not in EP_SIDE}
     kern["shared"] = {"ms": r["stage_ms"]["shared"], "side_stream": True,
@@ -597,8 +705,8 @@ def main_ep(cfg, args):
         "value": cfg.T_local * 1e3 / ms,
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
@@ -612,11 +720,11 @@ def main_ep(cfg, args):
         "ffn_mfma_frac": dk.get("mfma_frac"),
         "permute_combine_hbm_frac": perm_bytes / (perm_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
         "kernels": kern,
-        "wall_ms_per_step": r["wall_s"] * 1e3 / args.steps,
+        "wall_ms_per_step": r["wall_s"] * 1e3 / steps,
         "setup_s": r["setup_s"],
-        "cpu_baseline": None if args.no_cpu else cpu_baseline(cfg, args.cpu_seconds),
     }
-    print(json.dumps(line), flush=True)
+    return line
+
 
 
 if __name__ == "__main__":
