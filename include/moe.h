@@ -316,6 +316,28 @@ moe_status moe_layer_profiled(const moe_shape* s, const moe_weights* w, const vo
                               void* ws, size_t ws_bytes, hipStream_t stream, hipStream_t side,
                               hipEvent_t* events, int32_t n_events);
 
+/* Bytes of the fixed device scratch array behind moe_layer_static (per GPU). */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* moe_layer without a workspace argument and without any allocation, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Its workspace is a file-scope device array of
+ * MOE_STATIC_SCRATCH_BYTES (64 MiB) that the library reserves on each GPU it runs on,
+ * held until the process ends; shapes whose moe_workspace_bytes() exceeds it are
+ * rejected with MOE_EWORKSPACE before anything is enqueued (the DeepSeek-V3 decode shape
+ * -- H = 7168, 256 experts of I = 2048, top-8 -- fits up to 365 tokens with bf16 experts,
+ * 383 with fp8, 310 with W8A8 and 251 with W4A8 experts).
+ * Every call on a GPU shares that GPU's array, whose contents persist from the last call
+ * (nothing in it has to start at zero): calls that overlap on one GPU -- on different
+ * streams, or on one stream of a graph replayed while another call runs -- race, and the
+ * caller must order them.  Arguments, outputs and results as moe_layer (bit for bit);
+ * the stream must belong to the current device.  The first call on a device looks up the
+ * array's device address (hipGetSymbolAddress); MOE_EHIP if that fails.  No
+ * moe_get_error() is possible for this call (the error word lives in the array): its
+ * routing ids come from its own top-k and are always in range.                        */
+moe_status moe_layer_static(const moe_shape* s, const moe_weights* w, const void* x, void* out,
+                            int32_t* topk_idx, float* topk_w, float* logits, hipStream_t stream);
+
 /* Waits for `stream`, then reads and clears the device error word of `ws`:
  * MOE_EDEVICE if a routing call since the last check saw an expert id outside
  * its [e_base, e_base + E) range, else MOE_OK (MOE_EHIP on a runtime error). */

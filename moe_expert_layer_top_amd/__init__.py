@@ -8,5 +8,6 @@ from ._lib import (  # noqa: F401
     lib, moe_workspace_bytes, moe_grouped_ffn_workspace_bytes, moe_gate_topk, moe_init_routing,
     moe_grouped_ffn, moe_finalize_routing, moe_layer, moe_layer_overlap, moe_layer_profiled,
     moe_get_error, moe_router, router, moe_gate_topk_ex, moe_layer_ex,
-    moe_status_str, EV_NAMES, moe_layer_plan_of, moe_grouped_ffn_gathered,
+    moe_status_str, EV_NAMES, moe_layer_plan_of, moe_grouped_ffn_gathered, moe_layer_static,
+    MOE_STATIC_SCRATCH_BYTES,
 )

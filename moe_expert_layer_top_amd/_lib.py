@@ -24,8 +24,9 @@ EXPORTS = [
     "moe_workspace_bytes", "moe_grouped_ffn_workspace_bytes", "moe_gate_topk", "moe_gate_topk_ex",
     "moe_init_routing", "moe_grouped_ffn", "moe_finalize_routing", "moe_layer", "moe_layer_ex",
     "moe_layer_overlap", "moe_layer_profiled", "moe_get_error", "moe_status_str",
-    "moe_layer_plan_of", "moe_grouped_ffn_gathered",
+    "moe_layer_plan_of", "moe_grouped_ffn_gathered", "moe_layer_static",
 ]
+MOE_STATIC_SCRATCH_BYTES = 64 << 20
 SCORING = {"sigmoid": 0, "softmax": 1}
 EV_NAMES = ["start", "gate", "topk", "route", "expand", "plan", "ffn1", "ffn2", "shared", "finalize"]
 
@@ -102,6 +103,7 @@ def lib() -> ctypes.CDLL:
             "moe_status_str": (ctypes.c_char_p, [I32]),
             "moe_layer_plan_of": (I32, [S, ctypes.POINTER(moe_layer_plan)]),
             "moe_grouped_ffn_gathered": (I32, [S, I32, I32, P, I32, P, P, I32, P, P, P, P, P, P, P, SZ, P]),
+            "moe_layer_static": (I32, [S, ctypes.POINTER(moe_weights), P, P, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -222,6 +224,12 @@ def moe_layer(s, w: moe_weights, x, out, topk_idx, topk_w, logits, ws, stream=No
     _check(lib().moe_layer(ctypes.byref(s), ctypes.byref(w), _ptr(x), _ptr(out), _ptr(topk_idx),
                            _ptr(topk_w), _ptr(logits), _ptr(ws), ws.numel() * ws.element_size(),
                            _stream(stream)), "moe_layer")
+
+
+def moe_layer_static(s, w: moe_weights, x, out, topk_idx, topk_w, logits, stream=None):
+    """moe_layer on the library's fixed per-GPU scratch array (no workspace argument)."""
+    _check(lib().moe_layer_static(ctypes.byref(s), ctypes.byref(w), _ptr(x), _ptr(out), _ptr(topk_idx),
+                                  _ptr(topk_w), _ptr(logits), _stream(stream)), "moe_layer_static")
 
 
 def moe_layer_ex(s, rt, w: moe_weights, x, out, topk_idx, topk_w, logits, ws, side=None, stream=None):

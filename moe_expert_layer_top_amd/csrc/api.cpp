@@ -11,6 +11,7 @@
 #include <cmath>
 #include <climits>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "addr.h"
@@ -955,6 +956,52 @@ static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const voi
   st = moe_finalize_routing(s, at<void>(ws, L.y), at<void>(ws, L.sh_out), tw, eri, out, stream);
   if (st != MOE_OK) return st;
   return prof.mark(MOE_EV_FINALIZE, stream) == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ static scratch
+// moe_layer_static's workspace: one array per GPU, in device memory the code object
+// reserves when it loads on that GPU, held until the process ends.  In host code the
+// array's name is only a host-side stand-in: its device address on the current GPU comes
+// from hipGetSymbolAddress, taken once per device and kept in g_scratch_ptr; only that
+// address is ever handed to kernels.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current GPU's scratch array (set up on its first use there).
+moe_status static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_EHIP;
+  if (dev >= kMaxDevices) return MOE_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_static(const moe_shape* s, const moe_weights* w, const void* x, void* out,
+                            int32_t* topk_idx, float* topk_w, float* logits, hipStream_t stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK || (st = check_inter(s, s->I)) != MOE_OK) return st;
+  const moe_shape sh = shared_shape(s);
+  if ((st = check_inter(&sh, s->I_shared)) != MOE_OK) return st;
+  // the shape's workspace must fit the fixed array: checked before any device call
+  if (moe_workspace_bytes(s) > MOE_STATIC_SCRATCH_BYTES) return MOE_EWORKSPACE;
+  void* ws = nullptr;
+  if ((st = static_scratch(&ws)) != MOE_OK) return st;
+  return layer_impl(s, w, x, out, topk_idx, topk_w, logits, ws, MOE_STATIC_SCRATCH_BYTES, stream, Prof());
 }
 
 moe_status moe_get_error(void* ws, hipStream_t stream) {
