@@ -386,18 +386,22 @@ def _expert_f64(cfg, e):
 
 
 def _ffn_sample(cfg, offsets, a_rows_of, target_s):
-    """Time the oracle's grouped FFN on the whole row sets of the first m active experts
-    (the realized rows per expert of the full routing), m grown until the timed part
-    takes about target_s; each expert's float64 weights are made beforehand (resident
-    weights, as on the GPU).  Returns (seconds, rows timed, experts timed)."""
+    """Time the oracle's grouped FFN on the whole row sets of m active experts spread
+    evenly over the expert ids (the realized rows per expert of the full routing), m
+    grown until the timed part takes about target_s or the experts' float64 weights reach
+    ~12 GB; each expert's float64 weights are made beforehand (resident weights, as on
+    the GPU).  Returns (seconds, rows timed, experts timed)."""
     from concurrent.futures import ThreadPoolExecutor
 
     from oracle import moe as O
     n = np.diff(offsets)
     active = [int(e) for e in np.nonzero(n)[0]]
-    m = min(4, len(active))
+    # at most ~12 GB of float64 weights at a time
+    m_max = max(1, min(len(active), int(12e9 // (3 * cfg.I * cfg.H * 8))))
+    m = min(4, m_max)
     while True:
-        chosen = active[:m]
+        # experts spread evenly over the active ones (hot and cold alike in skewed loads)
+        chosen = [active[int(i * len(active) / m)] for i in range(m)]
         with ThreadPoolExecutor(16) as ex:
             wts = dict(zip(chosen, ex.map(lambda e: _expert_f64(cfg, e), chosen)))
         rows = np.concatenate([np.arange(offsets[e], offsets[e + 1]) for e in chosen])
@@ -407,9 +411,9 @@ def _ffn_sample(cfg, offsets, a_rows_of, target_s):
         O.grouped_ffn(a, sub_offs, lambda j: wts[chosen[j]],
                       quant_h="int8" if cfg.wt in ("int8", "int4") else cfg.wt == "fp8")
         dt = time.perf_counter() - t0
-        if dt >= 0.5 * target_s or m == len(active):
+        if dt >= 0.5 * target_s or m == m_max:
             return dt, int(rows.size), m
-        m = min(len(active), max(m + 1, int(m * min(4.0, target_s / max(dt, 1e-3)))))
+        m = min(m_max, max(m + 1, int(m * min(4.0, target_s / max(dt, 1e-3)))))
         del wts, a
 
 
