@@ -699,7 +699,8 @@ def ep_line(cfg, steps, warmup) -> dict:
                 "achieved": acc["ffn"]["bytes"] / (r["stage_ms"]["ffn"] / 1e3) / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(cfg.name, "ffn")
+    roof["traffic_unit"] = "HBM bytes per ffn stage (both expert GEMMs; rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roof["algorithmic_bytes"] = acc["ffn"]["bytes"]
     roof["mfma_frac"] = dk.get("mfma_frac")
     perm_ms = r["stage_ms"]["route"] + r["stage_ms"]["unsort"]
