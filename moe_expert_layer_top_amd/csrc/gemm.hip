@@ -340,20 +340,25 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
     if constexpr (MULTI) bk += t * tile_b;
     uint32_t m0w = lds_addr(buf);
     asm volatile("" : "+s"(m0w));
+    // every lane offset of this issue is read before the first DMA (fp8: from the LDS
+    // table, so one wait covers them all instead of one LDS round trip per DMA)
+    uint32_t offs[LMAX + 1];
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i) dma16m(ak, lane_off_of(i), m0w + i * NW * 1024u);
+    for (int i = 0; i <= LMAX; ++i) offs[i] = lane_off_of(i);
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) dma16m(ak, offs[i], m0w + i * NW * 1024u);
     if (NTW_OK && ntb) {
 #pragma unroll
       for (int i = 0; i < B_PER; ++i)
-        dma16m<true>(bk, lane_off_of(A_PER + i), m0w + BM * ROWB + i * NW * 1024u);
+        dma16m<true>(bk, offs[A_PER + i], m0w + BM * ROWB + i * NW * 1024u);
     } else {
 #pragma unroll
       for (int i = 0; i < B_PER; ++i)
-        dma16m<false>(bk, lane_off_of(A_PER + i), m0w + BM * ROWB + i * NW * 1024u);
+        dma16m<false>(bk, offs[A_PER + i], m0w + BM * ROWB + i * NW * 1024u);
     }
     if constexpr (FP8) {
-      if (wave < ASW) dma4s(sc_base + step, lane_off_of(LMAX), reinterpret_cast<uint8_t*>(&sa_st[b][64 * wave]));
-      else if (wave == ASW) dma4s(sc_base + step, lane_off_of(LMAX), reinterpret_cast<uint8_t*>(&sb_st[b][0]));
+      if (wave < ASW) dma4s(sc_base + step, offs[LMAX], reinterpret_cast<uint8_t*>(&sa_st[b][64 * wave]));
+      else if (wave == ASW) dma4s(sc_base + step, offs[LMAX], reinterpret_cast<uint8_t*>(&sb_st[b][0]));
     }
   };
 
@@ -394,21 +399,32 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
       // one v_mfma_scale_f32_16x16x128_f8f6f4 (unit hardware scales) per tile pair and
       // K block, promoted into the fp32 accumulator with s_a(token) * s_w(column block)
       // ([MND §Quantization]: activation scales vary only along K).  Lane holds 32
-      // codes (16-byte chunks 2 * kgrp and 2 * kgrp + 1) of its fragment row.  Weight
-      // fragments of the TN column tiles stay in registers; each row tile's activation
-      // fragment is read once and used TN times.
+      // codes of its fragment row: 16-byte chunks kgrp and kgrp + 4 of the 128-byte K
+      // block (any split of K between the lanes is the same product as long as both
+      // operands use it; this one reads conflict-free, where chunks 2 kgrp and 2 kgrp + 1
+      // spent half the LDS cycles in bank conflicts).  Weight fragments of the TN column
+      // tiles stay in registers; each row tile's activation fragment is read once and used
+      // TN times.
       // One LDS pointer per operand and chunk (stage base + lane offset), made opaque so
       // that every tile's read uses it with an immediate tile offset instead of a
       // precomputed address register per tile and stage.
       using lptr = __attribute__((address_space(3))) const uint8_t*;
-      lptr a_lo = (lptr)(buf + lane_off(2 * kgrp));
-      lptr a_hi = (lptr)(buf + lane_off(2 * kgrp + 1));
-      lptr b_lo = (lptr)(lb + lane_off(2 * kgrp));
-      lptr b_hi = (lptr)(lb + lane_off(2 * kgrp + 1));
+      lptr a_lo = (lptr)(buf + lane_off(kgrp));
+      lptr a_hi = (lptr)(buf + lane_off(kgrp + 4));
+      lptr b_lo = (lptr)(lb + lane_off(kgrp));
+      lptr b_hi = (lptr)(lb + lane_off(kgrp + 4));
       asm volatile("" : "+v"(a_lo), "+v"(a_hi), "+v"(b_lo), "+v"(b_hi));
       auto frag = [&](lptr lo_p, lptr hi_p, int tile) __attribute__((always_inline)) {
         const u32x4 lo = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(lo_p + tile * 16 * ROWB);
         const u32x4 hi = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(hi_p + tile * 16 * ROWB);
+        return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      };
+      // the same read, kept in program order (volatile), so that it stays in the step
+      // of the pipeline below that issues it
+      auto frag_v = [&](lptr lo_p, lptr hi_p, int tile) __attribute__((always_inline)) {
+        using vp = volatile const __attribute__((address_space(3))) u32x4*;
+        const u32x4 lo = *reinterpret_cast<vp>(lo_p + tile * 16 * ROWB);
+        const u32x4 hi = *reinterpret_cast<vp>(hi_p + tile * 16 * ROWB);
         return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       };
       i32x8 bw[TN];
@@ -422,19 +438,53 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
         // (block 1); plain store: the first 128 columns of the tile are block 0
         sb[i] = SWIGLU ? (i < TN / 2 ? sb0 : sb1) : (wn * TN * 16 < kQBlock ? sb0 : sb1);
       }
+      // Software pipeline over the row tiles: the MFMAs of row tile j are issued before
+      // the promotion of row tile j - 1, whose products have finished by then, so no
+      // MFMA waits on its own result and the promotion runs beside the next MFMAs.  The
+      // scheduling barriers keep the compiler from hoisting every row tile's fragment
+      // read to the top (which left no registers for separate products).
+      i32x8 at = frag(a_lo, a_hi, wm);
+      f32x4 prev[TN];
+      float fprev[TN];
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        const i32x8 at = frag(a_lo, a_hi, j * WM + wm);
         const float sa = sa_st[b][16 * (j * WM + wm) + (lane & 15)];
+        f32x4 cur[TN];
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+          cur[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              bw[i], at, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+        if (j + 1 < J) at = frag_v(a_lo, a_hi, (j + 1) * WM + wm);
+        if (j > 0) {
+#pragma unroll
+          for (int i = 0; i < TN; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              acc[j - 1][i][r] = fmaf(prev[i][r], fprev[i], acc[j - 1][i][r]);
+              // pins the promotion (and so the MFMAs it reads) to this step: pure
+              // arithmetic would otherwise sink below later reads and branches
+              asm volatile("" : "+v"(acc[j - 1][i][r]));
+            }
+        }
 #pragma unroll
         for (int i = 0; i < TN; ++i) {
-          const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              bw[i], at, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-          const float f = sa * sb[i];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[j][i][r] = fmaf(part[r], f, acc[j][i][r]);
+          prev[i] = cur[i];
+          fprev[i] = sa * sb[i];
         }
+        // order within the step: each MFMA followed by one LDS read and a few of the
+        // promotion FMAs, which run while the MFMA does
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[J - 1][i][r] = fmaf(prev[i][r], fprev[i], acc[J - 1][i][r]);
       return;
     }
 #pragma unroll
