@@ -23,6 +23,7 @@ using moe::GemmArgs;
 using moe::Unit;
 
 constexpr size_t kAlign = 256;
+static_assert(moe::kPlanInts * sizeof(int32_t) <= kAlign, "planner count array fits its slot");
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;
 constexpr int kGateMaxSplits = 16;
@@ -435,8 +436,11 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
   int mu;
   if (planned) {
     mu = max_units(cfg, fp8, G, R_max, alt_rows);
+    // XCD chunks balance 16-row tiles for the big tiles (their MFMAs set the time of a
+    // well-filled unit) and unit counts for the short ones (their time is the weights)
     hipError_t e = moe::launch_plan(io.offsets, G, io.offsets ? 0 : R_max, alt_rows, bm,
-                                    std::max(1, mu), units, n_units, st);
+                                    std::max(1, mu), cfg == moe::CFG_BIG ? bm / 2 : bm,
+                                    units, n_units, st);
     if (e != hipSuccess) return MOE_EHIP;
   } else {
     mu = (R_max + bm - 1) / bm;

@@ -193,8 +193,22 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   const int slot = bid / kXcds;
   const int n_grp = (p.n_tiles + tpw - 1) / tpw;
   const int per_unit = n_grp * p.splits;
-  const int u = (slot / per_unit) * kXcds + xcd;
-  const int rem = slot % per_unit;
+  int u, rem;
+  if constexpr (UNIFORM) {
+    u = (slot / per_unit) * kXcds + xcd;
+    rem = slot % per_unit;
+  } else {
+    // This XCD's chunk of the unit table, walked run by run (a run: one group's
+    // consecutive units), and inside a run N tile (and split) major: the workgroups
+    // that run together on the XCD share each weight panel through its L2.
+    const int c0 = p.n_units[1 + xcd], c1 = p.n_units[2 + xcd];
+    if (slot >= (c1 - c0) * per_unit) return;
+    const Unit uq = p.units[c0 + slot / per_unit];
+    const int rs = max(uq.first, c0), re = min(uq.first + uq.count, c1);
+    const int l = slot - (rs - c0) * per_unit;
+    rem = l / (re - rs);
+    u = rs + l % (re - rs);
+  }
   const int nt0 = (rem % n_grp) * tpw;           // first N tile of this workgroup
   const int ntc = min(tpw, p.n_tiles - nt0);     // N tiles it computes
   const int split = rem / n_grp;
@@ -205,7 +219,6 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
     un.row0 = u * BM;
     un.rows = min(BM, p.uniform_rows - u * BM);
   } else {
-    if (u >= *p.n_units) return;
     un = p.units[u];
   }
   const int rows = un.rows;
@@ -481,10 +494,12 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      if constexpr (J > 0) {
 #pragma unroll
-      for (int i = 0; i < TN; ++i)
+        for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[J - 1][i][r] = fmaf(prev[i][r], fprev[i], acc[J - 1][i][r]);
+          for (int r = 0; r < 4; ++r) acc[J - 1][i][r] = fmaf(prev[i][r], fprev[i], acc[J - 1][i][r]);
+      }
       return;
     }
 #pragma unroll
@@ -795,13 +810,26 @@ __global__ __launch_bounds__(WM* WN * 64) void dense_gemm_dma_kernel(GemmArgs p)
 // that run together) mixes the compute-heavy shared slices with weight-streaming
 // routed ones.  Units past `cap` (only reachable if offsets[G] exceeds the rows the
 // caller sized the workspace for) are dropped rather than written out of bounds.
+// Then the table is cut into kXcds chunks of consecutive units, one per XCD, of
+// near-equal cost and at most ceil(cap / kXcds) units each, the most a launch sized for
+// `cap` units gives one XCD.  A unit's cost is its 16-row tiles, counted as at least
+// cost_floor rows (below that its loads, not its MFMAs, set its time), plus one for its
+// prologue and epilogue; cost_floor = BM makes every unit cost the same.
+static_assert(kPlanInts == 2 + kXcds, "planner count array: count + chunk bounds");
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int G,
                                                     int rows_if_null, int extra_rows, int BM,
-                                                    int cap, Unit* __restrict__ units,
+                                                    int cap, int cost_floor, Unit* __restrict__ units,
                                                     int32_t* __restrict__ n_units) {
   __shared__ int32_t wsum[16];
   __shared__ int32_t carry;
-  if (threadIdx.x == 0) carry = 0;
+  __shared__ long long csum[16];
+  __shared__ long long ccarry;
+  __shared__ int32_t below[kXcds];
+  if (threadIdx.x == 0) {
+    carry = 0;
+    ccarry = 0;
+  }
+  if (threadIdx.x < kXcds) below[threadIdx.x] = 0;
   __syncthreads();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int nx = extra_rows > 0 ? (extra_rows + BM - 1) / BM : 0;
@@ -841,7 +869,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     __syncthreads();
     const int base = carry + wsum[w] + incl - nu;  // routed units of groups < g
     if (g < G) {
-      // the extra slices that go right before this group, then the group's own units
+      // the extra slices that go right before this group (a run of their own), then the
+      // group's own units
       const int x0 = extra_upto(g - 1), x1 = extra_upto(g);
       for (int i = x0; i < x1; ++i) {
         Unit un;
@@ -849,6 +878,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
         un.row0 = i * per_x;
         un.rows = min(per_x, extra_rows - i * per_x);
         un.flags = nx == 1 ? kUnitSoleReader : 0;
+        un.first = base + x0;
+        un.count = x1 - x0;
         if (base + i < cap) units[base + i] = un;
       }
       if (nu > 0) {
@@ -859,6 +890,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
           un.row0 = start + i * per;
           un.rows = min(per, n - i * per);
           un.flags = nu == 1 ? kUnitSoleReader : 0;
+          un.first = base + x1;
+          un.count = nu;
           if (base + x1 + i < cap) units[base + x1 + i] = un;
         }
       }
@@ -867,13 +900,76 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     if (threadIdx.x == 1023) carry = base + nu;
     __syncthreads();
   }
-  if (threadIdx.x == 0) *n_units = min(carry + nx, cap);
+  const int total = min(carry + nx, cap);
+  // Chunk bounds.  Cost of unit i: c_i = ceil(max(rows_i, cost_floor) / 16) + 1; unit i counts below
+  // target x (x = 1 .. kXcds-1) when its midpoint P_i + c_i / 2 lies before x / kXcds of
+  // the total cost (P_i: cost of the units before it).  The table was written by this
+  // block; the reads below bypass the L1 (volatile), so they see it.
+  auto cost_of = [&](int i) -> long long {
+    const int r = max(*reinterpret_cast<volatile const int32_t*>(&units[i].rows), cost_floor);
+    return (r + 15) / 16 + 1;
+  };
+  long long mine = 0;
+  for (int i = threadIdx.x; i < total; i += 1024) mine += cost_of(i);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mine += __shfl_xor(mine, o, 64);
+  if (lane == 0) csum[w] = mine;
+  __syncthreads();
+  long long all = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) all += csum[i];
+  __syncthreads();
+  int cnt[kXcds] = {};
+  for (int i0 = 0; i0 < total; i0 += 1024) {
+    const int i = i0 + threadIdx.x;
+    const long long c = i < total ? cost_of(i) : 0;
+    long long incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const long long v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) csum[w] = incl;
+    __syncthreads();
+    long long before = ccarry;
+    for (int v = 0; v < w; ++v) before += csum[v];
+    if (i < total) {
+      const long long mid2 = 2 * (before + incl - c) + c;   // twice the midpoint
+#pragma unroll
+      for (int x = 1; x < kXcds; ++x) cnt[x] += (mid2 * kXcds < 2LL * x * all) ? 1 : 0;
+    }
+    __syncthreads();
+    if (threadIdx.x == 1023) ccarry = before + incl;
+    __syncthreads();
+  }
+#pragma unroll
+  for (int x = 1; x < kXcds; ++x) {
+    int v = cnt[x];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane == 0) atomicAdd(&below[x], v);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // clamp in order: chunk x holds at most per_xcd units, and what is left fits the rest
+    const int per_xcd = (cap + kXcds - 1) / kXcds;
+    int b = 0;
+    n_units[0] = total;
+    n_units[1] = 0;
+    for (int x = 1; x < kXcds; ++x) {
+      const int lo = max(b, total - (kXcds - x) * per_xcd);
+      const int hi = b + per_xcd;
+      b = min(max(below[x], lo), hi);
+      n_units[1 + x] = b;
+    }
+    n_units[1 + kXcds] = total;
+  }
 }
 
 hipError_t launch_plan(const int32_t* offsets, int G, int rows_if_null, int extra_rows, int block_m,
-                       int cap, Unit* units, int32_t* n_units, hipStream_t st) {
-  plan_kernel<<<1, 1024, 0, st>>>(offsets, G, rows_if_null, extra_rows, block_m, cap, units,
-                                  n_units);
+                       int cap, int cost_floor, Unit* units, int32_t* n_units, hipStream_t st) {
+  plan_kernel<<<1, 1024, 0, st>>>(offsets, G, rows_if_null, extra_rows, block_m, cap, cost_floor,
+                                  units, n_units);
   return hipGetLastError();
 }
 

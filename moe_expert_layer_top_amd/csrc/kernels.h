@@ -8,10 +8,15 @@ namespace moe {
 
 constexpr int kSegSlots = 1024;  // routing slots per counting-sort segment (one wavefront)
 
-// Unit of grouped-GEMM work: rows [row0, row0 + rows) of group `group`.
+// Unit of grouped-GEMM work: rows [row0, row0 + rows) of group `group`.  The units of
+// one group (and the consecutive slices of the extra group) form a run of consecutive
+// table entries: `first` is the table index of the run's first unit, `count` its length.
 struct Unit {
-  int32_t group, row0, rows, flags;
+  int32_t group, row0, rows, flags, first, count;
 };
+// The planner's count array: [0] units in the table, [1 + x] (x = 0..kXcds) first unit
+// of XCD x's chunk of the table ([1 + kXcds] = the count again).
+constexpr int kPlanInts = 2 + 8;   // 8 = kXcds (checked where both are visible)
 // Unit::flags bit: no other unit reads this group's weights (the weight panel is streamed
 // once, with a non-temporal cache policy)
 constexpr int32_t kUnitSoleReader = 1;
@@ -40,7 +45,8 @@ struct GemmArgs {
   float* c_scale;           // EPI_SWIGLU_FP8: [rows, N/128]
   long long c_scale_ld;
   const Unit* units;        // device unit table (unused when uniform_rows > 0)
-  const int32_t* n_units;   // device unit count (unused when uniform_rows > 0)
+  const int32_t* n_units;   // device unit count and XCD chunk bounds (kPlanInts ints;
+                            // unused when uniform_rows > 0)
   int uniform_rows;         // > 0: one group of this many rows cut into BM slices
   int N;                    // logical output columns
   int K;                    // reduction length in elements
@@ -93,7 +99,7 @@ hipError_t launch_gemm_i8(GemmCfg cfg, Epilogue epi, bool w4, const GemmArgs& a,
 // NULL, one group of `rows_if_null` rows; extra_rows > 0 appends group G of that many
 // rows (rows counted from 0 in its own tensor).
 hipError_t launch_plan(const int32_t* offsets, int G, int rows_if_null, int extra_rows, int block_m,
-                       int cap, Unit* units, int32_t* n_units, hipStream_t st);
+                       int cap, int cost_floor, Unit* units, int32_t* n_units, hipStream_t st);
 
 // Router variant (the plain router: {0, 1, 1, 1, 1, 1.0f}); validated by the caller.
 struct RouterArgs {
