@@ -141,6 +141,16 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   constexpr int LMAX = (LD_ALL + NW - 1) / NW;   // DMA instructions per wave per stage
   constexpr int LREM = LD_ALL % NW;              // waves < LREM issue LMAX, others LMAX-1
   constexpr int STAGE = BM * ROWB + BN * ROWB_B;
+  // Loader wavefronts.  With a two-deep ring and 8 wavefronts, waves 0..3 (one per SIMD)
+  // issue every load of a stage and waves 4..7 none: a wavefront stalls until the CU
+  // accepts each of its loads, so this way one wavefront per SIMD starts its MFMAs right
+  // after the barrier while the other is still issuing, instead of both waiting on a
+  // burst of loads.  Otherwise every wavefront issues an equal share.
+  constexpr int LW = (NST == 2 && NW == 8) ? 4 : NW;
+  static_assert(A_LD % LW == 0 && B_LD % LW == 0, "chunks split evenly over the loaders");
+  constexpr int A_PER = A_LD / LW, B_PER = B_LD / LW;
+  constexpr int LPER = A_PER + B_PER;            // DMA chunks per loader wave and stage
+  static_assert(LW != NW || (LPER == LMAX && LREM == 0), "uniform per-wave DMA count");
   // Weights read by this unit alone stream through the caches non-temporally (they are
   // not read again); weights that other units of the group also read stay cacheable.
   // Packed int4 rows of a 128-element stage are 64-byte half lines: not non-temporal, so
@@ -176,7 +186,8 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   // fp8: the per-lane DMA offsets live in LDS and are re-read (volatile) at each issue;
   // in registers they would be spilled, and a scratch reload waits on vmcnt(0), which
   // would drain the DMAs in flight.
-  __shared__ uint32_t off_tab[FP8 ? (LMAX + 1) : 1][FP8 ? NT : 1];
+  __shared__ uint32_t off_tab[FP8 ? LPER : 1][FP8 ? LW * 64 : 1];   // loader lanes' chunk offsets
+  __shared__ uint32_t sc_tab[FP8 ? (ASW + 1) * 64 : 1];               // scale offsets, waves 0 .. ASW
 
   // A workgroup computes TPW consecutive N tiles of one unit (one K split); its ring runs
   // on from one tile's K steps into the next's, so the next tile's first stage is in
@@ -252,42 +263,42 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   bool ntb = false;   // wave-uniform: stream this unit's weights non-temporally
   if constexpr (!UNIFORM) ntb = (un.flags & kUnitSoleReader) != 0;
 
-  // DMA plan.  Every wavefront issues A_PER activation chunks (q = wave + i * NW) and
-  // B_PER weight chunks (q = wave + i * NW) per stage; both counts are compile-time, so
-  // the issue sequence has no branches.  Lane -> (row q*RPC + lane/CPR, physical 16-byte
-  // slot lane%CPR), which holds logical K chunk (lane%CPR) ^ swz(row).  Rows past the
-  // unit and columns past N re-load a valid row; their results are never stored.
-  static_assert(A_LD % NW == 0 && B_LD % NW == 0, "chunks split evenly over the wavefronts");
-  constexpr int A_PER = A_LD / NW, B_PER = B_LD / NW;
-  static_assert(A_PER + B_PER == LMAX && LREM == 0, "uniform per-wave DMA count");
-  uint32_t goff[LMAX];
+  // DMA plan.  Every loader wavefront issues A_PER activation chunks (q = wave + i * LW)
+  // and B_PER weight chunks (q = wave + i * LW) per stage; both counts are compile-time,
+  // so the issue sequence has no branches.  Lane -> (row q*RPC + lane/CPR, physical
+  // 16-byte slot lane%CPR), which holds logical K chunk (lane%CPR) ^ swz(row).  Rows past
+  // the unit and columns past N re-load a valid row; their results are never stored.
+  const bool loader = LW == NW || wave < LW;   // wave-uniform
+  uint32_t goff[LPER];
   const int lrow = lane / CPR;
   const int lphys = lane % CPR;
-#pragma unroll
-  for (int i = 0; i < A_PER; ++i) {
-    const int q = wave + i * NW;
-    const int r = q * RPC + lrow;
-    const int rc = r < rows ? r : rows - 1;
-    const long long src = gather ? gather[un.row0 + rc] / p.gather_div : rc;
-    goff[i] = static_cast<uint32_t>(src * lda + ((lphys ^ swz<ROWB>(r)) << 4));
-  }
   const int lrow_b = lane / CPR_B;
   const int lphys_b = lane % CPR_B;
+  if (loader) {
 #pragma unroll
-  for (int i = 0; i < B_PER; ++i) {
-    const int j = (wave + i * NW) * RPC_B + lrow_b;
-    int col, grow;
-    if constexpr (SWIGLU) {
-      constexpr int WCOLS = TN * 16, HALF = TN * 8;
-      const int wn2 = j / WCOLS, jj = j % WCOLS;
-      col = nt0 * (BN / 2) + wn2 * HALF + (jj % HALF);
-      grow = (jj < HALF ? 0 : p.up_off) + col;
-    } else {
-      col = nt0 * BN + j;
-      grow = col;
+    for (int i = 0; i < A_PER; ++i) {
+      const int q = wave + i * LW;
+      const int r = q * RPC + lrow;
+      const int rc = r < rows ? r : rows - 1;
+      const long long src = gather ? gather[un.row0 + rc] / p.gather_div : rc;
+      goff[i] = static_cast<uint32_t>(src * lda + ((lphys ^ swz<ROWB>(r)) << 4));
     }
-    if (col >= p.N) grow -= col - (p.N - 1);
-    goff[A_PER + i] = static_cast<uint32_t>(static_cast<long long>(grow) * p.ldb + ((lphys_b ^ swz<ROWB_B>(j)) << 4));
+#pragma unroll
+    for (int i = 0; i < B_PER; ++i) {
+      const int j = (wave + i * LW) * RPC_B + lrow_b;
+      int col, grow;
+      if constexpr (SWIGLU) {
+        constexpr int WCOLS = TN * 16, HALF = TN * 8;
+        const int wn2 = j / WCOLS, jj = j % WCOLS;
+        col = nt0 * (BN / 2) + wn2 * HALF + (jj % HALF);
+        grow = (jj < HALF ? 0 : p.up_off) + col;
+      } else {
+        col = nt0 * BN + j;
+        grow = col;
+      }
+      if (col >= p.N) grow -= col - (p.N - 1);
+      goff[A_PER + i] = static_cast<uint32_t>(static_cast<long long>(grow) * p.ldb + ((lphys_b ^ swz<ROWB_B>(j)) << 4));
+    }
   }
 
   // fp8 scale sources of this lane: wavefronts 0 .. BM/64-1 fetch the activation
@@ -322,18 +333,18 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
         join_u32_halves(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(sb)),
                         __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(sb >> 32))));
   }
+  using vlds = volatile __attribute__((address_space(3))) uint32_t*;
   if constexpr (FP8) {
+    if (loader) {
 #pragma unroll
-    for (int i = 0; i < LMAX; ++i) off_tab[i][tid] = goff[i];
-    off_tab[LMAX][tid] = sc_off;
+      for (int i = 0; i < LPER; ++i) off_tab[i][tid] = goff[i];
+    }
+    if (wave <= ASW) sc_tab[tid] = sc_off;
     // visible to this lane's own later reads; no other lane reads it
   }
   auto lane_off_of = [&](int i) __attribute__((always_inline)) {
-    if constexpr (FP8) {
-      using vlds = volatile __attribute__((address_space(3))) uint32_t*;
-      return ((vlds)&off_tab[i][0])[tid];
-    }
-    else return i < LMAX ? goff[i] : 0u;
+    if constexpr (FP8) return ((vlds)&off_tab[i][0])[tid];
+    else return goff[i];
   };
   // This wavefront's first 1 KB chunk of each ring buffer, as an LDS byte address
   // (wave-uniform).  Each DMA's M0 is formed from it with a compile-time offset at the
@@ -353,25 +364,30 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
     if constexpr (MULTI) bk += t * tile_b;
     uint32_t m0w = lds_addr(buf);
     asm volatile("" : "+s"(m0w));
-    // every lane offset of this issue is read before the first DMA (fp8: from the LDS
-    // table, so one wait covers them all instead of one LDS round trip per DMA)
-    uint32_t offs[LMAX + 1];
+    if (loader) {
+      // every lane offset of this issue is read before the first DMA (fp8: from the LDS
+      // table, so one wait covers them all instead of one LDS round trip per DMA)
+      uint32_t offs[LPER];
 #pragma unroll
-    for (int i = 0; i <= LMAX; ++i) offs[i] = lane_off_of(i);
+      for (int i = 0; i < LPER; ++i) offs[i] = lane_off_of(i);
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i) dma16m(ak, offs[i], m0w + i * NW * 1024u);
-    if (NTW_OK && ntb) {
+      for (int i = 0; i < A_PER; ++i) dma16m(ak, offs[i], m0w + i * LW * 1024u);
+      if (NTW_OK && ntb) {
 #pragma unroll
-      for (int i = 0; i < B_PER; ++i)
-        dma16m<true>(bk, offs[A_PER + i], m0w + BM * ROWB + i * NW * 1024u);
-    } else {
+        for (int i = 0; i < B_PER; ++i)
+          dma16m<true>(bk, offs[A_PER + i], m0w + BM * ROWB + i * LW * 1024u);
+      } else {
 #pragma unroll
-      for (int i = 0; i < B_PER; ++i)
-        dma16m<false>(bk, offs[A_PER + i], m0w + BM * ROWB + i * NW * 1024u);
+        for (int i = 0; i < B_PER; ++i)
+          dma16m<false>(bk, offs[A_PER + i], m0w + BM * ROWB + i * LW * 1024u);
+      }
     }
     if constexpr (FP8) {
-      if (wave < ASW) dma4s(sc_base + step, offs[LMAX], reinterpret_cast<uint8_t*>(&sa_st[b][64 * wave]));
-      else if (wave == ASW) dma4s(sc_base + step, offs[LMAX], reinterpret_cast<uint8_t*>(&sb_st[b][0]));
+      if (wave <= ASW) {
+        const uint32_t so = ((vlds)&sc_tab[0])[tid];
+        if (wave < ASW) dma4s(sc_base + step, so, reinterpret_cast<uint8_t*>(&sa_st[b][64 * wave]));
+        else dma4s(sc_base + step, so, reinterpret_cast<uint8_t*>(&sb_st[b][0]));
+      }
     }
   };
 
