@@ -548,7 +548,7 @@ DEFAULT_ALSO = "c5_skewed_fp8,c3_ep_rank_bf16,c4_decode_bf16"
 def parse_args(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c2_prefill_bf16")
     ap.add_argument("--also", default=None,
