@@ -203,17 +203,20 @@ bool merge_shared(const moe_shape* s) {
   return s->act == MOE_BF16 && (s->wt == MOE_BF16 || s->wt == MOE_INT8) && s->I_shared == s->I;
 }
 
-// N tiles per workgroup of the unsplit down projection with tall bf16 or int8 tiles: the
+// N tiles per workgroup of the unsplit down projection with tall int8 / int4 tiles: the
 // ring's one stage in flight carries on across a tile boundary (the next tile's first
 // stage loads while this tile's epilogue stores) and the workgroup's start-up (unit
 // read, offsets, first load) is paid once per several tiles.  Four, or two, while the
-// grid still holds a round of workgroups for the CUs (c2's down projection: 2.40 ->
-// 2.32 ms).  The gate / up projection keeps one tile per workgroup: there a second tile
-// re-reads the unit's activation rows (14 KB each at H = 7168), which cost more than the
-// start-up saved (measured +1% at c2, +8% at the EP rank share).  The decode tiles keep
-// one tile per workgroup in both GEMMs: grouping four measured 3-7% slower (c7, c8).
-int down_tiles_per_wg(moe::GemmCfg cfg, bool fp8, long long units, int N, int bn) {
-  if (cfg != moe::CFG_BIG || fp8 || N % bn != 0) return 1;
+// grid still holds a round of workgroups for the CUs (c6's down projection: 1.51 ->
+// 1.46 ms against one tile).  The bf16 tall tiles keep one tile per workgroup: with the
+// units of an expert walked N tile major on one XCD (the planner's chunks) and four
+// loader wavefronts, grouping no longer pays there (c2: 2.25 ms with one tile, 2.27 with
+// four, which also re-read the unit's rows of h from the last-level cache).  The gate /
+// up projection keeps one tile per workgroup: there a second tile re-reads the unit's
+// activation rows (14 KB each at H = 7168).  The decode tiles keep one tile per
+// workgroup in both GEMMs: grouping four measured 3-7% slower (c7, c8).
+int down_tiles_per_wg(moe::GemmCfg cfg, bool fp8, bool q8, long long units, int N, int bn) {
+  if (cfg != moe::CFG_BIG || fp8 || !q8 || N % bn != 0) return 1;
   const long long tiles = N / bn;
   for (int t : {4, 2})
     if (units * ((tiles + t - 1) / t) >= kCus) return t;
@@ -605,7 +608,7 @@ moe_status run_ffn(const moe_shape* s, int G, int R_max, int I, const FfnIo& io,
       e = moe::launch_sum_reduce(part2, sp.s2, p2.c_split2, alt_rows, H, nullptr, alt->y, st);
   } else {
     GemmArgs q2 = g2;
-    q2.tiles_per_wg = planned ? down_tiles_per_wg(cfg, fp8, est_units(G, R_max, alt_rows, bm), H, bn) : 1;
+    q2.tiles_per_wg = planned ? down_tiles_per_wg(cfg, fp8, i8, est_units(G, R_max, alt_rows, bm), H, bn) : 1;
     e = i8 ? moe::launch_gemm_i8(cfg, moe::EPI_STORE_BF16, w4, q2, mu, st)
            : moe::launch_gemm(cfg, moe::EPI_STORE_BF16, fp8, q2, mu, st);
   }
@@ -642,7 +645,7 @@ moe_status moe_layer_plan_of(const moe_shape* s, moe_layer_plan* out) {
   out->ffn2_tiles_per_wg =
       (s->act == MOE_F32 || sp.s2 > 1)
           ? 1
-          : down_tiles_per_wg(cfg, fp8, est_units(s->E, R, merge_shared(s) ? s->T : 0, out->block_m),
+          : down_tiles_per_wg(cfg, fp8, q8_weights(s), est_units(s->E, R, merge_shared(s) ? s->T : 0, out->block_m),
                               s->H, moe::gemm_block_n(cfg));
   return MOE_OK;
 }

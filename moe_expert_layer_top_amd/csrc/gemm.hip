@@ -192,9 +192,9 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   // A workgroup computes TPW consecutive N tiles of one unit (one K split); its ring runs
   // on from one tile's K steps into the next's, so the next tile's first stage is in
   // flight while this one's epilogue stores.  Only for plain stores (the down
-  // projection) where the ring is two deep (every wait drains the counter, so the
-  // epilogue's stores cannot shift it) and without fp8.
-  constexpr bool MULTI = !UNIFORM && !FP8 && NST == 2 && (EPI == EPI_STORE_BF16 || EPI == EPI_STORE_F32);
+  // projection) of int8 / int4 operands where the ring is two deep (every wait drains the
+  // counter, so the epilogue's stores cannot shift it).
+  constexpr bool MULTI = !UNIFORM && Q8 && NST == 2 && (EPI == EPI_STORE_BF16 || EPI == EPI_STORE_F32);
   const int tpw = MULTI ? p.tiles_per_wg : 1;
   // tiles past the first address their weight rows by a fixed offset from the first's,
   // which needs whole tiles along N (the launcher enforces it)
@@ -998,9 +998,9 @@ hipError_t go_dma(const GemmArgs& a, int max_units, hipStream_t st) {
   constexpr bool SWIGLU = EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_FP8;
   const int tpw = a.tiles_per_wg;
   if (tpw < 1) return hipErrorInvalidValue;
-  // several N tiles per workgroup: grouped two-deep rings with plain stores, without fp8,
+  // several N tiles per workgroup: grouped two-deep int8 / int4 rings with plain stores,
   // whole tiles along N
-  if (tpw > 1 && (FP8 || NST != 2 || SWIGLU || a.uniform_rows > 0 || a.N % BN != 0))
+  if (tpw > 1 && (!(I8 || W4) || NST != 2 || SWIGLU || a.uniform_rows > 0 || a.N % BN != 0))
     return hipErrorInvalidValue;
   const long long per_unit = static_cast<long long>((a.n_tiles + tpw - 1) / tpw) * a.splits;
   const long long slots = (static_cast<long long>(max_units) + kXcds - 1) / kXcds;

@@ -193,7 +193,7 @@ CONFIGS = {
     # number of K stages (each tile starts its own load ring) ----
     "p14_multi_bf16": MoEConfig(
         name="p14_multi_bf16", cid=44, T=1125, H=1280, E=128, k=8, I=256, I_shared=256,
-        act="bf16", wt="bf16", description="prefill, 128 experts, four down-projection tiles per workgroup"),
+        act="bf16", wt="bf16", description="prefill, 128 experts, H = 1280 (bf16 twin of p15 and p16)"),
     "p15_multi_w8a8": MoEConfig(
         name="p15_multi_w8a8", cid=45, T=1125, H=1280, E=128, k=8, I=384, I_shared=384,
         act="bf16", wt="int8", description="W8A8 prefill, 128 experts, several tiles per workgroup, odd K stages"),

@@ -169,11 +169,13 @@ def test_layer_plan_query(L):
 
     p = plan("c2_prefill_bf16")       # prefill: tall tiles, shared expert merged, rows gathered
     assert p == {"shared_merged": 1, "rows_gathered": 1, "ffn1_splits": 1, "ffn2_splits": 1, "block_m": 320,
-                 "ffn2_tiles_per_wg": 4}
-    # 32 experts of 256 rows and a shared expert of its own shape (not merged): 32 units,
-    # where two down-projection tiles per workgroup keep a round of workgroups
+                 "ffn2_tiles_per_wg": 1}
+    # the int8 down projection chains four N tiles per workgroup at the same shape
+    assert plan("c6_prefill_w8a8")["ffn2_tiles_per_wg"] == 4
+    # 32 experts of 256 rows (int8) and a shared expert of its own shape (not merged): 32
+    # units, where two down-projection tiles per workgroup keep a round of workgroups
     # (32 x 14 >= 256 CUs) and four would not
-    p = M.moe_layer_plan_of(M.shape(8192, 7168, 32, 1, 2048, 1024, "bf16", "bf16"))
+    p = M.moe_layer_plan_of(M.shape(8192, 7168, 32, 1, 2048, 1024, "bf16", "int8"))
     assert p["shared_merged"] == 0 and p["ffn2_tiles_per_wg"] == 2
     assert plan("c5_skewed_fp8")["ffn2_tiles_per_wg"] == 1      # fp8: one tile per workgroup
     assert plan("c4_decode_bf16")["ffn2_tiles_per_wg"] == 1     # decode tiles
