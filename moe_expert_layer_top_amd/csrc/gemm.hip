@@ -12,9 +12,14 @@
 //     than sizing work by the buffer bound), so no count ever crosses to the host.
 //     An expert's rows are cut into ceil(n/BM) near-equal slices, so a prefill
 //     expert (n <= BM) streams its weight panel from HBM exactly once.
-//   * Workgroups are dealt round-robin to the 8 XCDs; the block -> unit mapping
-//     keeps all N tiles of one unit on one XCD, so the unit's activation rows are
-//     fetched from HBM once and re-read from that XCD's L2.
+//   * Workgroups are dealt round-robin to the 8 XCDs.  The planner cuts the unit table
+//     into one contiguous, cost-balanced chunk per XCD; an XCD's workgroups walk its
+//     chunk expert by expert, N tile major inside an expert's units, so the workgroups
+//     that run together share each weight panel and each unit's activation rows
+//     through that XCD's L2.
+//   * In the two-deep 8-wavefront tiles, wavefronts 0-3 (one per SIMD) issue all of a
+//     stage's loads and 4-7 none: a wavefront stalls until the CU accepts each load,
+//     and this way one wavefront per SIMD starts its MFMAs while the other issues.
 //   * Operands are both K-contiguous ([out, in] weights).  Each stage moves a K slice
 //     of BM activation rows and BN weight rows straight into LDS (direct-to-LDS loads,
 //     an NST-deep ring, one barrier per stage), XOR-swizzled by row so the 16-byte
