@@ -40,6 +40,7 @@
 #include "addr.h"
 #include "common.h"
 #include "kernels.h"
+#include "plan.h"
 
 namespace moe {
 
@@ -220,10 +221,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
     const int c0 = p.n_units[1 + xcd], c1 = p.n_units[2 + xcd];
     if (slot >= (c1 - c0) * per_unit) return;
     const Unit uq = p.units[c0 + slot / per_unit];
-    const int rs = max(uq.first, c0), re = min(uq.first + uq.count, c1);
-    const int l = slot - (rs - c0) * per_unit;
-    rem = l / (re - rs);
-    u = rs + l % (re - rs);
+    plan_map_slot(slot, per_unit, c0, c1, uq.first, uq.count, &u, &rem);
   }
   const int nt0 = (rem % n_grp) * tpw;           // first N tile of this workgroup
   const int ntc = min(tpw, p.n_tiles - nt0);     // N tiles it computes
@@ -853,14 +851,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   if (threadIdx.x < kXcds) below[threadIdx.x] = 0;
   __syncthreads();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int nx = extra_rows > 0 ? (extra_rows + BM - 1) / BM : 0;
-  const int per_x = nx > 0 ? (((extra_rows + nx - 1) / nx + 15) & ~15) : 0;
-  // extra slices placed before the units of groups 0..g: min(nx, ceil((g + 1) * nx / G))
-  auto extra_upto = [&](int g) -> int {
-    if (nx == 0 || g < 0) return 0;
-    const long long c = (static_cast<long long>(g + 1) * nx + G - 1) / G;
-    return static_cast<int>(c < nx ? c : nx);
-  };
+  const int nx = plan_units_of(extra_rows, BM);
+  const int per_x = nx > 0 ? plan_slice_rows(extra_rows, nx) : 0;
   for (int g0 = 0; g0 < G; g0 += 1024) {
     const int g = g0 + threadIdx.x;
     int n = 0, start = 0;
@@ -868,7 +860,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
       start = offsets ? offsets[g] : 0;
       n = offsets ? offsets[g + 1] - start : rows_if_null;
     }
-    const int nu = n > 0 ? (n + BM - 1) / BM : 0;
+    const int nu = plan_units_of(n, BM);
     int incl = nu;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -892,7 +884,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     if (g < G) {
       // the extra slices that go right before this group (a run of their own), then the
       // group's own units
-      const int x0 = extra_upto(g - 1), x1 = extra_upto(g);
+      const int x0 = plan_extra_upto(g - 1, nx, G), x1 = plan_extra_upto(g, nx, G);
       for (int i = x0; i < x1; ++i) {
         Unit un;
         un.group = G;
@@ -904,7 +896,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
         if (base + i < cap) units[base + i] = un;
       }
       if (nu > 0) {
-        const int per = ((n + nu - 1) / nu + 15) & ~15;
+        const int per = plan_slice_rows(n, nu);
         for (int i = 0; i < nu; ++i) {
           Unit un;
           un.group = g;
@@ -927,8 +919,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   // the total cost (P_i: cost of the units before it).  The table was written by this
   // block; the reads below bypass the L1 (volatile), so they see it.
   auto cost_of = [&](int i) -> long long {
-    const int r = max(*reinterpret_cast<volatile const int32_t*>(&units[i].rows), cost_floor);
-    return (r + 15) / 16 + 1;
+    return plan_unit_cost(*reinterpret_cast<volatile const int32_t*>(&units[i].rows), cost_floor);
   };
   long long mine = 0;
   for (int i = threadIdx.x; i < total; i += 1024) mine += cost_of(i);
@@ -957,7 +948,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     if (i < total) {
       const long long mid2 = 2 * (before + incl - c) + c;   // twice the midpoint
 #pragma unroll
-      for (int x = 1; x < kXcds; ++x) cnt[x] += (mid2 * kXcds < 2LL * x * all) ? 1 : 0;
+      for (int x = 1; x < kXcds; ++x) cnt[x] += plan_below(mid2, x, kXcds, all) ? 1 : 0;
     }
     __syncthreads();
     if (threadIdx.x == 1023) ccarry = before + incl;
@@ -972,18 +963,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    // clamp in order: chunk x holds at most per_xcd units, and what is left fits the rest
-    const int per_xcd = (cap + kXcds - 1) / kXcds;
-    int b = 0;
     n_units[0] = total;
-    n_units[1] = 0;
-    for (int x = 1; x < kXcds; ++x) {
-      const int lo = max(b, total - (kXcds - x) * per_xcd);
-      const int hi = b + per_xcd;
-      b = min(max(below[x], lo), hi);
-      n_units[1 + x] = b;
-    }
-    n_units[1 + kXcds] = total;
+    plan_chunk_bounds(below, total, cap, kXcds, n_units + 1);
   }
 }
 

@@ -199,6 +199,24 @@ def test_layer_plan_query(L):
         M.moe_layer_plan_of(bad)
 
 
+def test_plan_helpers_on_the_cpu(tmp_path):
+    """The work-plan index arithmetic of the planner kernel and the grouped GEMM
+    (unit slices, the shared expert's slices spread through the table, per-XCD chunk
+    bounds by cost, slot -> (unit, N tile)), compiled from the kernels' own header by the
+    host compiler: on 405 unit tables (one dense group, empty and hot groups, more rows
+    than the sized bound, random uniform / Zipf-like / clustered counts) every N tile of
+    every unit is reached by exactly one workgroup of the launch grid, no XCD's chunk
+    exceeds the grid's slots for it, and a run of units is walked N tile major."""
+    exe = tmp_path / "plan_check"
+    src = os.path.join(ROOT, "tests", "csrc", "plan_check.cpp")
+    inc = os.path.join(ROOT, "moe_expert_layer_top_amd", "csrc")
+    subprocess.run(["g++", "-std=c++17", "-O2", "-Wall", "-Werror", "-I", inc, src, "-o", str(exe)],
+                   check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "all plan checks passed" in r.stdout
+
+
 def test_address_helpers_on_the_cpu(tmp_path):
     """The 64-bit base rebuilt from two 32-bit halves (the fp8 scale loads of the grouped
     GEMM) and the 32-bit lane-offset bound, compiled from the kernels' own header by the
