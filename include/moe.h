@@ -83,7 +83,8 @@ typedef struct {
  * (0 if the shape is invalid). */
 size_t moe_workspace_bytes(const moe_shape* s);
 
-/* Workspace bytes needed by moe_grouped_ffn for G groups and at most R_max rows. */
+/* Workspace bytes needed by moe_grouped_ffn for G groups (1 .. 1024) and at most R_max
+ * rows (0 if the arguments are invalid). */
 size_t moe_grouped_ffn_workspace_bytes(const moe_shape* s, int32_t G, int32_t R_max);
 
 /* How moe_layer runs shape `s`: a host-side description of its launch plan, for callers
@@ -179,7 +180,7 @@ moe_status moe_init_routing(const moe_shape* s, const void* x, const int32_t* id
  * y = (silu(a W1^T) * (a W3^T)) W2^T with its own weights.  The group sizes
  * are read on the device ([MND §Quantization]: kernels read the routed token
  * counts instead of sizing work by the buffer bound).
- *   G              number of groups (experts)
+ *   G              number of groups (experts), 1 .. 1024 (MOE_EUNSUPPORTED above)
  *   R_max          rows in a and y (>= group_offsets[G], which the kernels read)
  *   a              [R_max, H]  act, or fp8 / int8 codes when s->wt is fp8 / int8 or int4
  *   a_scale        fp32 [R_max, H/128] (fp8), [R_max] (int8), else NULL

@@ -651,7 +651,8 @@ moe_status moe_layer_plan_of(const moe_shape* s, moe_layer_plan* out) {
 }
 
 size_t moe_grouped_ffn_workspace_bytes(const moe_shape* s, int32_t G, int32_t R_max) {
-  if (check_shape(s) != MOE_OK || check_inter(s, s->I) != MOE_OK || G < 1 || R_max < 0) return 0;
+  if (check_shape(s) != MOE_OK || check_inter(s, s->I) != MOE_OK || G < 1 || G > kMaxE || R_max < 0)
+    return 0;
   return std::max<size_t>(ffn_layout(s, G, R_max, s->I).total, kAlign);
 }
 
@@ -751,6 +752,7 @@ moe_status moe_grouped_ffn(const moe_shape* s, int32_t G, int32_t R_max, const v
   if (st != MOE_OK) return st;
   if ((st = check_inter(s, s->I)) != MOE_OK) return st;
   if (G < 1 || R_max < 0) return MOE_EINVAL;
+  if (G > kMaxE) return MOE_EUNSUPPORTED;
   const bool scaled = s->wt == MOE_FP8_E4M3 || q8_weights(s);
   if (!group_offsets || !ws) return MOE_EINVAL;
   if (R_max > 0 && (!a || !w13 || !w2 || !y)) return MOE_EINVAL;
@@ -770,6 +772,7 @@ moe_status moe_grouped_ffn_gathered(const moe_shape* s, int32_t G, int32_t R_max
   if (st != MOE_OK) return st;
   if ((st = check_inter(s, s->I)) != MOE_OK) return st;
   if (G < 1 || R_max < 0 || a_rows < 0 || row_div < 1) return MOE_EINVAL;
+  if (G > kMaxE) return MOE_EUNSUPPORTED;
   if (s->act == MOE_F32) return MOE_EUNSUPPORTED;   // the fp32 kernels read rows in order
   const bool fp8 = s->wt == MOE_FP8_E4M3, scaled = fp8 || q8_weights(s);
   if (!moe::lane_offsets_fit_u32((fp8 || q8_weights(s)) ? 1 : 2, a_rows, s->H)) return MOE_EUNSUPPORTED;

@@ -820,146 +820,118 @@ __global__ __launch_bounds__(WM* WN * 64) void dense_gemm_dma_kernel(GemmArgs p)
 
 // Experts: units come from the device-built table.
 // ------------------------------------------------------------------ unit planner
-// One block: units per group = ceil(n / BM) near-equal slices (rows rounded up to
-// 16), prefix-summed over groups, then each group writes its slices.  When
-// extra_rows > 0 there is one more group, index G, of extra_rows rows starting at row
-// 0 of its own tensor (the shared expert folded into the routed launch).  Its n_x
-// slices are spread evenly through the table -- slice i goes right before the units of
-// group floor(i * G / n_x) -- so every stretch of consecutive units (the workgroups
-// that run together) mixes the compute-heavy shared slices with weight-streaming
-// routed ones.  Units past `cap` (only reachable if offsets[G] exceeds the rows the
-// caller sized the workspace for) are dropped rather than written out of bounds.
-// Then the table is cut into kXcds chunks of consecutive units, one per XCD, of
-// near-equal cost and at most ceil(cap / kXcds) units each, the most a launch sized for
-// `cap` units gives one XCD.  A unit's cost is its 16-row tiles, counted as at least
-// cost_floor rows (below that its loads, not its MFMAs, set its time), plus one for its
-// prologue and epilogue; cost_floor = BM makes every unit cost the same.
+// One block of 1024 threads, thread g owning group g (G <= 1024, the callers' limit):
+// units per group = ceil(n / BM) near-equal slices (rows rounded up to 16), prefix-summed
+// over groups, then each group writes its slices.  When extra_rows > 0 there is one more
+// group, index G, of extra_rows rows starting at row 0 of its own tensor (the shared
+// expert folded into the routed launch).  Its n_x slices are spread evenly through the
+// table -- slice i goes right before the units of group floor(i * G / n_x) -- so every
+// stretch of consecutive units (the workgroups that run together) mixes the
+// compute-heavy shared slices with weight-streaming routed ones.  Units past `cap` (only
+// reachable if offsets[G] exceeds the rows the caller sized the workspace for) are
+// dropped rather than written out of bounds.  Then the table is cut into kXcds chunks of
+// consecutive units, one per XCD, of near-equal cost and at most ceil(cap / kXcds) units
+// each, the most a launch sized for `cap` units gives one XCD.  A unit's cost is its
+// 16-row tiles, counted as at least cost_floor rows (below that its loads, not its MFMAs,
+// set its time), plus one for its prologue and epilogue; cost_floor = BM makes every unit
+// cost the same.  Counts and costs are scanned together and every value stays in
+// registers, so the table is written once and never read back.
 static_assert(kPlanInts == 2 + kXcds, "planner count array: count + chunk bounds");
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int G,
                                                     int rows_if_null, int extra_rows, int BM,
                                                     int cap, int cost_floor, Unit* __restrict__ units,
                                                     int32_t* __restrict__ n_units) {
   __shared__ int32_t wsum[16];
-  __shared__ int32_t carry;
   __shared__ long long csum[16];
-  __shared__ long long ccarry;
   __shared__ int32_t below[kXcds];
-  if (threadIdx.x == 0) {
-    carry = 0;
-    ccarry = 0;
-  }
   if (threadIdx.x < kXcds) below[threadIdx.x] = 0;
-  __syncthreads();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = threadIdx.x;
   const int nx = plan_units_of(extra_rows, BM);
   const int per_x = nx > 0 ? plan_slice_rows(extra_rows, nx) : 0;
-  for (int g0 = 0; g0 < G; g0 += 1024) {
-    const int g = g0 + threadIdx.x;
-    int n = 0, start = 0;
-    if (g < G) {
-      start = offsets ? offsets[g] : 0;
-      n = offsets ? offsets[g + 1] - start : rows_if_null;
-    }
-    const int nu = plan_units_of(n, BM);
-    int incl = nu;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
-    if (lane == 63) wsum[w] = incl;
-    __syncthreads();
-    if (w == 0) {
-      const int v = lane < 16 ? wsum[lane] : 0;
-      int inc = v;
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const int uu = __shfl_up(inc, o, 64);
-        if (lane >= o) inc += uu;
-      }
-      if (lane < 16) wsum[lane] = inc - v;
-    }
-    __syncthreads();
-    const int base = carry + wsum[w] + incl - nu;  // routed units of groups < g
-    if (g < G) {
-      // the extra slices that go right before this group (a run of their own), then the
-      // group's own units
-      const int x0 = plan_extra_upto(g - 1, nx, G), x1 = plan_extra_upto(g, nx, G);
-      for (int i = x0; i < x1; ++i) {
-        Unit un;
-        un.group = G;
-        un.row0 = i * per_x;
-        un.rows = min(per_x, extra_rows - i * per_x);
-        un.flags = nx == 1 ? kUnitSoleReader : 0;
-        un.first = base + x0;
-        un.count = x1 - x0;
-        if (base + i < cap) units[base + i] = un;
-      }
-      if (nu > 0) {
-        const int per = plan_slice_rows(n, nu);
-        for (int i = 0; i < nu; ++i) {
-          Unit un;
-          un.group = g;
-          un.row0 = start + i * per;
-          un.rows = min(per, n - i * per);
-          un.flags = nu == 1 ? kUnitSoleReader : 0;
-          un.first = base + x1;
-          un.count = nu;
-          if (base + x1 + i < cap) units[base + x1 + i] = un;
-        }
-      }
-    }
-    __syncthreads();
-    if (threadIdx.x == 1023) carry = base + nu;
-    __syncthreads();
+  int n = 0, start = 0;
+  if (g < G) {
+    start = offsets ? offsets[g] : 0;
+    n = offsets ? offsets[g + 1] - start : rows_if_null;
   }
-  const int total = min(carry + nx, cap);
-  // Chunk bounds.  Cost of unit i: c_i = ceil(max(rows_i, cost_floor) / 16) + 1; unit i counts below
-  // target x (x = 1 .. kXcds-1) when its midpoint P_i + c_i / 2 lies before x / kXcds of
-  // the total cost (P_i: cost of the units before it).  The table was written by this
-  // block; the reads below bypass the L1 (volatile), so they see it.
-  auto cost_of = [&](int i) -> long long {
-    return plan_unit_cost(*reinterpret_cast<volatile const int32_t*>(&units[i].rows), cost_floor);
-  };
-  long long mine = 0;
-  for (int i = threadIdx.x; i < total; i += 1024) mine += cost_of(i);
+  const int nu = plan_units_of(n, BM);
+  const int per = nu > 0 ? plan_slice_rows(n, nu) : 0;
+  const int x0 = g < G ? plan_extra_upto(g - 1, nx, G) : 0;
+  const int x1 = g < G ? plan_extra_upto(g, nx, G) : 0;
+  auto extra_rows_of = [&](int i) { return min(per_x, extra_rows - i * per_x); };
+  auto own_rows_of = [&](int i) { return min(per, n - i * per); };
+  // units of groups before g: a block scan of nu
+  int incl = nu;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mine += __shfl_xor(mine, o, 64);
-  if (lane == 0) csum[w] = mine;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[w] = incl;
   __syncthreads();
+  int base = incl - nu;   // routed units of groups < g
+  for (int v = 0; v < w; ++v) base += wsum[v];
+  int routed = 0;
+  for (int v = 0; v < 16; ++v) routed += wsum[v];
+  const int total = min(routed + nx, cap);
+  // this thread's table entries: extras at base + x0 .. base + x1 - 1, then its own units
+  // at base + x1 ..; their cost (entries past the cap are dropped and cost nothing)
+  long long cg = 0;
+  for (int i = x0; i < x1; ++i)
+    if (base + i < cap) cg += plan_unit_cost(extra_rows_of(i), cost_floor);
+  for (int i = 0; i < nu; ++i)
+    if (base + x1 + i < cap) cg += plan_unit_cost(own_rows_of(i), cost_floor);
+  long long cincl = cg;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const long long v = __shfl_up(cincl, o, 64);
+    if (lane >= o) cincl += v;
+  }
+  if (lane == 63) csum[w] = cincl;
+  if (g < G) {
+    for (int i = x0; i < x1; ++i) {
+      Unit un;
+      un.group = G;
+      un.row0 = i * per_x;
+      un.rows = extra_rows_of(i);
+      un.flags = nx == 1 ? kUnitSoleReader : 0;
+      un.first = base + x0;
+      un.count = x1 - x0;
+      if (base + i < cap) units[base + i] = un;
+    }
+    for (int i = 0; i < nu; ++i) {
+      Unit un;
+      un.group = g;
+      un.row0 = start + i * per;
+      un.rows = own_rows_of(i);
+      un.flags = nu == 1 ? kUnitSoleReader : 0;
+      un.first = base + x1;
+      un.count = nu;
+      if (base + x1 + i < cap) units[base + x1 + i] = un;
+    }
+  }
+  __syncthreads();
+  long long before = cincl - cg;   // cost of the table entries before this thread's
+  for (int v = 0; v < w; ++v) before += csum[v];
   long long all = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) all += csum[i];
-  __syncthreads();
+  for (int v = 0; v < 16; ++v) all += csum[v];
+  // units whose cost midpoint lies before x / kXcds of the total
   int cnt[kXcds] = {};
-  for (int i0 = 0; i0 < total; i0 += 1024) {
-    const int i = i0 + threadIdx.x;
-    const long long c = i < total ? cost_of(i) : 0;
-    long long incl = c;
+  auto count = [&](int idx, int rows) {
+    if (idx >= cap) return;
+    const long long c = plan_unit_cost(rows, cost_floor);
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const long long v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
-    if (lane == 63) csum[w] = incl;
-    __syncthreads();
-    long long before = ccarry;
-    for (int v = 0; v < w; ++v) before += csum[v];
-    if (i < total) {
-      const long long mid2 = 2 * (before + incl - c) + c;   // twice the midpoint
-#pragma unroll
-      for (int x = 1; x < kXcds; ++x) cnt[x] += plan_below(mid2, x, kXcds, all) ? 1 : 0;
-    }
-    __syncthreads();
-    if (threadIdx.x == 1023) ccarry = before + incl;
-    __syncthreads();
-  }
+    for (int x = 1; x < kXcds; ++x) cnt[x] += plan_below(2 * before + c, x, kXcds, all) ? 1 : 0;
+    before += c;
+  };
+  for (int i = x0; i < x1; ++i) count(base + i, extra_rows_of(i));
+  for (int i = 0; i < nu; ++i) count(base + x1 + i, own_rows_of(i));
 #pragma unroll
   for (int x = 1; x < kXcds; ++x) {
     int v = cnt[x];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    if (lane == 0) atomicAdd(&below[x], v);
+    if (lane == 0 && v != 0) atomicAdd(&below[x], v);
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -970,6 +942,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
 
 hipError_t launch_plan(const int32_t* offsets, int G, int rows_if_null, int extra_rows, int block_m,
                        int cap, int cost_floor, Unit* units, int32_t* n_units, hipStream_t st) {
+  if (G < 1 || G > 1024) return hipErrorInvalidValue;   // one group per planner thread
   plan_kernel<<<1, 1024, 0, st>>>(offsets, G, rows_if_null, extra_rows, block_m, cap, cost_floor,
                                   units, n_units);
   return hipGetLastError();

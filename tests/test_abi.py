@@ -94,6 +94,14 @@ def test_validation_errors_enqueue_nothing(L):
                            None) == M.MOE_EINVAL
     assert L.moe_grouped_ffn(ctypes.byref(s), 0, 10, *P[:3], DUMMY, None, DUMMY, None, DUMMY, DUMMY,
                              1 << 30, None) == M.MOE_EINVAL
+    # more groups than the planner's one thread per group (too small a workspace, so a
+    # regression would report EWORKSPACE rather than launch)
+    assert L.moe_grouped_ffn(ctypes.byref(s), 1025, 10, *P[:3], DUMMY, None, DUMMY, None, DUMMY, DUMMY,
+                             16, None) == M.MOE_EUNSUPPORTED
+    assert L.moe_grouped_ffn_gathered(ctypes.byref(s), 1025, 10, DUMMY, 64, None, DUMMY, 1, DUMMY, DUMMY,
+                                      None, DUMMY, None, DUMMY, DUMMY, 16, None) == M.MOE_EUNSUPPORTED
+    assert M.moe_grouped_ffn_workspace_bytes(s, 1025, 10) == 0
+    assert M.moe_grouped_ffn_workspace_bytes(s, 1024, 10) > 0
     fp8 = M.shape(16, 256, 8, 2, 128, 128, "bf16", "fp8")
     assert L.moe_grouped_ffn(ctypes.byref(fp8), 8, 32, DUMMY, None, DUMMY, DUMMY, None, DUMMY, None,
                              DUMMY, DUMMY, 1 << 30, None) == M.MOE_EINVAL   # fp8 needs scales
