@@ -266,11 +266,13 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   bool ntb = false;   // wave-uniform: stream this unit's weights non-temporally
   if constexpr (!UNIFORM) ntb = (un.flags & kUnitSoleReader) != 0;
 
-  // DMA plan.  Every loader wavefront issues A_PER activation chunks (q = wave + i * LW)
-  // and B_PER weight chunks (q = wave + i * LW) per stage; both counts are compile-time,
-  // so the issue sequence has no branches.  Lane -> (row q*RPC + lane/CPR, physical
-  // 16-byte slot lane%CPR), which holds logical K chunk (lane%CPR) ^ swz(row).  Rows past
-  // the unit and columns past N re-load a valid row; their results are never stored.
+  // DMA plan.  Every loader wavefront issues up to A_PER activation chunks (q = wave + i *
+  // LW) and B_PER weight chunks (q = wave + i * LW) per stage.  Lane -> (row q*RPC +
+  // lane/CPR, physical 16-byte slot lane%CPR), which holds logical K chunk (lane%CPR) ^
+  // swz(row).  Rows past the unit inside a chunk and columns past N re-load a valid row;
+  // in the two-deep rings (whose waits drain the counter, so the per-wave load count may
+  // vary) an activation chunk wholly past the unit's rows is not loaded and its LDS rows
+  // keep stale data.  Either way those rows only feed result rows that are never stored.
   const bool loader = LW == NW || wave < LW;   // wave-uniform
   uint32_t goff[LPER];
   const int lrow = lane / CPR;
@@ -374,7 +376,8 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
 #pragma unroll
       for (int i = 0; i < LPER; ++i) offs[i] = lane_off_of(i);
 #pragma unroll
-      for (int i = 0; i < A_PER; ++i) dma16m(ak, offs[i], m0w + i * LW * 1024u);
+      for (int i = 0; i < A_PER; ++i)   // wave-uniform test: chunk q holds a row of the unit
+        if (NST != 2 || (wave + i * LW) * RPC < rows) dma16m(ak, offs[i], m0w + i * LW * 1024u);
       if (NTW_OK && ntb) {
 #pragma unroll
         for (int i = 0; i < B_PER; ++i)
