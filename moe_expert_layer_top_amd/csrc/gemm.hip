@@ -688,7 +688,42 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
       }
     }
   }
-  if constexpr (EPI == EPI_STORE_BF16 || EPI == EPI_STORE_F32) {
+  if constexpr (EPI == EPI_STORE_BF16 && TN % 2 == 0) {
+    // Tiles i and i + 1 in pairs: lanes kgrp and kgrp ^ 1 (lane ^ 16, the same token row)
+    // swap one 4-column half, so an even kgrp holds columns 4 * kgrp .. + 7 of tile i and
+    // an odd one columns 4 * (kgrp - 1) .. + 7 of tile i + 1, 16 bytes either way; a store
+    // instruction then writes 64 contiguous bytes of each of its 16 rows instead of 32.
+    const bool odd = (kgrp & 1) != 0;
+    const int cpair = nt * BN + wn * TN * 16 + (odd ? 16 : 0) + 4 * (kgrp & ~1);
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      if (j >= jcount) continue;   // wave-uniform
+      const int row = 16 * (j * WM + wm) + crow;
+      uint16_t* crow_p = static_cast<uint16_t*>(cptr_e) + static_cast<long long>(row0_e + row) * ldc_e;
+#pragma unroll
+      for (int i = 0; i < TN; i += 2) {
+        const uint32_t a0 = pack_bf16x2(acc[j][i][0], acc[j][i][1]);
+        const uint32_t a1 = pack_bf16x2(acc[j][i][2], acc[j][i][3]);
+        const uint32_t b0 = pack_bf16x2(acc[j][i + 1][0], acc[j][i + 1][1]);
+        const uint32_t b1 = pack_bf16x2(acc[j][i + 1][2], acc[j][i + 1][3]);
+        // every lane takes part in the swap; the partner lane has the same row, so the
+        // row test below drops both or neither
+        const uint32_t r0 = __shfl_xor(odd ? a0 : b0, 16, 64);
+        const uint32_t r1 = __shfl_xor(odd ? a1 : b1, 16, 64);
+        if (row >= rows) continue;
+        const uint4 v = odd ? make_uint4(r0, r1, b0, b1) : make_uint4(a0, a1, r0, r1);
+        const int col = cpair + 16 * i;
+        if (col + 7 < p.N) {
+          *reinterpret_cast<uint4*>(crow_p + col) = v;
+        } else {
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int r = 0; r < 8; ++r)
+            if (col + r < p.N) crow_p[col + r] = static_cast<uint16_t>(w[r >> 1] >> (16 * (r & 1)));
+        }
+      }
+    }
+  } else if constexpr (EPI == EPI_STORE_BF16 || EPI == EPI_STORE_F32) {
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       if (j >= jcount) continue;
