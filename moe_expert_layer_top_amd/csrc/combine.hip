@@ -161,9 +161,7 @@ __global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float* __restr
       const bool zero = m == 0.f;
       const float scale = zero ? 1.0f : m / 448.0f;
       const float inv = zero ? 0.0f : 448.0f / m;
-      uint32_t q = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) q |= f32_to_e4m3(hv[i] * inv) << (8 * i);
+      const uint32_t q = f32x4_to_e4m3(hv[0] * inv, hv[1] * inv, hv[2] * inv, hv[3] * inv);
       *reinterpret_cast<uint32_t*>(h + static_cast<long long>(r) * I + c) = zero ? 0u : q;
       if ((threadIdx.x & 31) == 0) h_scale[static_cast<long long>(r) * (I / kQBlock) + c / kQBlock] = scale;
     } else {

@@ -33,28 +33,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-// OCP e4m3fn encode of a float32 with round-to-nearest-even and saturation to
-// +-448, written from the format definition (1 sign, 4 exponent bits with bias
-// 7, 3 mantissa bits; exponent field 0 is subnormal with spacing 2^-9).
-__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7fffffffu;
-  if (a >= 0x43e00000u) return sign | 0x7eu;  // |v| >= 448 (and inf): saturate
-  int e = static_cast<int>(a >> 23) - 127;    // unbiased float exponent
-  if (e < -6) {
-    // subnormal result: round |v| / 2^-9 to an integer 0..8 (8 == smallest normal)
-    float q = rintf(__uint_as_float(a) * 512.0f);  // exact scaling by a power of two
-    return sign | static_cast<uint32_t>(q);
-  }
-  // normal: keep 3 mantissa bits, round half to even on the dropped 20 bits
-  uint32_t mant = a & 0x7fffffu;
-  uint32_t keep = mant >> 20;
-  uint32_t rest = mant & 0xfffffu;
-  uint32_t r = (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ? 1u : 0u;
-  uint32_t code = (static_cast<uint32_t>(e + 7) << 3) + keep + r;  // carry rolls into the exponent
-  if (code > 0x7eu) code = 0x7eu;
-  return sign | code;
+// OCP e4m3fn encode (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent
+// field 0 subnormal with spacing 2^-9) with round-to-nearest-even and saturation to +-448,
+// of four floats packed as bytes 0 .. 3: gfx950's v_cvt_pk_fp8_f32, two values per
+// instruction, on the values clamped to +-448 first.  On every non-NaN float32 it gives
+// the same code as the encode written out from the format definition (rounding the 20
+// dropped mantissa bits half to even, subnormals as round(|v| / 2^-9), |v| >= 448 to
+// 0x7e); a NaN input gives +-448.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
+  const float ca = fminf(fmaxf(a, -448.0f), 448.0f), cb = fminf(fmaxf(b, -448.0f), 448.0f);
+  const float cc = fminf(fmaxf(c, -448.0f), 448.0f), cd = fminf(fmaxf(d, -448.0f), 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false);   // bytes 0, 1
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(cc, cd, w, true);         // bytes 2, 3
+  return static_cast<uint32_t>(w);
 }
 
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {

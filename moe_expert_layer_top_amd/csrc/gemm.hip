@@ -827,9 +827,9 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
 #pragma unroll
       for (int i = 0; i < HT; ++i) {
         const int col = nt * (BN / 2) + wn * (TN * 8) + 16 * i + ccol4;
-        uint32_t q = 0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) q |= (zero ? 0u : f32_to_e4m3(acc[j][i][r] * inv)) << (8 * r);
+        const uint32_t q = zero ? 0u
+                                : f32x4_to_e4m3(acc[j][i][0] * inv, acc[j][i][1] * inv, acc[j][i][2] * inv,
+                                                acc[j][i][3] * inv);
         if (col + 3 < p.N) {
           *reinterpret_cast<uint32_t*>(hrow + col) = q;
         } else {

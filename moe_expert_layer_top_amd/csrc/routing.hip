@@ -572,11 +572,8 @@ __global__ __launch_bounds__(256) void expand_quant_kernel(const uint16_t* __res
     const bool zero = amax == 0.f;
     const float scale = zero ? 1.0f : amax / 448.0f;
     const float inv = zero ? 0.0f : 448.0f / amax;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(v[i] * inv) << (8 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(v[4 + i] * inv) << (8 * i);
+    uint32_t lo = f32x4_to_e4m3(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    uint32_t hi = f32x4_to_e4m3(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
     if (zero) lo = hi = 0;
     const uint2 q = make_uint2(lo, hi);
     for (int j = 0; j < k; ++j) {
