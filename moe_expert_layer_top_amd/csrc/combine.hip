@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float* __restr
     }
     float hv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hv[i] = g[i] / (1.0f + __expf(-g[i])) * u[i];
+    for (int i = 0; i < 4; ++i) hv[i] = silu_fast(g[i]) * u[i];
     if constexpr (FP8) {
       float m = fmaxf(fmaxf(fabsf(hv[0]), fabsf(hv[1])), fmaxf(fabsf(hv[2]), fabsf(hv[3])));
 #pragma unroll

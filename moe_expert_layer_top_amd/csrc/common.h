@@ -33,6 +33,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// silu(g) = g / (1 + e^-g) for results rounded to bf16 or fp8 next: the hardware
+// exponential and reciprocal (v_exp_f32, v_rcp_f32, about 1 ulp each) instead of the
+// correctly rounded division sequence; the error stays far below the 8-bit mantissa.
+__device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
 // OCP e4m3fn encode (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent
 // field 0 subnormal with spacing 2^-9) with round-to-nearest-even and saturation to +-448,
 // of four floats packed as bytes 0 .. 3: gfx950's v_cvt_pk_fp8_f32, two values per

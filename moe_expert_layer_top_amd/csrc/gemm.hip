@@ -771,7 +771,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
         for (int r = 0; r < 4; ++r) {
           const float g = acc[j][i][r];
           const float up = acc[j][i + HT][r];
-          hv[r] = g / (1.0f + __expf(-g)) * up;
+          hv[r] = silu_fast(g) * up;
         }
         uint16_t* hp = static_cast<uint16_t*>(cptr_e) + static_cast<long long>(row0_e + row) * ldc_e + col;
         if (col + 3 < p.N) {
@@ -802,7 +802,7 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float g = acc[j][i][r];
-          const float hv = g / (1.0f + __expf(-g)) * acc[j][i + HT][r];
+          const float hv = silu_fast(g) * acc[j][i + HT][r];
           acc[j][i][r] = hv;
           m = fmaxf(m, fabsf(hv));
         }
