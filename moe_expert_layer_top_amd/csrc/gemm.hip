@@ -25,7 +25,8 @@
 //     an NST-deep ring, one barrier per stage), XOR-swizzled by row so the 16-byte
 //     fragment reads of 8 consecutive lanes hit distinct banks.
 //   * Wavefronts own 16-row tiles round-robin, so a partially filled unit spreads
-//     its valid rows over all wavefronts; tiles past the unit's rows are skipped.
+//     its valid rows over all wavefronts; tiles past the unit's rows are skipped, and
+//     the two-deep rings do not load activation chunks wholly past them.
 //   * bf16: v_mfma_f32_16x16x32_bf16.  fp8 (e4m3): one v_mfma 16x16x128 per
 //     128-wide K block, promoted into the fp32 accumulator with the 1x128
 //     activation scale times the 128x128 weight scale ([MND §Quantization]:
@@ -33,7 +34,8 @@
 //     K block).
 //   * Epilogues: SwiGLU (h = silu(gate) * up, gate and up columns of the same
 //     h column sit in the same lane), optional 1x128 fp8 quantization of h,
-//     bf16 store, or fp32 split-k partials.
+//     bf16 store (tile pairs regrouped by a lane swap into 16-byte stores), or fp32
+//     split-k partials; bf16 and e4m3 rounding use gfx950's conversion instructions.
 
 #include <type_traits>
 
