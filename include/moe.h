@@ -15,7 +15,8 @@
  *   [V32] page "NPU DeepSeek-V3.2-Exp inference optimization practice".
  *
  * Conventions shared by every call
- *   - Tensor pointers are DEVICE pointers, row-major, 16-byte aligned.  The
+ *   - Tensor pointers are DEVICE pointers, row-major, 16-byte aligned (a non-null
+ *     pointer that is not is MOE_EINVAL: the kernels move 16-byte vectors).  The
  *     caller allocates and owns every buffer and the workspace; the library
  *     allocates nothing, frees nothing and keeps no state between calls.
  *   - Every call only enqueues work on `stream`; none synchronizes or reads

@@ -11,6 +11,7 @@
 #include <cmath>
 #include <climits>
 #include <cstdint>
+#include <initializer_list>
 #include <mutex>
 
 #include "../../include/moe.h"
@@ -34,6 +35,14 @@ constexpr long long kCus = 256;             // MI355X compute units
 constexpr int kMinSliceStages = 8;        // K stages per split-K slice, at least
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Tensor pointers must be 16-byte aligned (the kernels move 16-byte vectors); null
+// pointers, the optional arguments, pass.
+bool aligned16(std::initializer_list<const void*> ps) {
+  for (const void* q : ps)
+    if (reinterpret_cast<uintptr_t>(q) & 15u) return false;
+  return true;
+}
 
 int elem_bytes(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 2 : 1; }  // int4: 1 (bound)
 
@@ -673,6 +682,7 @@ moe_status moe_gate_topk_ex(const moe_shape* s, const moe_router* router, const 
   if (!router_args(s, router, &ra)) return MOE_EINVAL;
   if (s->T > 0 && (!x || !w_gate || !topk_idx || !topk_w)) return MOE_EINVAL;
   if (!ws) return MOE_EINVAL;
+  if (!aligned16({x, w_gate, bias, logits, topk_idx, topk_w, ws})) return MOE_EINVAL;
   const size_t need = moe_workspace_bytes(s);
   if (need == 0) return MOE_EINVAL;
   if (ws_bytes < need) return MOE_EWORKSPACE;
@@ -714,6 +724,9 @@ static moe_status init_routing_impl(const moe_shape* s, const void* x, const int
   if (s->T > 0 && (!ids || !expanded_row_idx)) return MOE_EINVAL;
   if (expanded_x && s->T > 0 && !x) return MOE_EINVAL;
   if (expanded_x && (fp8 || i8) && !expanded_scale) return MOE_EINVAL;
+  if (!aligned16({x, ids, expanded_x, expanded_scale, expanded_row_idx, sorted_src, tokens_per_expert,
+                  expert_offsets, ws, tok_q, tok_s}))
+    return MOE_EINVAL;
   const size_t need = moe_workspace_bytes(s);
   if (need == 0) return MOE_EINVAL;
   if (ws_bytes < need) return MOE_EWORKSPACE;
@@ -757,6 +770,7 @@ moe_status moe_grouped_ffn(const moe_shape* s, int32_t G, int32_t R_max, const v
   if (!group_offsets || !ws) return MOE_EINVAL;
   if (R_max > 0 && (!a || !w13 || !w2 || !y)) return MOE_EINVAL;
   if (scaled && R_max > 0 && (!a_scale || !w13_scale || !w2_scale)) return MOE_EINVAL;
+  if (!aligned16({a, a_scale, group_offsets, w13, w13_scale, w2, w2_scale, y, ws})) return MOE_EINVAL;
   if (ws_bytes < moe_grouped_ffn_workspace_bytes(s, G, R_max)) return MOE_EWORKSPACE;
   FfnIo io{a, a_scale, group_offsets, w13, w13_scale, w2, w2_scale, y};
   return run_ffn(s, G, R_max, s->I, io, ws, stream);
@@ -779,6 +793,8 @@ moe_status moe_grouped_ffn_gathered(const moe_shape* s, int32_t G, int32_t R_max
   if (!group_offsets || !ws) return MOE_EINVAL;
   if (R_max > 0 && (!a || !row_of || !w13 || !w2 || !y)) return MOE_EINVAL;
   if (scaled && R_max > 0 && (!a_scale || !w13_scale || !w2_scale)) return MOE_EINVAL;
+  if (!aligned16({a, a_scale, row_of, group_offsets, w13, w13_scale, w2, w2_scale, y, ws}))
+    return MOE_EINVAL;
   if (ws_bytes < moe_grouped_ffn_workspace_bytes(s, G, R_max)) return MOE_EWORKSPACE;
   FfnIo io{a, a_scale, group_offsets, w13, w13_scale, w2, w2_scale, y};
   io.gather = row_of;
@@ -793,6 +809,7 @@ moe_status moe_finalize_routing(const moe_shape* s, const void* y, const void* s
   if (st != MOE_OK) return st;
   if (s->T == 0) return MOE_OK;
   if (!y || !expanded_row_idx || !out) return MOE_EINVAL;
+  if (!aligned16({y, skip, topk_w, expanded_row_idx, out})) return MOE_EINVAL;
   return hip_status(moe::launch_finalize(y, skip, topk_w, expanded_row_idx, out, s->T, s->H, s->k,
                                          elem_bytes(s->act), stream));
 }
@@ -873,6 +890,9 @@ static moe_status layer_impl(const moe_shape* s, const moe_weights* w, const voi
   const bool q8 = q8_weights(s);
   if ((fp8 || q8) && (!w->w13_scale || !w->w2_scale)) return MOE_EINVAL;
   if (q8 && s->T > 0 && (!w->sh_w13_scale || !w->sh_w2_scale)) return MOE_EINVAL;
+  if (!aligned16({x, out, topk_idx, topk_w, logits, ws, w->w_gate, w->w13, w->w2, w->sh_w13, w->sh_w2,
+                  w->w13_scale, w->w2_scale, w->bias, w->sh_w13_scale, w->sh_w2_scale}))
+    return MOE_EINVAL;
   const size_t need = moe_workspace_bytes(s);
   if (need == 0) return MOE_EINVAL;
   if (ws_bytes < need) return MOE_EWORKSPACE;

@@ -144,6 +144,47 @@ def test_validation_errors_enqueue_nothing(L):
     assert L.moe_get_error(None, None) == M.MOE_EINVAL
 
 
+def test_misaligned_pointers_are_rejected(L):
+    """Tensor pointers must be 16-byte aligned: one that is not is MOE_EINVAL before
+    anything is enqueued.  Every call passes a 16-byte workspace, so a call that got past
+    the alignment check would stop at the workspace check (MOE_EWORKSPACE) and never
+    launch on the dummy pointers."""
+    s = M.shape(16, 256, 8, 2, 128, 128)
+    off = ctypes.c_void_p(DUMMY.value + 8)
+
+    def each_misaligned(args, call):
+        for i, a in enumerate(args):
+            if a is None:
+                continue
+            bad = list(args)
+            bad[i] = off
+            assert call(bad) == M.MOE_EINVAL, i
+        assert call(args) == M.MOE_EWORKSPACE
+
+    # x, w_gate, bias, logits, topk_idx, topk_w, ws
+    each_misaligned([DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY],
+                    lambda a: L.moe_gate_topk(ctypes.byref(s), *a, 16, None))
+    # x, ids | expanded_x, expanded_scale, expanded_row_idx, sorted_src, counts, offsets, ws
+    each_misaligned([DUMMY, DUMMY, DUMMY, None, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY],
+                    lambda a: L.moe_init_routing(ctypes.byref(s), a[0], a[1], 0, *a[2:], 16, None))
+    # a, a_scale, offsets, w13, w13_scale, w2, w2_scale, y, ws
+    each_misaligned([DUMMY, None, DUMMY, DUMMY, None, DUMMY, None, DUMMY, DUMMY],
+                    lambda a: L.moe_grouped_ffn(ctypes.byref(s), 8, 32, *a, 16, None))
+    fp8 = M.shape(16, 256, 8, 2, 128, 128, "bf16", "fp8")
+    each_misaligned([DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY],
+                    lambda a: L.moe_grouped_ffn(ctypes.byref(fp8), 8, 32, *a, 16, None))
+    # a | a_scale, row_of | offsets, w13, w13_scale, w2, w2_scale, y, ws
+    each_misaligned([DUMMY, None, DUMMY, DUMMY, DUMMY, None, DUMMY, None, DUMMY, DUMMY],
+                    lambda a: L.moe_grouped_ffn_gathered(ctypes.byref(s), 8, 32, a[0], 64, a[1], a[2], 1,
+                                                         *a[3:], 16, None))
+
+    # the layer: its own pointers, then each weight pointer
+    def layer(a):
+        w = M.moe_weights(*a[4:])
+        return L.moe_layer(ctypes.byref(s), ctypes.byref(w), a[0], a[1], a[2], a[3], None, DUMMY, 16, None)
+    each_misaligned([DUMMY, DUMMY, DUMMY, DUMMY] + [DUMMY] * 5 + [None, None, DUMMY, None, None], layer)
+
+
 def test_router_validation_enqueues_nothing(L):
     """Invalid router variants are rejected on the host (MOE_EINVAL) before any launch."""
     s = M.shape(16, 256, 16, 4, 128, 128)
