@@ -194,7 +194,9 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   // fp8: the per-lane DMA offsets live in LDS and are re-read (volatile) at each issue;
   // in registers they would be spilled, and a scratch reload waits on vmcnt(0), which
   // would drain the DMAs in flight.
-  __shared__ uint32_t off_tab[FP8 ? LPER : 1][FP8 ? LW * 64 : 1];   // loader lanes' chunk offsets
+  // loader lanes' chunk offsets, four per 16-byte entry (one 16-byte read per four DMAs)
+  constexpr int OFFG = (LPER + 3) / 4;
+  __shared__ __attribute__((aligned(16))) u32x4 off_tab[FP8 ? OFFG : 1][FP8 ? LW * 64 : 1];
   __shared__ uint32_t sc_tab[FP8 ? (ASW + 1) * 64 : 1];               // scale offsets, waves 0 .. ASW
 
   // A workgroup computes TPW consecutive N tiles of one unit (one K split); its ring runs
@@ -344,15 +346,15 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
   if constexpr (FP8) {
     if (loader) {
 #pragma unroll
-      for (int i = 0; i < LPER; ++i) off_tab[i][tid] = goff[i];
+      for (int g = 0; g < OFFG; ++g)
+        off_tab[g][tid] = u32x4{goff[4 * g], 4 * g + 1 < LPER ? goff[4 * g + 1] : 0u,
+                                4 * g + 2 < LPER ? goff[4 * g + 2] : 0u, 4 * g + 3 < LPER ? goff[4 * g + 3] : 0u};
     }
     if (wave <= ASW) sc_tab[tid] = sc_off;
     // visible to this lane's own later reads; no other lane reads it
   }
-  auto lane_off_of = [&](int i) __attribute__((always_inline)) {
-    if constexpr (FP8) return ((vlds)&off_tab[i][0])[tid];
-    else return goff[i];
-  };
+  // (fp8 reads its offsets from the LDS table at each issue instead)
+  auto lane_off_of = [&](int i) __attribute__((always_inline)) { return goff[i]; };
   // This wavefront's first 1 KB chunk of each ring buffer, as an LDS byte address
   // (wave-uniform).  Each DMA's M0 is formed from it with a compile-time offset at the
   // issue itself: the empty asm below makes the base a fresh value per issue, so the
@@ -373,10 +375,23 @@ __device__ __forceinline__ void gemm_dma_body(const GemmArgs& p) {
     asm volatile("" : "+s"(m0w));
     if (loader) {
       // every lane offset of this issue is read before the first DMA (fp8: from the LDS
-      // table, so one wait covers them all instead of one LDS round trip per DMA)
+      // table, four offsets per 16-byte read, so one wait covers them all instead of one
+      // LDS round trip per DMA)
       uint32_t offs[LPER];
+      if constexpr (FP8) {
+        using vlds4 = volatile __attribute__((address_space(3))) u32x4*;
 #pragma unroll
-      for (int i = 0; i < LPER; ++i) offs[i] = lane_off_of(i);
+        for (int g = 0; g < OFFG; ++g) {
+          const u32x4 o = ((vlds4)&off_tab[g][0])[tid];
+          offs[4 * g] = o.x;
+          if (4 * g + 1 < LPER) offs[4 * g + 1] = o.y;
+          if (4 * g + 2 < LPER) offs[4 * g + 2] = o.z;
+          if (4 * g + 3 < LPER) offs[4 * g + 3] = o.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < LPER; ++i) offs[i] = lane_off_of(i);
+      }
 #pragma unroll
       for (int i = 0; i < A_PER; ++i)   // wave-uniform test: chunk q holds a row of the unit
         if (NST != 2 || (wave + i * LW) * RPC < rows) dma16m(ak, offs[i], m0w + i * LW * 1024u);
