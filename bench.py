@@ -540,6 +540,27 @@ def copy_calibration(nbytes=1 << 30, reps=3):
     print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": reps}), flush=True)
 
 
+def copy_ceiling(nbytes=1 << 30, reps=5) -> dict:
+    """The achievable HBM rate beside the nominal 8 TB/s: a device-to-device copy of
+    `nbytes` (it reads nbytes and writes nbytes) timed with HIP events on the current
+    stream, after the bench's timed region; GB/s = 2 * nbytes / mean time per copy."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    end.record()
+    end.synchronize()
+    ms = start.elapsed_time(end) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"GB/s": 2 * nbytes / (ms / 1e3) / 1e9, "bytes_per_copy": 2 * nbytes, "ms_per_copy": ms,
+            "note": "device-to-device copy of 1 GiB (read + write bytes), after the timed region"}
+
+
 # ----------------------------------------------------------------------------- main
 
 DEFAULT_ALSO = "c5_skewed_fp8,c3_ep_rank_bf16,c4_decode_bf16"
@@ -590,6 +611,9 @@ def main():
             steps, warm = min(args.steps, 10), min(args.warmup, 2)
             o = ep_line(ocfg, steps, warm) if ocfg.pretagged else layer_line(ocfg, args, steps, warm)
             line["other_workloads"][name] = summary_of(o)
+    line["hbm_copy"] = copy_ceiling()
+    if line["roofline"]["unit"] == "GB/s":
+        line["roofline"]["frac_of_copy"] = line["roofline"]["achieved"] / line["hbm_copy"]["GB/s"]
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     else:
