@@ -540,6 +540,16 @@ def copy_calibration(nbytes=1 << 30, reps=3):
     print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": reps}), flush=True)
 
 
+def rows_histogram(tpe) -> dict:
+    """Realized routed rows per expert, as the number of experts in each row-count bucket."""
+    edges = [(0, 0), (1, 2), (3, 8), (9, 32), (33, 128), (129, 512), (513, 2048), (2049, 1 << 40)]
+    out = {}
+    for lo, hi in edges:
+        key = str(lo) if lo == hi else (f"{lo}-{hi}" if hi < 1 << 40 else f">={lo}")
+        out[key] = int(np.count_nonzero((tpe >= lo) & (tpe <= hi)))
+    return out
+
+
 def copy_ceiling(nbytes=1 << 30, reps=5) -> dict:
     """The achievable HBM rate beside the nominal 8 TB/s: a device-to-device copy of
     `nbytes` (it reads nbytes and writes nbytes) timed with HIP events on the current
@@ -627,11 +637,12 @@ def summary_of(line: dict) -> dict:
     out = {"ms_per_step": line["ms_per_step"], "tokens_per_s": line["value"], "steps": line["steps"],
            "dtype": line["dtype"], "config": line["config"],
            "roofline": {k: roof[k] for k in ("kernel", "bound", "achieved", "peak", "unit", "frac", "traffic",
-                                              "mfma_frac")},
+                                              "mfma_frac", "traffic_ratio", "rereads_flag") if k in roof},
            "ffn_mfma_frac": line["ffn_mfma_frac"], "permute_combine_hbm_frac": line["permute_combine_hbm_frac"],
            "kernels_ms": {k: round(v["ms"], 4) for k, v in line["kernels"].items()}}
-    if "rows_per_s" in line:
-        out["rows_per_s"] = line["rows_per_s"]
+    for k in ("rows_per_s", "ffn_mfma_frac_bf16_peak", "rows_per_expert_histogram"):
+        if k in line:
+            out[k] = line[k]
     return out
 
 
@@ -669,6 +680,10 @@ def layer_line(cfg, args, steps=None, warmup=None) -> dict:
     roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roof["algorithmic_bytes"] = acc[dom]["bytes"]
     roof["mfma_frac"] = dk.get("mfma_frac")
+    if roof["traffic"] is not None:
+        # measured over algorithmic bytes; above 1.2 means panels or rows are read again
+        roof["traffic_ratio"] = roof["traffic"] / roof["algorithmic_bytes"]
+        roof["rereads_flag"] = roof["traffic_ratio"] > 1.2
     # expand is an empty stage when the rows are gathered inside ffn1
     permute_ms = r["stage_ms"]["expand"] + r["stage_ms"]["finalize"]
     permute_bytes = acc["expand"]["bytes"] + acc["finalize"]["bytes"]
@@ -691,11 +706,14 @@ def layer_line(cfg, args, steps=None, warmup=None) -> dict:
                    "I_shared": cfg.I_shared, "act": cfg.act, "wt": cfg.wt},
         "roofline": roof,
         "ffn_mfma_frac": ffn_flops / (ffn_ms / 1e3) / 1e12 / PEAK_TFLOPS[acc["ffn1"]["dt"]],
+        # fp8 experts: the same FFN rate against the bf16 peak as well
+        "ffn_mfma_frac_bf16_peak": ffn_flops / (ffn_ms / 1e3) / 1e12 / PEAK_TFLOPS["bf16"],
         "permute_combine_hbm_frac": permute_bytes / (permute_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
         "kernels": kern,
         "shared_expert": shared_mode,
         "active_experts": int(np.count_nonzero(r["tpe"])),
         "max_rows_per_expert": int(r["tpe"].max()),
+        "rows_per_expert_histogram": rows_histogram(r["tpe"]),
         "wall_ms_per_step": r["wall_s"] * 1e3 / steps,
         "cold_ms_per_step": r["cold_ms"],
         "setup_s": r["setup_s"],
@@ -727,6 +745,9 @@ def ep_line(cfg, steps, warmup) -> dict:
     roof["traffic_unit"] = "HBM bytes per ffn stage (both expert GEMMs; rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roof["algorithmic_bytes"] = acc["ffn"]["bytes"]
     roof["mfma_frac"] = dk.get("mfma_frac")
+    if roof["traffic"] is not None:
+        roof["traffic_ratio"] = roof["traffic"] / roof["algorithmic_bytes"]
+        roof["rereads_flag"] = roof["traffic_ratio"] > 1.2
     perm_ms = r["stage_ms"]["route"] + r["stage_ms"]["unsort"]
     perm_bytes = acc["route"]["bytes"] + acc["unsort"]["bytes"]
     line = {
